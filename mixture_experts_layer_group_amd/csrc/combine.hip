@@ -1,0 +1,100 @@
+// Combine: the routed expert outputs go back to token order, each scaled by
+// its routing weight, summed with the always-on shared experts (dockyard_rl
+// "Mixture-of-Experts" page, "The pipeline", combine; "Mixture of Experts"
+// blog page, the third program's scatter-add, where a token routed to k
+// experts collects k contributions; "Mixture-of-Experts Documentation",
+// shared expert).  Written as a gather -- each token reads its own kept rows
+// through slot_row -- so the sum has a fixed order (slot 0..k-1, then the
+// shared experts) and needs no atomics.  Dropped slots (row -1) add nothing.
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(w[j] << 16);
+    v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float* v) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float* v) {
+  uint4 a;
+  a.x = pack_bf16x2(v[0], v[1]);
+  a.y = pack_bf16x2(v[2], v[3]);
+  a.z = pack_bf16x2(v[4], v[5]);
+  a.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(p) = a;
+}
+__device__ __forceinline__ void store8(float* p, const float* v) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+constexpr int kMaxSlots = 64;
+
+// One block per token.
+template <typename T>
+__global__ void __launch_bounds__(256)
+combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ slot_row,
+               const float* __restrict__ topk_w, const T* __restrict__ ysh,
+               T* __restrict__ out, int64_t Tn, int k, int S, int d) {
+  __shared__ int32_t rows[kMaxSlots];
+  __shared__ float wts[kMaxSlots];
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x < k) {
+    rows[threadIdx.x] = slot_row[t * k + threadIdx.x];
+    wts[threadIdx.x] = topk_w[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < k; ++i) {
+      const int32_t r = rows[i];
+      if (r < 0) continue;
+      float v[8];
+      load8(y + static_cast<int64_t>(r) * d + c, v);
+      const float wi = wts[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wi, v[j], acc[j]);
+    }
+    for (int s = 0; s < S; ++s) {
+      float v[8];
+      load8(ysh + (static_cast<int64_t>(s) * Tn + t) * d + c, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] += v[j];
+    }
+    store8(out + t * d + c, acc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const Dims& D, const void* y_rows,
+                          const int32_t* slot_row, const float* topk_w,
+                          const void* y_shared, void* out, hipStream_t s) {
+  if (D.k > kMaxSlots) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(D.T));
+  const int S = y_shared ? D.S : 0;
+  if (D.bf16)
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(y_rows), slot_row, topk_w,
+                       static_cast<const uint16_t*>(y_shared),
+                       static_cast<uint16_t*>(out), D.T, D.k, S, D.d);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(y_rows), slot_row, topk_w,
+                       static_cast<const float*>(y_shared),
+                       static_cast<float*>(out), D.T, D.k, S, D.d);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,390 @@
+// Grouped expert GEMMs on CDNA4 bf16 matrix cores (fp32 accumulation), over
+// the ragged per-expert row groups that the dispatch produced: the "one
+// grouped matmul over the ragged per-expert token groups" of the dockyard_rl
+// "Mixture-of-Experts" page ("The pipeline", grouped GEMM), with the
+// two-products-per-expert structure of the "Mixture of Experts" blog page's
+// third program (moe_forward).
+//
+//   up   (GEMM1): H[r, f] = act(x[tok(r)] . W_gate[e][f] (, x . W_up[e][f]))
+//                 SwiGLU = silu(gate) * up (Edge0 "MoE Spec and Routing",
+//                 _swiglu); ReLU ("Mixture of Experts" blog, expert_forward)
+//   down (GEMM2): Y[r, n] = H[r] . W_down[e][n]
+//
+// Kernel shape (gfx950):
+//   * a 256 x 256 output tile per 256-thread workgroup, K steps of 64;
+//     each of the 4 waves owns a 128 x 128 sub-tile = 4 x 4 blocks of
+//     v_mfma_f32_32x32x16_bf16.  The weight tile is the MFMA A operand
+//     (rows = output columns) and the activation tile the B operand, so a
+//     lane's accumulators hold 4 consecutive output columns of one row;
+//   * both operands are K-contiguous in HBM (weights are [out, in]) and go
+//     straight from HBM to LDS (buffer_load_dwordx4 ... lds, no staging
+//     registers) into double-buffered tiles (2 x 64 KiB); the next K step is
+//     in flight while the current one is multiplied.  The 16-byte chunks of
+//     each 128-byte LDS row are XOR-swizzled (conflict-free for 8- and
+//     16-lane LDS phases); the swizzle is applied on the global side, since
+//     a direct load writes LDS at lane*16;
+//   * activation rows are gathered on load through sorted_token (no
+//     permuted copy of x);
+//   * SwiGLU: a tile's 256 weight rows are 128 gate rows then the same 128
+//     up rows; each wave holds gate and up accumulators of the same
+//     (row, column) in the same lanes, so the epilogue fuses silu(g) * u;
+//   * ragged groups without a host sync: the grid is an upper bound on the
+//     tile count; each workgroup reads the per-expert M-tile prefix written
+//     by the dispatch and exits if surplus.  Workgroup ids are remapped so
+//     that each of the 8 XCDs (hardware dispatch is round-robin over XCDs)
+//     gets a contiguous range of tiles, ordered 8 N-tiles fastest inside an
+//     expert's M-tiles, so concurrently running tiles on one XCD share
+//     weight and activation tiles in its L2.
+#include <algorithm>
+
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kRowBytes = BK * 2;           // 128
+constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand per stage
+constexpr int kNG = 8;                      // N-tiles per scheduling column group
+static_assert(BM == kGemm1BM && BM == kGemm2BM, "tile prefix BM mismatch");
+
+enum Mode { kSwiGLU = 0, kReLU = 1, kDown = 2 };
+
+struct GemmArgs {
+  const uint16_t* a;            // activation rows (x or H)
+  const int32_t* sorted_token;  // gather table (nullptr: row = group row)
+  const int32_t* offsets;       // [E+1] group row offsets (nullptr: one group)
+  const int32_t* tiles;         // [E+1] group M-tile prefix (nullptr: one group)
+  int E;
+  int32_t single_rows;          // rows of the single group
+  const uint16_t* w0;           // gate / in / down  [E][N][K]
+  const uint16_t* w1;           // up (SwiGLU)
+  int N;                        // weight rows per expert
+  int K;                        // reduction length (row length of a and w)
+  uint16_t* out;                // [rows][ldo]
+  int ldo;                      // output row length (F or d)
+  int NT;                       // N tiles
+};
+
+// byte offset of 16-byte chunk c of row r inside a swizzled tile
+__device__ __forceinline__ int swz(int r, int c) {
+  return r * kRowBytes + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
+}
+
+__device__ __forceinline__ int largest_le(const int32_t* __restrict__ p, int E,
+                                          int32_t v) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p[mid] <= v) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
+
+template <int MODE, bool GATHER>
+__global__ void __launch_bounds__(256, 1)
+grouped_gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileBytes];
+  uint8_t* sA = smem;                   // [2][BM rows][128 B]
+  uint8_t* sW = smem + 2 * kTileBytes;  // [2][BN rows][128 B]
+
+  // ---------------- tile scheduling
+  const int total_mt = g.tiles ? g.tiles[g.E] : (g.single_rows + BM - 1) / BM;
+  const int real = total_mt * g.NT;
+  const int share = (real + 7) >> 3;
+  const int bid = blockIdx.x;
+  const int local = bid >> 3;
+  if (local >= share) return;
+  const int L = (bid & 7) * share + local;
+  if (L >= real) return;
+  int gm, nt;
+  {
+    const int full = g.NT / kNG;
+    const int colgrp = L / (total_mt * kNG);
+    if (colgrp < full) {
+      const int rem = L - colgrp * total_mt * kNG;
+      gm = rem / kNG;
+      nt = colgrp * kNG + rem % kNG;
+    } else {
+      const int ng = g.NT - full * kNG;
+      const int rem = L - full * total_mt * kNG;
+      gm = rem / ng;
+      nt = full * kNG + rem % ng;
+    }
+  }
+  int e = 0, row0, cnt, mt;
+  if (g.tiles) {
+    e = largest_le(g.tiles, g.E, gm);
+    mt = gm - g.tiles[e];
+    row0 = g.offsets[e];
+    cnt = g.offsets[e + 1] - row0;
+  } else {
+    mt = gm;
+    row0 = 0;
+    cnt = g.single_rows;
+  }
+  const int m0 = mt * BM;  // first row of this tile inside the group
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---------------- direct-to-LDS load descriptors
+  // Each wave-wide buffer_load_dwordx4 ... lds fills 1 KiB of LDS (8 rows of
+  // 128 B) at lane*16; lane l therefore fetches the global chunk that the
+  // swizzle places at position l%8 of row l/8.  Wave w issues blocks
+  // j*4 + w (j = 0..7) of each 32 KiB operand tile.
+  const int64_t K = g.K;
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(g.a), (short)0, -1, 0x00020000);
+  const uint16_t* wbase0 = g.w0 + static_cast<int64_t>(e) * g.N * K;
+  const uint16_t* wbase1 = (MODE == kSwiGLU ? g.w1 : g.w0) + static_cast<int64_t>(e) * g.N * K;
+  const __amdgpu_buffer_rsrc_t rsW0 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(wbase0), (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsW1 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(wbase1), (short)0, -1, 0x00020000);
+  uint32_t voffA[8], voffW[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = (j * 4 + wave) * 8 + (lane >> 3);  // tile row
+    const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);  // chunk at position lane%8
+    int m = m0 + r;
+    if (m > cnt - 1) m = cnt - 1;  // clamp ragged tail to a valid row
+    const int64_t arow = GATHER ? static_cast<int64_t>(g.sorted_token[row0 + m])
+                                : static_cast<int64_t>(row0 + m);
+    voffA[j] = static_cast<uint32_t>(arow * K * 2 + c * 16);
+    int n = (MODE == kSwiGLU) ? nt * (BN / 2) + (r & 127) : nt * BN + r;
+    if (n > g.N - 1) n = g.N - 1;
+    voffW[j] = static_cast<uint32_t>(static_cast<int64_t>(n) * K * 2 + c * 16);
+  }
+
+  // ---------------- per-lane fragment offsets
+  // MFMA 32x32x16: lane l supplies row (l % 32), K elements 8*(l/32)..+8
+  const int fr = lane & 31;
+  const int fh = lane >> 5;
+  int wrow[4], arow_l[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    if (MODE == kSwiGLU)
+      wrow[nb] = ((nb & 2) ? 128 : 0) + wn * 64 + (nb & 1) * 32 + fr;
+    else
+      wrow[nb] = wn * 128 + nb * 32 + fr;
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) arow_l[mb] = wm * 128 + mb * 32 + fr;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int KT = g.K / BK;
+  auto issue = [&](int kt, int buf) {
+    const int soff = kt * kRowBytes;  // K advance in bytes
+    uint8_t* a = sA + buf * kTileBytes;
+    uint8_t* w = sW + buf * kTileBytes;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int blk = (j * 4 + wave) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsA, (__attribute__((address_space(3))) void*)(a + blk), 16, voffA[j],
+          soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          j < 4 ? rsW0 : rsW1, (__attribute__((address_space(3))) void*)(w + blk),
+          16, voffW[j], soff, 0, 0);
+    }
+  };
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) issue(kt + 1, cur ^ 1);
+    const uint8_t* a = sA + cur * kTileBytes;
+    const uint8_t* w = sW + cur * kTileBytes;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int ch = ks * 2 + fh;
+      bf16x8 wf[4], af[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        wf[nb] = *reinterpret_cast<const bf16x8*>(w + swz(wrow[nb], ch));
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        af[mb] = *reinterpret_cast<const bf16x8*>(a + swz(arow_l[mb], ch));
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              wf[nb], af[mb], acc[nb][mb], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---------------- epilogue
+  // lane holds, for block (nb, mb) and item v: output column
+  //   colbase(nb) + 8*(v/4) + 4*(lane/32) + v%4, row arow_l[mb].
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = m0 + arow_l[mb];
+    if (m >= cnt) continue;
+    uint16_t* orow = g.out + static_cast<int64_t>(row0 + m) * g.ldo;
+    if (MODE == kSwiGLU) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * (BN / 2) + wn * 64 + nb * 32 + 8 * q + 4 * fh;
+          if (col >= g.N) continue;
+          float h[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            h[v] = silu(acc[nb][mb][4 * q + v]) * acc[nb + 2][mb][4 * q + v];
+          uint2 pk;
+          pk.x = pack_bf16x2(h[0], h[1]);
+          pk.y = pack_bf16x2(h[2], h[3]);
+          *reinterpret_cast<uint2*>(orow + col) = pk;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * BN + wn * 128 + nb * 32 + 8 * q + 4 * fh;
+          if (col >= g.N) continue;
+          float h[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float z = acc[nb][mb][4 * q + v];
+            h[v] = (MODE == kReLU) ? (z > 0.f ? z : 0.f) : z;
+          }
+          uint2 pk;
+          pk.x = pack_bf16x2(h[0], h[1]);
+          pk.y = pack_bf16x2(h[2], h[3]);
+          *reinterpret_cast<uint2*>(orow + col) = pk;
+        }
+      }
+    }
+  }
+}
+
+int ntiles(int mode, int N) {
+  const int cols = mode == kSwiGLU ? BN / 2 : BN;
+  return (N + cols - 1) / cols;
+}
+
+hipError_t launch_one(int mode, bool gather, const GemmArgs& g, int64_t mt_upper,
+                      hipStream_t s) {
+  int64_t n = mt_upper * g.NT;
+  n = (n + 7) / 8 * 8;
+  if (n <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(n)), block(256);
+  if (mode == kSwiGLU && gather)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, true>), grid, block, 0, s, g);
+  else if (mode == kSwiGLU)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, false>), grid, block, 0, s, g);
+  else if (mode == kReLU && gather)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, true>), grid, block, 0, s, g);
+  else if (mode == kReLU)
+    hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, false>), grid, block, 0, s, g);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<kDown, false>), grid, block, 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_shared_bf16(const Dims& D, const void* x,
+                              const moe_expert_weights& w, void* Hs, void* Ys,
+                              hipStream_t s) {
+  const int up_mode = D.swiglu ? kSwiGLU : kReLU;
+  const int64_t mt = (D.T + BM - 1) / BM;
+  for (int sh = 0; sh < D.S; ++sh) {
+    const int64_t wo = static_cast<int64_t>(sh) * D.Fs * D.d;
+    GemmArgs g{};
+    g.a = static_cast<const uint16_t*>(x);
+    g.E = 1;
+    g.single_rows = static_cast<int32_t>(D.T);
+    g.w0 = static_cast<const uint16_t*>(w.shared_gate) + wo;
+    g.w1 = D.swiglu ? static_cast<const uint16_t*>(w.shared_up) + wo : nullptr;
+    g.N = D.Fs;
+    g.K = D.d;
+    g.out = static_cast<uint16_t*>(Hs);
+    g.ldo = D.Fs;
+    g.NT = ntiles(up_mode, D.Fs);
+    hipError_t err = launch_one(up_mode, false, g, mt, s);
+    if (err != hipSuccess) return err;
+    GemmArgs h{};
+    h.a = static_cast<const uint16_t*>(Hs);
+    h.E = 1;
+    h.single_rows = static_cast<int32_t>(D.T);
+    h.w0 = static_cast<const uint16_t*>(w.shared_down) + wo;
+    h.N = D.d;
+    h.K = D.Fs;
+    h.out = static_cast<uint16_t*>(Ys) + static_cast<int64_t>(sh) * D.T * D.d;
+    h.ldo = D.d;
+    h.NT = ntiles(kDown, D.d);
+    err = launch_one(kDown, false, h, mt, s);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
+                           const int32_t* tiles1, const int32_t* tiles2,
+                           const int32_t* sorted_token, const void* x,
+                           const moe_expert_weights& w, void* H, void* Hs,
+                           void* Y, void* Ys, hipStream_t s) {
+  const int up_mode = D.swiglu ? kSwiGLU : kReLU;
+  // kept rows are at most min(T*k, E*capacity); cap is already <= T*k
+  const int64_t nmax = std::min<int64_t>(D.slots, D.cap * D.E);
+  {
+    GemmArgs g{};
+    g.a = static_cast<const uint16_t*>(x);
+    g.sorted_token = sorted_token;
+    g.offsets = offsets;
+    g.tiles = tiles1;
+    g.E = D.E;
+    g.w0 = static_cast<const uint16_t*>(w.gate);
+    g.w1 = D.swiglu ? static_cast<const uint16_t*>(w.up) : nullptr;
+    g.N = D.F;
+    g.K = D.d;
+    g.out = static_cast<uint16_t*>(H);
+    g.ldo = D.F;
+    g.NT = ntiles(up_mode, D.F);
+    hipError_t err = launch_one(up_mode, true, g, nmax / BM + D.E, s);
+    if (err != hipSuccess) return err;
+  }
+  {
+    GemmArgs g{};
+    g.a = static_cast<const uint16_t*>(H);
+    g.offsets = offsets;
+    g.tiles = tiles2;
+    g.E = D.E;
+    g.w0 = static_cast<const uint16_t*>(w.down);
+    g.N = D.d;
+    g.K = D.F;
+    g.out = static_cast<uint16_t*>(Y);
+    g.ldo = D.d;
+    g.NT = ntiles(kDown, D.d);
+    hipError_t err = launch_one(kDown, false, g, nmax / BM + D.E, s);
+    if (err != hipSuccess) return err;
+  }
+  if (D.S > 0) return launch_shared_bf16(D, x, w, Hs, Ys, s);
+  return hipSuccess;
+}
+
+}  // namespace moe

@@ -1,0 +1,118 @@
+// Internal declarations shared by the HIP translation units of the MoE
+// library.  Not part of the C ABI (that is include/moe.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// round to nearest even (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// ---------------------------------------------------------------- waves
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------- sizes
+// Per-call problem sizes derived from a validated spec.
+struct Dims {
+  int64_t T;
+  int E, k, d, F, S, Fs;
+  int64_t slots;      // T * k
+  int64_t cap;        // INT64_MAX when unlimited
+  bool bf16;          // bf16 activations
+  bool u4;            // 4-bit routed weights
+  bool swiglu;
+};
+
+// Workspace carve-up (byte offsets, each 256-aligned).
+struct WsLayout {
+  size_t logits, probpart, hist, tiles1, tiles2;
+  size_t topk_ids, topk_w, counts, offsets, sorted_token, sorted_w, slot_row,
+      dropped;
+  size_t H, Hs, Y, Ys;
+  size_t total;
+  int route_blocks;     // selection kernel grid (prob partial rows)
+  int dispatch_blocks;  // count / scatter grid (histogram rows)
+};
+
+constexpr int kDispatchChunk = 2048;  // slots per dispatch block
+constexpr int kSelectWaves = 4;       // tokens in flight per select block
+
+// GEMM tile rows (M) of the bf16 grouped kernels; the dispatch scan writes
+// the per-expert M-tile prefix for them.
+constexpr int kGemm1BM = 256;
+constexpr int kGemm2BM = 256;
+
+// ---------------------------------------------------------------- launchers
+// router.hip
+hipError_t launch_router_logits(const Dims& D, int act_dtype, int router_dtype,
+                                const void* x, const void* wr, float* logits,
+                                hipStream_t s);
+hipError_t launch_router_select(const Dims& D, const moe_spec& sp,
+                                const float* logits, const float* bias,
+                                int32_t* ids, float* w, float* probpart,
+                                int nblocks, hipStream_t s);
+hipError_t launch_prob_finalize(const Dims& D, const float* probpart,
+                                int nblocks, float* prob_sum, hipStream_t s);
+
+// dispatch.hip
+hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
+                           int32_t* hist, int nblocks, int32_t* counts,
+                           int32_t* offsets, int32_t* sorted_token,
+                           float* sorted_w, int32_t* slot_row, int32_t* dropped,
+                           int32_t* tiles1, int32_t* tiles2, hipStream_t s);
+hipError_t launch_gather_rows(const Dims& D, const int32_t* offsets,
+                              const int32_t* sorted_token, const void* x,
+                              void* x_perm, hipStream_t s);
+hipError_t launch_tile_prefix(const Dims& D, const int32_t* offsets,
+                              int32_t* tiles1, int32_t* tiles2, hipStream_t s);
+
+// gemm_bf16.hip (bf16 activations, bf16 weights, MFMA)
+hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
+                           const int32_t* tiles1, const int32_t* tiles2,
+                           const int32_t* sorted_token, const void* x,
+                           const moe_expert_weights& w, void* H, void* Hs,
+                           void* Y, void* Ys, hipStream_t s);
+// gemm_f32.hip (fp32 activations and weights, VALU)
+hipError_t launch_ffn_f32(const Dims& D, const int32_t* offsets,
+                          const int32_t* sorted_token, const void* x,
+                          const moe_expert_weights& w, void* H, void* Hs,
+                          void* Y, void* Ys, hipStream_t s);
+// gemm_u4.hip (bf16 activations, 4-bit affine routed weights, VALU)
+hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
+                         const int32_t* sorted_token, const void* x,
+                         const moe_expert_weights& w, void* H, void* Y,
+                         hipStream_t s);
+// shared experts with bf16 weights on the MFMA kernel (used by the u4 path)
+hipError_t launch_shared_bf16(const Dims& D, const void* x,
+                              const moe_expert_weights& w, void* Hs, void* Ys,
+                              hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const Dims& D, const void* y_rows,
+                          const int32_t* slot_row, const float* topk_w,
+                          const void* y_shared, void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,393 @@
+// Router: logits L = x @ Wr^T (fp32 accumulation on the vector ALUs -- the
+// router is the smallest weight of the layer and is kept out of the matrix
+// cores), then the top-k selection of either routing kind:
+//   SOFTMAX_TOPK  -- Edge0 "MoE Spec and Routing" page, select_from_logits;
+//                    "Mixture of Experts" blog page, route (softmax, keep
+//                    the k most probable, renormalise over them);
+//   SIGMOID_GROUP -- Edge0 page, group_select_from_logits (sigmoid scores,
+//                    a selection-only bias, group-limited top-k, routed
+//                    scaling).
+// Ranking is decided on fp32 values with ties to the lower index, so it is
+// reproducible bit for bit; softmax is monotone, so ranking the logits is
+// ranking the probabilities.
+#include "moe_internal.hpp"
+
+#include <math.h>
+
+namespace moe {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float ld1(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld1<float>(const float* p, int64_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+// 8 consecutive elements as fp32 (p + i must be 16-byte aligned for bf16,
+// 32-byte for fp32)
+__device__ __forceinline__ void ld8(const float* p, int64_t i, float* v) {
+  const float4* q = reinterpret_cast<const float4*>(p + i);
+  float4 a = q[0], b = q[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void ld8(const uint16_t* p, int64_t i, float* v) {
+  uint4 a = *reinterpret_cast<const uint4*>(p + i);
+  uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(w[j] << 16);
+    v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+  }
+}
+
+// ------------------------------------------------------------------ logits
+// Tiled fp32 GEMM for many tokens: a 64x64 (token x expert) tile per block,
+// 4x4 outputs per thread, K staged through LDS in steps of 32.
+constexpr int LT = 64, LE = 64, LK = 32;
+
+template <typename XT, typename WT>
+__global__ void __launch_bounds__(256)
+logits_tiled_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
+                    float* __restrict__ L, int64_t T, int E, int d) {
+  __shared__ float xs[LK][LT + 4];
+  __shared__ float ws[LK][LE + 4];
+  const int tid = threadIdx.x;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * LT;
+  const int e0 = blockIdx.y * LE;
+  const int tx = tid % 16, ty = tid / 16;
+  float acc[4][4] = {};
+  const int lr = tid / 4;        // row loaded by this thread
+  const int lk = (tid % 4) * 8;  // its 8-element K chunk
+  const bool vec = (d % 8) == 0;
+  for (int k0 = 0; k0 < d; k0 += LK) {
+    float v[8];
+    {
+      const int64_t t = t0 + lr;
+      const int k = k0 + lk;
+      if (t < T && vec && k + 8 <= d) {
+        ld8(x, t * d + k, v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          v[j] = (t < T && k + j < d) ? ld1(x, t * d + k + j) : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xs[lk + j][lr] = v[j];
+    }
+    {
+      const int e = e0 + lr;
+      const int k = k0 + lk;
+      if (e < E && vec && k + 8 <= d) {
+        ld8(wr, static_cast<int64_t>(e) * d + k, v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          v[j] = (e < E && k + j < d)
+                     ? ld1(wr, static_cast<int64_t>(e) * d + k + j)
+                     : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ws[lk + j][lr] = v[j];
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < LK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) L[t * E + e] = acc[i][j];
+    }
+  }
+}
+
+// Few tokens (decode): one wave per expert row, lanes split K, 4 tokens at
+// a time; the expert's router row is read once per 4 tokens (then cached).
+template <typename XT, typename WT>
+__global__ void __launch_bounds__(256)
+logits_rowdot_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
+                     float* __restrict__ L, int64_t T, int E, int d) {
+  const int lane = threadIdx.x % kWave;
+  const int e = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (e >= E) return;
+  const WT* wrow = wr + static_cast<int64_t>(e) * d;
+  for (int64_t t0 = 0; t0 < T; t0 += 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int k = lane * 8; k < d; k += kWave * 8) {
+      float wv[8];
+      ld8(wrow, k, wv);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (t0 + i < T) {
+          float xv[8];
+          ld8(x, (t0 + i) * d + k, xv);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i] = fmaf(xv[j], wv[j], acc[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s = wave_sum(acc[i]);
+      if (lane == 0 && t0 + i < T) L[(t0 + i) * E + e] = s;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ select
+// (value, index) order used for every top-k: larger value first, equal
+// values ordered by the lower index.
+__device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
+  return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// Wave-wide best (value, index) among candidates; lanes without one pass
+// index INT_MAX.
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(v, o, kWave);
+    const int i2 = __shfl_xor(i, o, kWave);
+    if (i2 != INT_MAX && (i == INT_MAX || better(v2, i2, v, i))) {
+      v = v2;
+      i = i2;
+    }
+  }
+}
+
+// One wave per token; EPL = experts per lane (expert lane + 64*j).
+template <int EPL>
+__global__ void __launch_bounds__(256)
+select_kernel(const float* __restrict__ L, const float* __restrict__ bias,
+              int32_t* __restrict__ ids, float* __restrict__ wout,
+              float* __restrict__ probpart, int64_t T, int E, int k,
+              int router, int norm, float scaling, int n_group,
+              int topk_group) {
+  __shared__ float sel_lds[kSelectWaves][EPL * kWave];
+  __shared__ float pacc[kSelectWaves][EPL * kWave];
+  const int lane = threadIdx.x % kWave;
+  const int wv = threadIdx.x / kWave;
+  float pa[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) pa[j] = 0.f;
+  const bool want_p = probpart != nullptr;
+  const int G = router == MOE_ROUTER_SIGMOID_GROUP ? E / n_group : 0;
+
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kSelectWaves + wv; t < T;
+       t += static_cast<int64_t>(gridDim.x) * kSelectWaves) {
+    float v[EPL];
+    float sc[EPL];  // sigmoid scores (SIGMOID_GROUP)
+    uint32_t cand = 0;  // bit j: expert lane+64j may still be chosen
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + kWave * j;
+      v[j] = e < E ? L[t * E + e] : 0.f;
+      sc[j] = 0.f;
+      if (e < E) cand |= 1u << j;
+    }
+    if (router == MOE_ROUTER_SIGMOID_GROUP) {
+      // s = sigmoid(L) held in fp32 (evaluated in fp64, rounded once);
+      // selection score s + bias, also fp32
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + kWave * j;
+        sc[j] = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(v[j]))));
+        v[j] = sc[j] + ((bias != nullptr && e < E) ? bias[e] : 0.f);
+        if (e < E) sel_lds[wv][e] = v[j];
+      }
+      if (topk_group < n_group) {
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // group score: sum of the two largest selection scores
+        float gs = 0.f;
+        int gi = INT_MAX;
+        if (lane < n_group) {
+          float a = -INFINITY, b = -INFINITY;
+          for (int q = 0; q < G; ++q) {
+            const float y = sel_lds[wv][lane * G + q];
+            if (y > a) {
+              b = a;
+              a = y;
+            } else if (y > b) {
+              b = y;
+            }
+          }
+          gs = a + b;
+          gi = lane;
+        }
+        // keep the best topk_group groups (ties to the lower group)
+        uint64_t kept = 0;
+        for (int r = 0; r < topk_group; ++r) {
+          float bv = gs;
+          int bi = ((kept >> lane) & 1ull) ? INT_MAX : gi;
+          wave_best(bv, bi);
+          kept |= 1ull << bi;
+        }
+#pragma unroll
+        for (int j = 0; j < EPL; ++j) {
+          const int e = lane + kWave * j;
+          if (e < E && !((kept >> (e / G)) & 1ull)) cand &= ~(1u << j);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    // top-k by repeated wave argmax; lane r keeps the r-th winner
+    int my_id = 0;
+    float my_val = 0.f;
+    for (int r = 0; r < k; ++r) {
+      float bv = 0.f;
+      int bi = INT_MAX;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const int e = lane + kWave * j;
+        if (((cand >> j) & 1u) && (bi == INT_MAX || better(v[j], e, bv, bi))) {
+          bv = v[j];
+          bi = e;
+        }
+      }
+      wave_best(bv, bi);
+      if (lane == r) {
+        my_id = bi;
+        my_val = bv;
+      }
+      if ((bi % kWave) == lane) cand &= ~(1u << (bi / kWave));
+    }
+    float wk;
+    if (router == MOE_ROUTER_SOFTMAX_TOPK) {
+      const float m = __shfl(my_val, 0, kWave);  // the largest logit
+      float S = 0.f;
+      if (want_p || !norm) {
+        float part = 0.f;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (lane + kWave * j < E) part += expf(v[j] - m);
+        S = wave_sum(part);
+      }
+      if (want_p) {
+        const float inv = 1.f / S;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (lane + kWave * j < E) pa[j] += expf(v[j] - m) * inv;
+      }
+      const float ex = lane < k ? expf(my_val - m) : 0.f;
+      const float den = norm ? wave_sum(ex) : S;
+      wk = ex / den;
+    } else {
+      // raw sigmoid of the chosen expert (bias excluded), fetched from the
+      // lane that holds it
+      float s_e = 0.f;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const float y = __shfl(sc[j], my_id % kWave, kWave);
+        if (my_id / kWave == j) s_e = y;
+      }
+      if (lane >= k) s_e = 0.f;
+      const float den = wave_sum(s_e) + 1e-20f;
+      wk = (norm ? s_e / den : s_e) * scaling;
+    }
+    if (lane < k) {
+      ids[t * k + lane] = my_id;
+      wout[t * k + lane] = wk;
+    }
+  }
+  if (want_p) {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) pacc[wv][lane + kWave * j] = pa[j];
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      float s = 0.f;
+      for (int q = 0; q < kSelectWaves; ++q) s += pacc[q][e];
+      probpart[static_cast<int64_t>(blockIdx.x) * E + e] = s;
+    }
+  }
+}
+
+__global__ void prob_finalize_kernel(const float* __restrict__ part, int nb,
+                                     int E, float* __restrict__ out) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  float s = 0.f;
+  for (int b = 0; b < nb; ++b) s += part[static_cast<int64_t>(b) * E + e];
+  out[e] = s;
+}
+
+template <typename XT, typename WT>
+hipError_t logits_dispatch(const Dims& D, const void* x, const void* wr,
+                           float* L, hipStream_t s) {
+  const XT* xp = static_cast<const XT*>(x);
+  const WT* wp = static_cast<const WT*>(wr);
+  if (D.T <= 64 && (D.d % 8) == 0) {
+    dim3 grid((D.E + 3) / 4);
+    hipLaunchKernelGGL((logits_rowdot_kernel<XT, WT>), grid, dim3(256), 0, s,
+                       xp, wp, L, D.T, D.E, D.d);
+  } else {
+    dim3 grid(static_cast<unsigned>((D.T + LT - 1) / LT), (D.E + LE - 1) / LE);
+    hipLaunchKernelGGL((logits_tiled_kernel<XT, WT>), grid, dim3(256), 0, s,
+                       xp, wp, L, D.T, D.E, D.d);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_router_logits(const Dims& D, int act_dtype, int router_dtype,
+                                const void* x, const void* wr, float* logits,
+                                hipStream_t s) {
+  const bool xb = act_dtype == MOE_DTYPE_BF16;
+  const bool wb = router_dtype == MOE_DTYPE_BF16;
+  if (xb && wb) return logits_dispatch<uint16_t, uint16_t>(D, x, wr, logits, s);
+  if (xb) return logits_dispatch<uint16_t, float>(D, x, wr, logits, s);
+  if (wb) return logits_dispatch<float, uint16_t>(D, x, wr, logits, s);
+  return logits_dispatch<float, float>(D, x, wr, logits, s);
+}
+
+hipError_t launch_router_select(const Dims& D, const moe_spec& sp,
+                                const float* logits, const float* bias,
+                                int32_t* ids, float* w, float* probpart,
+                                int nblocks, hipStream_t s) {
+  const int epl = (D.E + kWave - 1) / kWave;
+  const float scaling =
+      sp.router == MOE_ROUTER_SIGMOID_GROUP ? sp.routed_scaling : 1.0f;
+#define MOE_SELECT(N)                                                        \
+  hipLaunchKernelGGL((select_kernel<N>), dim3(nblocks), dim3(256), 0, s,     \
+                     logits, bias, ids, w, probpart, D.T, D.E, D.k, sp.router, \
+                     sp.norm_topk_prob, scaling, sp.n_group, sp.topk_group)
+  if (epl <= 1) MOE_SELECT(1);
+  else if (epl <= 2) MOE_SELECT(2);
+  else if (epl <= 4) MOE_SELECT(4);
+  else if (epl <= 8) MOE_SELECT(8);
+  else MOE_SELECT(16);
+#undef MOE_SELECT
+  return hipGetLastError();
+}
+
+hipError_t launch_prob_finalize(const Dims& D, const float* probpart,
+                                int nblocks, float* prob_sum, hipStream_t s) {
+  hipLaunchKernelGGL(prob_finalize_kernel, dim3((D.E + 255) / 256), dim3(256),
+                     0, s, probpart, nblocks, D.E, prob_sum);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,194 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and
+compare every stage with the CPU oracle, to the bars of the parity protocol:
+
+  * router logits within the dot-product forward error bound
+    |L_gpu - L| <= gamma_d * sum_j |x_j Wr_ej|, gamma_d = d u / (1 - d u),
+    u = 2^-24 (fp32 accumulation of exact products);
+  * routing ids bit-exact against the oracle's selection run on the GPU's
+    own fp32 logits (near-tie tokens, margin < 1e-6, are reported; softmax
+    ranking is decided on identical fp32 values, so all tokens must agree);
+    weights within 1e-6;
+  * dispatch (counts, offsets, permutation, slot rows, drops) bit-exact;
+  * layer output max |err| <= 2e-2 * RMS(ref) for bf16 and <= 1e-4 *
+    RMS(ref) for fp32; fully dropped tokens exactly 0.
+"""
+from __future__ import annotations
+
+import math
+import sys
+import time
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+import torch
+
+import mixture_experts_layer_group_amd as moe
+import oracle
+import synth
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-4
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def spec_dict(cfg) -> Dict:
+    return {"router": cfg.router, "E": cfg.E, "top_k": cfg.top_k, "act": cfg.act,
+            "capacity_factor": cfg.capacity_factor, "shared_experts": cfg.shared_experts,
+            "norm_topk_prob": cfg.norm_topk_prob, "routed_scaling": cfg.routed_scaling,
+            "n_group": cfg.n_group, "topk_group": cfg.topk_group}
+
+
+def make_inputs(cfg, base=synth.SEED_BASE, device="cuda"):
+    return synth.make_layer_inputs(cfg, device, base=base)
+
+
+def run_layer(cfg, inp, T: Optional[int] = None):
+    """moe_layer_forward with every optional output requested."""
+    T = cfg.T if T is None else T
+    spec = moe.spec_from_config(cfg)
+    dev = "cuda"
+    adt = torch.bfloat16 if cfg.act_dtype == synth.BF16 else torch.float32
+    E, k = cfg.E, cfg.top_k
+    r = {
+        "out": torch.full((T, cfg.d), float("nan"), dtype=adt, device=dev),
+        "topk_ids": torch.full((T, k), -7, dtype=torch.int32, device=dev),
+        "topk_w": torch.zeros((T, k), dtype=torch.float32, device=dev),
+        "logits": torch.zeros((T, E), dtype=torch.float32, device=dev),
+        "counts_pre": torch.zeros(E, dtype=torch.int32, device=dev),
+        "offsets": torch.zeros(E + 1, dtype=torch.int32, device=dev),
+        "dropped": torch.zeros(1, dtype=torch.int32, device=dev),
+        "prob_sum": torch.zeros(E, dtype=torch.float32, device=dev)
+        if cfg.router == synth.SOFTMAX_TOPK else None,
+        "slot_row": torch.full((T, k), -7, dtype=torch.int32, device=dev),
+        "sorted_token": torch.full((max(1, T * k),), -7, dtype=torch.int32, device=dev),
+    }
+    ws = moe.workspace(spec, T)
+    stats = moe.layer_stats(**{n: r[n] for n in moe._S_FIELDS})
+    moe.moe_layer_forward(spec, T, inp["x"], inp["w_router"], inp["expert_bias"],
+                          inp, r["out"], stats=stats, workspace=ws)
+    torch.cuda.synchronize()
+    return r
+
+
+def bank_for(cfg, inp) -> oracle.ExpertBank:
+    """Oracle expert bank that copies one expert's tensors to the host on
+    demand (exact copies of what the GPU read)."""
+    cache: Dict = {}
+
+    def fetch(name, e):
+        key = (name, e)
+        if key not in cache:
+            if len(cache) > 48:
+                cache.clear()
+            cache[key] = synth.host_array(inp[name][e])
+        return cache[key]
+
+    return oracle.ExpertBank(fetch, cfg.act, u4=cfg.weight_dtype == synth.U4,
+                             group=cfg.quant_group)
+
+
+def logits_bound(x_h, wr_h, d):
+    u = 2.0 ** -24
+    gamma = d * u / (1 - d * u)
+    X = np.abs(oracle.as_f64(x_h))
+    W = np.abs(oracle.as_f64(wr_h))
+    return gamma * (X @ W.T)
+
+
+def check_route(cfg, inp, r, full_logits_check=True):
+    """Logits bound, ids bit-exact vs the oracle on the GPU logits, weights
+    within 1e-6.  Returns (ids_gpu, w_oracle (fp64), flags)."""
+    spec = spec_dict(cfg)
+    L_gpu = r["logits"].cpu().numpy()
+    x_h, wr_h = synth.host_array(inp["x"]), synth.host_array(inp["w_router"])
+    bias_h = synth.host_array(inp["expert_bias"])
+    if full_logits_check:
+        L_ref = oracle.router_logits(x_h, wr_h)
+        bound = logits_bound(x_h, wr_h, cfg.d)
+        err = np.abs(L_gpu.astype(np.float64) - L_ref)
+        assert np.all(err <= bound), f"logits outside the fp32 dot bound: {(err - bound).max()}"
+    ids_o, w_o, p_o = oracle.route_from_logits(L_gpu, spec, bias_h)
+    flags = oracle.near_tie_flags(L_gpu, spec, bias_h)
+    ids_g = r["topk_ids"].cpu().numpy()
+    w_g = r["topk_w"].cpu().numpy().astype(np.float64)
+    bad = np.any(ids_g != ids_o, axis=1)
+    log(f"  route: {int(flags.sum())} near-tie tokens, {int(bad.sum())} id mismatches "
+        f"({int((bad & ~flags).sum())} unflagged)")
+    assert not np.any(bad & ~flags), "routing ids differ on unflagged tokens"
+    if cfg.router == synth.SOFTMAX_TOPK:
+        assert not np.any(bad), "softmax ranking is decided on identical fp32 values"
+    ok = ~bad
+    assert np.all(np.abs(w_g[ok] - w_o[ok]) <= 1e-6), \
+        f"routing weights off by {np.abs(w_g[ok] - w_o[ok]).max()}"
+    # downstream stages follow the GPU routing: a flagged token whose ids
+    # differ keeps the GPU's ids and weights together
+    w_o = w_o.copy()
+    w_o[bad] = w_g[bad]
+    if r.get("prob_sum") is not None and p_o is not None:
+        ps = r["prob_sum"].cpu().numpy().astype(np.float64)
+        ref = p_o.sum(axis=0)
+        assert np.all(np.abs(ps - ref) <= 1e-6 * cfg.T + 1e-5 * np.abs(ref)), \
+            f"prob_sum off by {np.abs(ps - ref).max()}"
+    return ids_g, w_o, flags
+
+
+def check_dispatch(cfg, ids_g, r):
+    T, k, E = cfg.T, cfg.top_k, cfg.E
+    cap = oracle.capacity_for(T, k, E, cfg.capacity_factor)
+    d = oracle.dispatch(ids_g, E, cap)
+    n = int(d["offsets"][E])
+    assert np.array_equal(r["counts_pre"].cpu().numpy(), d["count_pre"]), "counts_pre"
+    assert np.array_equal(r["offsets"].cpu().numpy(), d["offsets"]), "offsets"
+    assert int(r["dropped"].cpu().item()) == d["dropped"], "dropped"
+    assert np.array_equal(r["sorted_token"].cpu().numpy()[:n], d["sorted_token"]), "sorted_token"
+    assert np.array_equal(r["slot_row"].cpu().numpy(), d["slot_row"]), "slot_row"
+    log(f"  dispatch: capacity {cap}, kept {n}, dropped {d['dropped']} (bit-exact)")
+    return d
+
+
+def check_output(cfg, inp, r, ids_g, w_o, disp, tokens: Optional[Sequence[int]] = None):
+    tol = BF16_TOL if cfg.act_dtype == synth.BF16 else F32_TOL
+    toks = list(range(cfg.T)) if tokens is None else list(tokens)
+    bank = bank_for(cfg, inp)
+    t0 = time.time()
+    ref = oracle.ffn_and_combine(synth.host_array(inp["x"]), ids_g, w_o, disp, bank,
+                                 spec_dict(cfg), toks)
+    got = r["out"].float().cpu().numpy().astype(np.float64)[toks]
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    err = float(np.abs(got - ref).max())
+    log(f"  output: {len(toks)} tokens, max|err| {err:.3e}, RMS(ref) {rms:.3e}, "
+        f"ratio {err / max(rms, 1e-300):.2e} (bar {tol}), oracle {time.time() - t0:.1f}s")
+    assert err <= tol * rms, f"max|err| {err} > {tol} * RMS {rms}"
+    # fully dropped tokens with no shared expert are exactly zero
+    if cfg.shared_experts == 0:
+        sr = disp["slot_row"]
+        dead = [j for j, t in enumerate(toks) if np.all(sr[t] < 0)]
+        if dead:
+            assert np.all(got[dead] == 0.0), "fully dropped tokens must give exactly 0"
+            log(f"  {len(dead)} fully dropped tokens are exactly 0")
+    return err, rms
+
+
+def check_end_to_end_routing(cfg, inp, ids_g):
+    """Routing from the oracle's own fp64 logits agrees outside near ties."""
+    spec = spec_dict(cfg)
+    x_h, wr_h = synth.host_array(inp["x"]), synth.host_array(inp["w_router"])
+    bias_h = synth.host_array(inp["expert_bias"])
+    L = oracle.router_logits(x_h, wr_h)
+    ids_o, _, _ = oracle.route_from_logits(L, spec, bias_h)
+    flags = oracle.near_tie_flags(L, spec, bias_h)
+    bad = np.any(ids_o != ids_g, axis=1)
+    log(f"  end-to-end routing: {int(bad.sum())} tokens differ, {int((bad & ~flags).sum())} "
+        f"unflagged (near ties {int(flags.sum())})")
+    assert not np.any(bad & ~flags)
+
+
+def full_check(cfg, inp, r, tokens=None, full_logits_check=True):
+    ids_g, w_o, flags = check_route(cfg, inp, r, full_logits_check)
+    disp = check_dispatch(cfg, ids_g, r)
+    check_output(cfg, inp, r, ids_g, w_o, disp, tokens)
+    return ids_g, disp

@@ -1,0 +1,112 @@
+"""CPU checks of the C-ABI library: it loads without a GPU, exports every
+symbol that include/moe.h declares, and its host-only calls (validation,
+capacity, workspace size, status strings) behave as documented.  No compute
+call is made here."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_group_amd as moe
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return sorted(set(re.findall(r"^(?:moe_status|const char\*)\s+(moe_\w+)\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.library()
+    syms = header_symbols()
+    assert len(syms) == 9
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert sorted(moe.EXPORTS) == syms
+
+
+def base(**kw):
+    d = dict(E=8, top_k=2, d=128, F=256)
+    d.update(kw)
+    return moe.make_spec(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    ({"E": 1, "top_k": 1}, 1),
+    ({"top_k": 0}, 2),
+    ({"top_k": 9}, 2),
+    ({"capacity_factor": 0.5}, 3),
+    ({"capacity_factor": -1.0}, 1),
+    ({"capacity_factor": 1.0}, 0),
+    ({"router": "sigmoid_group", "n_group": 3, "topk_group": 1}, 1),   # 8 % 3
+    ({"router": "sigmoid_group", "n_group": 8, "topk_group": 1}, 1),   # groups of 1
+    ({"router": "sigmoid_group", "n_group": 4, "topk_group": 0}, 1),
+    ({"router": "sigmoid_group", "n_group": 4, "topk_group": 5}, 1),
+    ({"router": "sigmoid_group", "n_group": 4, "topk_group": 1, "top_k": 3}, 1),
+    ({"router": "sigmoid_group", "n_group": 4, "topk_group": 2, "top_k": 4}, 0),
+    ({"shared_experts": 1, "shared_F": 0}, 1),
+    ({"weight_dtype": "u4", "quant_group": 32}, 1),
+    ({"weight_dtype": "u4", "d": 96}, 1),
+    ({"weight_dtype": "f32"}, 1),                 # bf16 activations, f32 weights
+    ({"act_dtype": "f32", "weight_dtype": "bf16"}, 7),
+    ({"d": 100}, 7),
+    ({"act_dtype": "f32", "weight_dtype": "f32", "d": 40, "F": 24}, 0),
+    ({"d": 96}, 7),                               # bf16 needs multiples of 64
+])
+def test_validation_codes(kw, status):
+    assert moe.moe_spec_validate(base(**kw), 16) == status
+
+
+def test_shape_errors():
+    assert moe.moe_spec_validate(base(), -1) == 4
+    assert moe.moe_spec_validate(base(top_k=8), 2 ** 31) == 4
+
+
+def test_capacity_matches_oracle_formula():
+    for T, k, E, cf in [(64, 2, 8, 1.25), (16384, 8, 128, 1.0), (7, 3, 5, 1.5),
+                        (3, 1, 8, 1.0), (1000, 2, 6, 1.1), (1, 1, 2, 1.0)]:
+        spec = base(E=E, top_k=k, capacity_factor=cf)
+        assert moe.moe_capacity(spec, T) == oracle.capacity_for(T, k, E, cf)
+    assert moe.moe_capacity(base(), 100) == 2 ** 63 - 1
+
+
+def test_workspace_sizes():
+    cfg = synth.CONFIGS[2]
+    spec = moe.spec_from_config(cfg)
+    a = moe.moe_workspace_size(spec, 1000)
+    b = moe.moe_workspace_size(spec, 4096)
+    assert 0 < a < b
+    # holds at least the hidden activation and expert outputs in bf16
+    assert b >= 4096 * 2 * (cfg.F + cfg.d) * 2
+    for c in synth.CONFIGS.values():
+        assert moe.moe_workspace_size(moe.spec_from_config(c), c.T) > 0
+
+
+def test_status_strings():
+    for code in range(8):
+        assert len(moe.status_string(code)) > 0
+    assert moe.status_string(99) == "unknown status"
+
+
+def test_errors_raise_before_any_launch():
+    """Invalid specs are rejected on the host: these calls pass no device
+    memory at all and must fail with the validation status."""
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_layer_forward(base(top_k=0), 4, 0, 0, None, {}, 0, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_route(base(), 4, 0, 0, None, 0, 0, stream=0)
+    assert e.value.status == 4  # null pointers
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_route(base(), 4, 16, 16, None, 16, 16, stream=0)
+    assert e.value.status == 5  # no workspace
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_route(base(), 4, 16, 16, 32, 16, 16, workspace=16, ws_bytes=1 << 40,
+                      stream=0)
+    assert e.value.status == 1  # a selection bias with softmax routing
