@@ -91,7 +91,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload id (1-5)")
-    ap.add_argument("--cpu-sample", type=int, default=48,
+    ap.add_argument("--cpu-sample", type=int, default=256,
                     help="tokens whose expert FFN the CPU oracle evaluates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -109,8 +109,8 @@ def main() -> int:
     inp = synth.make_layer_inputs(cfg, "cuda")
     spec = moe.spec_from_config(cfg)
     T = cfg.T
-    adt = torch.bfloat16 if cfg.act_dtype == "bf16" else torch.float32
-    out = torch.empty((T, cfg.d), dtype=adt, device="cuda")
+    odt = torch.bfloat16 if cfg.out_dtype == "bf16" else torch.float32
+    out = torch.empty((T, cfg.d), dtype=odt, device="cuda")
     ws = moe.workspace(spec, T)
     w = moe.expert_weights(inp)
     dev = "cuda"
@@ -139,8 +139,8 @@ def main() -> int:
     # the grouped expert FFN alone (both GEMMs), each call timed with HIP
     # events on the stream the kernels run on
     n_kept = int(offsets[-1].item())
-    y = torch.empty((T * cfg.top_k, cfg.d), dtype=adt, device=dev)
-    ysh = (torch.empty((cfg.shared_experts * T, cfg.d), dtype=adt, device=dev)
+    y = torch.empty((T * cfg.top_k, cfg.d), dtype=torch.float32, device=dev)
+    ysh = (torch.empty((cfg.shared_experts * T, cfg.d), dtype=torch.float32, device=dev)
            if cfg.shared_experts else None)
     for _ in range(2):
         moe.moe_grouped_ffn(spec, T, offsets, sorted_token, inp["x"], w, y, ysh, ws)

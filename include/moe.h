@@ -72,6 +72,8 @@ typedef struct moe_spec {
   int32_t weight_dtype;    /* routed expert weights: F32, BF16 or U4_AFFINE */
   int32_t router_dtype;    /* router weight Wr: F32 or BF16 */
   int32_t quant_group;     /* U4_AFFINE group size along K (64) */
+  int32_t out_dtype;       /* F32 or BF16: the layer output (the combine
+                              accumulates in fp32 either way) */
 } moe_spec;
 
 /* Expert weights, device pointers, the Edge0 page's SEPARATE layout: one
@@ -127,7 +129,8 @@ typedef void* moe_stream_t;
  * validation of the blog page's MoEConfig / Router / MoELayer:
  *   MOE_ERR_INVALID_TOPK        k outside [1, E]
  *   MOE_ERR_CAPACITY_TOO_TIGHT  0 < capacity_factor < 1
- *   MOE_ERR_INVALID_ARG         E < 2; d, F < 1; unknown enum; negative
+ *   MOE_ERR_INVALID_ARG         E < 2; d, F < 1; unknown enum (out_dtype
+ *     must be F32 or BF16); negative
  *     capacity factor; SIGMOID_GROUP with n_group < 1, E % n_group != 0,
  *     E/n_group < 2 (a group's top-two is undefined), topk_group outside
  *     [1, n_group], or k > topk_group*E/n_group; shared experts with
@@ -208,13 +211,15 @@ moe_status moe_dispatch(const moe_spec* spec, int64_t T,
  * and for every shared expert s and token t
  *   y_shared[s*T + t] = FFN_shared_s(x[t]).
  * SwiGLU: W_down (silu(W_gate x) * (W_up x)); ReLU: W_down relu(W_gate x).
- * bf16 activations use bf16 MFMA with fp32 accumulation and round the
- * hidden activation to bf16 between the two products.
+ * bf16 activations use matrix cores with fp32 accumulation: bf16 x bf16
+ * for the gate/up product, whose hidden activation is rounded to fp16
+ * (saturating at +-65504), then fp16 x fp16 for the down product (the bf16
+ * weights are converted exactly in registers); expert outputs stay fp32.
  *  offsets, sorted_token  device, as produced by moe_dispatch
  *  x         device [T,d] act dtype
  *  weights   host struct of device pointers
- *  y_rows    device out [T*k, d] act dtype (rows >= offsets[E] untouched)
- *  y_shared  device out [S*T, d] act dtype, or NULL when S = 0 */
+ *  y_rows    device out [T*k, d] fp32 (rows >= offsets[E] untouched)
+ *  y_shared  device out [S*T, d] fp32, or NULL when S = 0 */
 moe_status moe_grouped_ffn(const moe_spec* spec, int64_t T,
                            const int32_t* offsets, const int32_t* sorted_token,
                            const void* x, const moe_expert_weights* weights,
@@ -228,9 +233,9 @@ moe_status moe_grouped_ffn(const moe_spec* spec, int64_t T,
  *            + sum_s y_shared[s*T + t]
  * accumulated in fp32 in the fixed order i = 0..k-1 then s (no atomics);
  * dropped slots add nothing and the kept weights are not renormalised.
- *  y_rows device [T*k, d], y_shared device [S*T, d] or NULL, act dtype
+ *  y_rows device [T*k, d] fp32, y_shared device [S*T, d] fp32 or NULL
  *  slot_row device [T,k] int32, topk_w device [T,k] fp32
- *  out device out [T,d] act dtype */
+ *  out device out [T,d] out dtype */
 moe_status moe_combine(const moe_spec* spec, int64_t T, const void* y_rows,
                        const int32_t* slot_row, const float* topk_w,
                        const void* y_shared, void* out, moe_stream_t stream);
@@ -242,7 +247,7 @@ moe_status moe_combine(const moe_spec* spec, int64_t T, const void* y_rows,
  * dropped and which has no shared expert gets exactly 0.
  *  x, w_router, expert_bias  as moe_route
  *  weights   host struct of device pointers (see moe_expert_weights)
- *  out       device out [T,d] act dtype
+ *  out       device out [T,d] out dtype
  *  stats     host struct of optional device outputs, or NULL
  *  workspace device, at least moe_workspace_size bytes */
 moe_status moe_layer_forward(const moe_spec* spec, int64_t T, const void* x,

@@ -36,7 +36,7 @@ class MoESpec(ctypes.Structure):
                 ("shared_experts", ctypes.c_int32), ("shared_ffn", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("router_dtype", ctypes.c_int32),
-                ("quant_group", ctypes.c_int32)]
+                ("quant_group", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
 
 
 _W_FIELDS = ["gate", "up", "down", "gate_scale", "gate_bias", "up_scale", "up_bias",
@@ -108,11 +108,13 @@ def make_spec(E: int, top_k: int, d: int, F: int, router: str = "softmax_topk",
               n_group: int = 0, topk_group: int = 0, capacity_factor: float = 0.0,
               shared_experts: int = 0, shared_F: int = 0, act: str = "swiglu",
               act_dtype: str = "bf16", weight_dtype: str = "bf16",
-              router_dtype: str = "f32", quant_group: int = 64) -> MoESpec:
+              router_dtype: str = "f32", quant_group: int = 64,
+              out_dtype: str = "f32") -> MoESpec:
     return MoESpec(E, top_k, d, F, ROUTER[router], int(bool(norm_topk_prob)),
                    float(routed_scaling), n_group, topk_group, float(capacity_factor),
                    shared_experts, shared_F, ACT[act], DTYPE[act_dtype],
-                   DTYPE[weight_dtype], DTYPE[router_dtype], quant_group)
+                   DTYPE[weight_dtype], DTYPE[router_dtype], quant_group,
+                   DTYPE[out_dtype])
 
 
 def spec_from_config(cfg) -> MoESpec:
@@ -122,7 +124,7 @@ def spec_from_config(cfg) -> MoESpec:
                      cfg.routed_scaling, cfg.n_group, cfg.topk_group,
                      cfg.capacity_factor, cfg.shared_experts, cfg.shared_F, cfg.act,
                      cfg.act_dtype, cfg.weight_dtype, cfg.router_dtype,
-                     cfg.quant_group)
+                     cfg.quant_group, getattr(cfg, "out_dtype", "f32"))
 
 
 # ---------------------------------------------------------------- helpers

@@ -11,15 +11,6 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ void load8(const uint16_t* p, float* v) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v[2 * j] = __uint_as_float(w[j] << 16);
-    v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-  }
-}
 __device__ __forceinline__ void load8(const float* p, float* v) {
   const float4 a = reinterpret_cast<const float4*>(p)[0];
   const float4 b = reinterpret_cast<const float4*>(p)[1];
@@ -41,12 +32,13 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
 
 constexpr int kMaxSlots = 64;
 
-// One block per token.
-template <typename T>
+// One block per token; expert outputs are fp32, the result is written in
+// the output type.
+template <typename OutT>
 __global__ void __launch_bounds__(256)
-combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ slot_row,
-               const float* __restrict__ topk_w, const T* __restrict__ ysh,
-               T* __restrict__ out, int64_t Tn, int k, int S, int d) {
+combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ slot_row,
+               const float* __restrict__ topk_w, const float* __restrict__ ysh,
+               OutT* __restrict__ out, int64_t Tn, int k, int S, int d) {
   __shared__ int32_t rows[kMaxSlots];
   __shared__ float wts[kMaxSlots];
   const int64_t t = blockIdx.x;
@@ -84,16 +76,15 @@ hipError_t launch_combine(const Dims& D, const void* y_rows,
   if (D.k > kMaxSlots) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(D.T));
   const int S = y_shared ? D.S : 0;
-  if (D.bf16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(y_rows), slot_row, topk_w,
-                       static_cast<const uint16_t*>(y_shared),
-                       static_cast<uint16_t*>(out), D.T, D.k, S, D.d);
+  const float* y = static_cast<const float*>(y_rows);
+  const float* ys = static_cast<const float*>(y_shared);
+  if (D.out_bf16)
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, y,
+                       slot_row, topk_w, ys, static_cast<uint16_t*>(out), D.T,
+                       D.k, S, D.d);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(y_rows), slot_row, topk_w,
-                       static_cast<const float*>(y_shared),
-                       static_cast<float*>(out), D.T, D.k, S, D.d);
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, y, slot_row,
+                       topk_w, ys, static_cast<float*>(out), D.T, D.k, S, D.d);
   return hipGetLastError();
 }
 

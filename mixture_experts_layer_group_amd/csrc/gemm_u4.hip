@@ -12,8 +12,9 @@
 //
 // One kernel serves both products:
 //   up   : unit = hidden column f; the lane loads the gate row f and the up
-//          row f, the epilogue writes H = silu(gate) * up (bf16)
-//   down : unit = output column n of W_down, writes Y (bf16)
+//          row f, the epilogue writes H = silu(gate) * up (fp16, as on the
+//          matrix-core path)
+//   down : unit = output column n of W_down, writes Y (fp32)
 // LPR lanes share one unit and each lane streams VPL 16-byte vectors of it
 // per pass; a wave works on 64/LPR units at once and reduces inside each
 // lane group.
@@ -43,14 +44,14 @@ template <bool PAIR, int LPR, int VPL>
 __global__ void __launch_bounds__(256)
 u4_kernel(const int32_t* __restrict__ offsets,
           const int32_t* __restrict__ sorted_token,  // nullptr: a rows direct
-          const uint16_t* __restrict__ a,             // [.., K] bf16
+          const uint16_t* __restrict__ a,             // [.., K] bf16 x or fp16 H
           const uint32_t* __restrict__ q0,            // [E][N][K/8]
           const uint16_t* __restrict__ s0,            // [E][N][K/G]
           const uint16_t* __restrict__ b0,
           const uint32_t* __restrict__ q1,            // up (PAIR)
           const uint16_t* __restrict__ s1,
           const uint16_t* __restrict__ b1,
-          uint16_t* __restrict__ out, int N, int K, int G) {
+          void* __restrict__ out, int N, int K, int G) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [kRC][K]
   const int e = blockIdx.x;
   const int32_t row0 = offsets[e];
@@ -123,8 +124,15 @@ u4_kernel(const int32_t* __restrict__ offsets,
               const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
               for (int m = 0; m < 4; ++m) {
-                xf[8 * h + 2 * m] = __uint_as_float(tw[m] << 16);
-                xf[8 * h + 2 * m + 1] = __uint_as_float(tw[m] & 0xffff0000u);
+                if (PAIR) {  // bf16 tokens
+                  xf[8 * h + 2 * m] = __uint_as_float(tw[m] << 16);
+                  xf[8 * h + 2 * m + 1] = __uint_as_float(tw[m] & 0xffff0000u);
+                } else {     // fp16 hidden rows
+                  xf[8 * h + 2 * m] = static_cast<float>(
+                      __builtin_bit_cast(_Float16, static_cast<uint16_t>(tw[m] & 0xffffu)));
+                  xf[8 * h + 2 * m + 1] = static_cast<float>(
+                      __builtin_bit_cast(_Float16, static_cast<uint16_t>(tw[m] >> 16)));
+                }
               }
             }
             float xsum = 0.f, pa = 0.f, pb = 0.f;
@@ -152,9 +160,14 @@ u4_kernel(const int32_t* __restrict__ offsets,
 #pragma unroll
         for (int r = 0; r < kRC; ++r) {
           if (r >= nr) break;
-          float v = acc0[r];
-          if (PAIR) v = v / (1.f + __expf(-v)) * acc1[r];
-          out[static_cast<int64_t>(row0 + rc0 + r) * N + u] = f32_to_bf16(v);
+          const int64_t o = static_cast<int64_t>(row0 + rc0 + r) * N + u;
+          if (PAIR) {  // hidden activation, fp16 (saturating)
+            float h = acc0[r] / (1.f + __expf(-acc0[r])) * acc1[r];
+            h = fminf(fmaxf(h, -65504.f), 65504.f);
+            static_cast<_Float16*>(out)[o] = static_cast<_Float16>(h);
+          }
+          else  // expert output, fp32
+            static_cast<float*>(out)[o] = acc0[r];
         }
       }
     }
@@ -176,7 +189,7 @@ hipError_t launch_u4(int K, dim3 grid, size_t lds, hipStream_t s,
                      const int32_t* offsets, const int32_t* st,
                      const uint16_t* a, const uint32_t* q0, const uint16_t* s0,
                      const uint16_t* b0, const uint32_t* q1, const uint16_t* s1,
-                     const uint16_t* b1, uint16_t* out, int N, int G) {
+                     const uint16_t* b1, void* out, int N, int G) {
   int lpr, vpl;
   pick_shape(K, &lpr, &vpl);
 #define MOE_U4(L, V)                                                          \
@@ -213,7 +226,7 @@ hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
         static_cast<const uint16_t*>(w.gate_scale),
         static_cast<const uint16_t*>(w.gate_bias),
         static_cast<const uint32_t*>(w.up), static_cast<const uint16_t*>(w.up_scale),
-        static_cast<const uint16_t*>(w.up_bias), static_cast<uint16_t*>(H), D.F,
+        static_cast<const uint16_t*>(w.up_bias), H, D.F,
         group);
     if (err != hipSuccess) return err;
   }
@@ -225,7 +238,7 @@ hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
         static_cast<const uint16_t*>(H), static_cast<const uint32_t*>(w.down),
         static_cast<const uint16_t*>(w.down_scale),
         static_cast<const uint16_t*>(w.down_bias), nullptr, nullptr, nullptr,
-        static_cast<uint16_t*>(Y), D.d, group);
+        Y, D.d, group);
   }
 }
 

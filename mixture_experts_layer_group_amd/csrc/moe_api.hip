@@ -40,6 +40,8 @@ moe_status validate(const moe_spec* sp, int64_t T) {
     return MOE_ERR_INVALID_ARG;
   if (s.router_dtype != MOE_DTYPE_F32 && s.router_dtype != MOE_DTYPE_BF16)
     return MOE_ERR_INVALID_ARG;
+  if (s.out_dtype != MOE_DTYPE_F32 && s.out_dtype != MOE_DTYPE_BF16)
+    return MOE_ERR_INVALID_ARG;
   // Edge0 "MoE Spec and Routing" page: group-limited routing needs groups
   // of at least two experts (each group scores its top two)
   if (s.router == MOE_ROUTER_SIGMOID_GROUP) {
@@ -110,6 +112,7 @@ Dims dims_of(const moe_spec& s, int64_t T) {
   D.bf16 = s.act_dtype == MOE_DTYPE_BF16;
   D.u4 = s.weight_dtype == MOE_DTYPE_U4_AFFINE;
   D.swiglu = s.act == MOE_ACT_SWIGLU;
+  D.out_bf16 = s.out_dtype == MOE_DTYPE_BF16;
   return D;
 }
 
@@ -142,8 +145,8 @@ WsLayout layout_of(const Dims& D) {
   L.dropped = take(4);
   L.H = take(S * D.F * es);
   L.Hs = take(static_cast<size_t>(D.S) * T * D.Fs * es);
-  L.Y = take(S * D.d * es);
-  L.Ys = take(static_cast<size_t>(D.S) * T * D.d * es);
+  L.Y = take(S * D.d * 4);
+  L.Ys = take(static_cast<size_t>(D.S) * T * D.d * 4);
   L.total = o;
   return L;
 }

@@ -44,6 +44,7 @@ struct Dims {
   bool bf16;          // bf16 activations
   bool u4;            // 4-bit routed weights
   bool swiglu;
+  bool out_bf16;      // layer output in bf16 (else fp32)
 };
 
 // Workspace carve-up (byte offsets, each 256-aligned).
@@ -110,7 +111,7 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
                               const moe_expert_weights& w, void* Hs, void* Ys,
                               hipStream_t s);
 
-// combine.hip
+// combine.hip (expert outputs are fp32)
 hipError_t launch_combine(const Dims& D, const void* y_rows,
                           const int32_t* slot_row, const float* topk_w,
                           const void* y_shared, void* out, hipStream_t s);

@@ -71,6 +71,7 @@ class LayerConfig:
     weight_dtype: str = BF16
     router_dtype: str = F32
     quant_group: int = 64
+    out_dtype: str = F32  # layer output (fp32 accumulation result by default)
     # generation recipe only
     bias_range: float = 0.0  # U(-r, r) selection bias (sigmoid-group)
     zipf_s: float = 0.0  # > 0: fold a Zipf popularity prior into router rows

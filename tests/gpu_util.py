@@ -9,8 +9,10 @@ compare every stage with the CPU oracle, to the bars of the parity protocol:
     ranking is decided on identical fp32 values, so all tokens must agree);
     weights within 1e-6;
   * dispatch (counts, offsets, permutation, slot rows, drops) bit-exact;
-  * layer output max |err| <= 2e-2 * RMS(ref) for bf16 and <= 1e-4 *
-    RMS(ref) for fp32; fully dropped tokens exactly 0.
+  * layer output max |err| <= 2e-2 * RMS(ref) for bf16 arithmetic and
+    <= 1e-4 * RMS(ref) for fp32; when the output itself is stored in bf16,
+    each element may further differ by the half-ulp of that final rounding
+    (2^-8 |ref|); fully dropped tokens exactly 0.
 """
 from __future__ import annotations
 
@@ -51,10 +53,10 @@ def run_layer(cfg, inp, T: Optional[int] = None):
     T = cfg.T if T is None else T
     spec = moe.spec_from_config(cfg)
     dev = "cuda"
-    adt = torch.bfloat16 if cfg.act_dtype == synth.BF16 else torch.float32
+    odt = torch.bfloat16 if cfg.out_dtype == synth.BF16 else torch.float32
     E, k = cfg.E, cfg.top_k
     r = {
-        "out": torch.full((T, cfg.d), float("nan"), dtype=adt, device=dev),
+        "out": torch.full((T, cfg.d), float("nan"), dtype=odt, device=dev),
         "topk_ids": torch.full((T, k), -7, dtype=torch.int32, device=dev),
         "topk_w": torch.zeros((T, k), dtype=torch.float32, device=dev),
         "logits": torch.zeros((T, E), dtype=torch.float32, device=dev),
@@ -159,7 +161,11 @@ def check_output(cfg, inp, r, ids_g, w_o, disp, tokens: Optional[Sequence[int]] 
                                  spec_dict(cfg), toks)
     got = r["out"].float().cpu().numpy().astype(np.float64)[toks]
     rms = math.sqrt(float(np.mean(ref ** 2)))
-    err = float(np.abs(got - ref).max())
+    absdiff = np.abs(got - ref)
+    if cfg.out_dtype == synth.BF16:
+        # the final rounding of the output to bf16 adds at most half an ulp
+        absdiff = np.maximum(absdiff - 2.0 ** -8 * np.abs(ref), 0.0)
+    err = float(absdiff.max())
     log(f"  output: {len(toks)} tokens, max|err| {err:.3e}, RMS(ref) {rms:.3e}, "
         f"ratio {err / max(rms, 1e-300):.2e} (bar {tol}), oracle {time.time() - t0:.1f}s")
     assert err <= tol * rms, f"max|err| {err} > {tol} * RMS {rms}"
@@ -173,17 +179,54 @@ def check_output(cfg, inp, r, ids_g, w_o, disp, tokens: Optional[Sequence[int]] 
     return err, rms
 
 
+def logit_error_flags(cfg, L, B, bias):
+    """Tokens whose top-k decision could flip when every logit moves by up
+    to B[t] (the fp32 dot-product error bound of the GPU logits): the
+    boundary gap of the ranked scores is within twice the largest possible
+    score change.  Softmax ranks logits directly; sigmoid scores move by at
+    most B/4 (the sigmoid's slope is at most 1/4) and group scores, sums of
+    two of them, by at most B/2."""
+    T, E = L.shape
+    k = cfg.top_k
+    flags = np.zeros(T, dtype=bool)
+    if cfg.router == synth.SOFTMAX_TOPK:
+        if k < E:
+            srt = -np.sort(-L, axis=1)
+            flags |= (srt[:, k - 1] - srt[:, k]) <= 2 * B
+        return flags
+    s = 1.0 / (1.0 + np.exp(-L))
+    sel = s + (bias.astype(np.float64)[None, :] if bias is not None else 0.0)
+    G = E // cfg.n_group
+    grp = -np.sort(-sel.reshape(T, cfg.n_group, G), axis=2)
+    gs = grp[:, :, 0] + grp[:, :, 1]
+    if cfg.topk_group < cfg.n_group:
+        gsrt = -np.sort(-gs, axis=1)
+        flags |= (gsrt[:, cfg.topk_group - 1] - gsrt[:, cfg.topk_group]) <= 2 * (B / 2)
+        drop = oracle.rank_descending(gs)[:, cfg.topk_group:]
+        m = sel.reshape(T, cfg.n_group, G).copy()
+        m[np.arange(T)[:, None], drop, :] = -np.inf
+        sel = m.reshape(T, E)
+    if k < cfg.topk_group * G:
+        srt = -np.sort(-sel, axis=1)
+        flags |= (srt[:, k - 1] - srt[:, k]) <= 2 * (B / 4)
+    return flags
+
+
 def check_end_to_end_routing(cfg, inp, ids_g):
-    """Routing from the oracle's own fp64 logits agrees outside near ties."""
+    """Routing from the oracle's own fp64 logits agrees with the GPU's
+    except on tokens that are near ties (margin < 1e-6 of the oracle's
+    selection scores) or whose decision lies within the fp32 logit error
+    bound (see logit_error_flags)."""
     spec = spec_dict(cfg)
     x_h, wr_h = synth.host_array(inp["x"]), synth.host_array(inp["w_router"])
     bias_h = synth.host_array(inp["expert_bias"])
     L = oracle.router_logits(x_h, wr_h)
     ids_o, _, _ = oracle.route_from_logits(L, spec, bias_h)
-    flags = oracle.near_tie_flags(L, spec, bias_h)
+    B = logits_bound(x_h, wr_h, cfg.d).max(axis=1)
+    flags = oracle.near_tie_flags(L, spec, bias_h) | logit_error_flags(cfg, L, B, bias_h)
     bad = np.any(ids_o != ids_g, axis=1)
     log(f"  end-to-end routing: {int(bad.sum())} tokens differ, {int((bad & ~flags).sum())} "
-        f"unflagged (near ties {int(flags.sum())})")
+        f"unflagged (flagged {int(flags.sum())} of {cfg.T})")
     assert not np.any(bad & ~flags)
 
 

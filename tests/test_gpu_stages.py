@@ -48,6 +48,9 @@ MEDIUM = {
     # bf16 shared expert with ReLU and many tokens (several M tiles)
     "relu-shared-tiles": C("relu-shared-tiles", 112, T=1100, d=256, E=8, top_k=2, F=256,
                            act=synth.RELU, shared_experts=1, shared_F=320),
+    # bf16 layer output
+    "bf16-output": C("bf16-output", 113, T=800, d=320, E=8, top_k=2, F=448,
+                     out_dtype=synth.BF16, capacity_factor=1.25),
 }
 
 
@@ -93,7 +96,7 @@ def test_single_token_and_empty_batch():
     # T = 0 is a no-op that touches nothing
     import mixture_experts_layer_group_amd as moe
     spec = moe.spec_from_config(cfg)
-    out = torch.full((1, cfg.d), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((1, cfg.d), 7.0, dtype=torch.float32, device="cuda")
     moe.moe_layer_forward(spec, 0, inp["x"], inp["w_router"], None, inp, out,
                           workspace=torch.empty(1, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
@@ -125,10 +128,10 @@ def test_stagewise_api_matches_layer():
     xp = torch.zeros((T * k, d), dtype=torch.bfloat16, device=dev)
     moe.moe_dispatch(spec, T, ids, tw, counts, offsets, st, sw, sr, dropped,
                      inp["x"], xp, ws)
-    y = torch.zeros((T * k, d), dtype=torch.bfloat16, device=dev)
-    ysh = torch.zeros((T, d), dtype=torch.bfloat16, device=dev)
+    y = torch.zeros((T * k, d), dtype=torch.float32, device=dev)
+    ysh = torch.zeros((T, d), dtype=torch.float32, device=dev)
     moe.moe_grouped_ffn(spec, T, offsets, st, inp["x"], inp, y, ysh, ws)
-    out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
     moe.moe_combine(spec, T, y, sr, tw, ysh, out)
     torch.cuda.synchronize()
     r = gu.run_layer(cfg, inp)
