@@ -91,7 +91,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload id (1-5)")
-    ap.add_argument("--cpu-sample", type=int, default=256,
+    ap.add_argument("--cpu-sample", type=int, default=2048,
                     help="tokens whose expert FFN the CPU oracle evaluates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

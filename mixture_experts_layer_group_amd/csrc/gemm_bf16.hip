@@ -1,9 +1,9 @@
-// Grouped expert GEMMs on CDNA4 bf16 matrix cores (fp32 accumulation), over
-// the ragged per-expert row groups that the dispatch produced: the "one
-// grouped matmul over the ragged per-expert token groups" of the dockyard_rl
-// "Mixture-of-Experts" page ("The pipeline", grouped GEMM), with the
-// two-products-per-expert structure of the "Mixture of Experts" blog page's
-// third program (moe_forward).
+// Grouped expert GEMMs on CDNA4 matrix cores (fp32 accumulation) over the
+// ragged per-expert row groups that the dispatch produced: all routed
+// experts are evaluated by one launch per projection instead of a loop over
+// experts (dockyard_rl "Mixture-of-Experts" page, "The pipeline", grouped
+// GEMM), with the two products per expert of the "Mixture of Experts" blog
+// page's third program (moe_forward).
 //
 //   up   (GEMM1): H[r, f] = act(x[tok(r)] . W_gate[e][f] (, x . W_up[e][f]))
 //                 SwiGLU = silu(gate) * up (Edge0 "MoE Spec and Routing",
@@ -19,9 +19,9 @@
 // (the conversion saturates at +-65504).
 //
 // Kernel shape (gfx950):
-//   * a 256 x 256 output tile per 256-thread workgroup, K steps of 64;
-//     each of the 4 waves owns a 128 x 128 sub-tile = 4 x 4 blocks of
-//     v_mfma_f32_32x32x16_bf16.  The weight tile is the MFMA A operand
+//   * a 256 x 256 output tile per 512-thread workgroup, K steps of 64;
+//     each of the 8 waves (2 per SIMD, so one fills the other's issue gaps)
+//     owns a 128 x 64 sub-tile = 4 x 2 blocks of v_mfma_f32_32x32x16;  The weight tile is the MFMA A operand
 //     (rows = output columns) and the activation tile the B operand, so a
 //     lane's accumulators hold 4 consecutive output columns of one row;
 //   * both operands are K-contiguous in HBM (weights are [out, in]) and go
@@ -44,6 +44,7 @@
 //     expert's M-tiles, so concurrently running tiles on one XCD share
 //     weight and activation tiles in its L2.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_internal.hpp"
 
@@ -58,6 +59,11 @@ constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kRowBytes = BK * 2;           // 128
 constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand per stage
 constexpr int kNG = 8;                      // N-tiles per scheduling column group
+constexpr int kWaves = 8;                   // 2 waves per SIMD
+constexpr int kThreads = kWaves * 64;
+constexpr int kWavesN = 4;                  // waves along N (2 along M)
+constexpr int MB = 4, NB = 2;               // 32x32 blocks per wave: 128 x 64
+constexpr int kLoads = 32 / kWaves;         // 1 KiB direct loads per operand per wave
 static_assert(BM == kGemm1BM && BM == kGemm2BM, "tile prefix BM mismatch");
 
 enum Mode { kSwiGLU = 0, kReLU = 1, kDown = 2 };
@@ -78,7 +84,10 @@ struct GemmArgs {
   int NT;                       // N tiles
 };
 
-// byte offset of 16-byte chunk c of row r inside a swizzled tile
+// byte offset of 16-byte chunk c (0..7) of row r inside a swizzled tile.
+// The XOR pattern keeps the 32 rows read by one MFMA fragment load on
+// distinct banks whether the LDS serves 8 lanes (32 banks) or 16 lanes (64
+// banks) of a 16-byte read per cycle.
 __device__ __forceinline__ int swz(int r, int c) {
   return r * kRowBytes + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
 }
@@ -119,7 +128,7 @@ __device__ __forceinline__ half8 bf16x8_to_f16x8(bf16x8 v) {
 }
 
 template <int MODE, bool GATHER>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(kThreads, 1)
 grouped_gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileBytes];
   uint8_t* sA = smem;                   // [2][BM rows][128 B]
@@ -165,13 +174,13 @@ grouped_gemm_kernel(GemmArgs g) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
 
   // ---------------- direct-to-LDS load descriptors
   // Each wave-wide buffer_load_dwordx4 ... lds fills 1 KiB of LDS (8 rows of
   // 128 B) at lane*16; lane l therefore fetches the global chunk that the
   // swizzle places at position l%8 of row l/8.  Wave w issues blocks
-  // j*4 + w (j = 0..7) of each 32 KiB operand tile.
+  // j*kWaves + w of each 32 KiB operand tile.
   const int64_t K = g.K;
   const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(g.a), (short)0, -1, 0x00020000);
@@ -181,11 +190,11 @@ grouped_gemm_kernel(GemmArgs g) {
       const_cast<uint16_t*>(wbase0), (short)0, -1, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsW1 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(wbase1), (short)0, -1, 0x00020000);
-  uint32_t voffA[8], voffW[8];
+  uint32_t voffA[kLoads], voffW[kLoads];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = (j * 4 + wave) * 8 + (lane >> 3);  // tile row
-    const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);  // chunk at position lane%8
+  for (int j = 0; j < kLoads; ++j) {
+    const int r = (j * kWaves + wave) * 8 + (lane >> 3);  // tile row
+    const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);     // chunk at position lane%8
     int m = m0 + r;
     if (m > cnt - 1) m = cnt - 1;  // clamp ragged tail to a valid row
     const int64_t arow = GATHER ? static_cast<int64_t>(g.sorted_token[row0 + m])
@@ -197,25 +206,27 @@ grouped_gemm_kernel(GemmArgs g) {
   }
 
   // ---------------- per-lane fragment offsets
-  // MFMA 32x32x16: lane l supplies row (l % 32), K elements 8*(l/32)..+8
+  // MFMA 32x32x16: lane l supplies row (l % 32), K elements 8*(l/32)..+8.
+  // A wave owns 128 activation rows (4 blocks) and 64 weight rows (2
+  // blocks); for SwiGLU those are 32 gate rows and the matching 32 up rows.
   const int fr = lane & 31;
   const int fh = lane >> 5;
-  int wrow[4], arow_l[4];
+  int wrow[NB], arow_l[MB];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     if (MODE == kSwiGLU)
-      wrow[nb] = ((nb & 2) ? 128 : 0) + wn * 64 + (nb & 1) * 32 + fr;
+      wrow[nb] = (nb ? 128 : 0) + wn * 32 + fr;
     else
-      wrow[nb] = wn * 128 + nb * 32 + fr;
+      wrow[nb] = wn * 64 + nb * 32 + fr;
   }
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) arow_l[mb] = wm * 128 + mb * 32 + fr;
+  for (int mb = 0; mb < MB; ++mb) arow_l[mb] = wm * 128 + mb * 32 + fr;
 
-  f32x16 acc[4][4];
+  f32x16 acc[NB][MB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < MB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -225,68 +236,140 @@ grouped_gemm_kernel(GemmArgs g) {
     uint8_t* a = sA + buf * kTileBytes;
     uint8_t* w = sW + buf * kTileBytes;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int blk = (j * 4 + wave) * 1024;
+    for (int j = 0; j < kLoads; ++j) {
+      const int blk = (j * kWaves + wave) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsA, (__attribute__((address_space(3))) void*)(a + blk), 16, voffA[j],
           soff, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          j < 4 ? rsW0 : rsW1, (__attribute__((address_space(3))) void*)(w + blk),
-          16, voffW[j], soff, 0, 0);
+          j < kLoads / 2 ? rsW0 : rsW1,
+          (__attribute__((address_space(3))) void*)(w + blk), 16, voffW[j], soff,
+          0, 0);
+    }
+  };
+
+  // fragments are double-buffered in registers: the LDS reads for K
+  // sub-step s+1 are in flight while the MFMAs of sub-step s run.  The next
+  // K tile's first fragments are read right after the barrier that
+  // publishes it, ahead of the current tile's last MFMAs.  On the fp16 path
+  // the weight fragments are read raw (bf16) and converted later in the
+  // sub-step, so no conversion waits on its LDS read.
+  using frag_t = typename std::conditional<MODE == kDown, half8, bf16x8>::type;
+  frag_t wf[2][NB], af[2][MB];
+  bf16x8 wraw[2][NB];
+  auto read_frags = [&](int buf, int ks, int fb) {
+    const uint8_t* a = sA + buf * kTileBytes;
+    const uint8_t* w = sW + buf * kTileBytes;
+    const int ch = ks * 2 + fh;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if constexpr (MODE == kDown)
+        wraw[fb][nb] = *reinterpret_cast<const bf16x8*>(w + swz(wrow[nb], ch));
+      else
+        wf[fb][nb] = *reinterpret_cast<const bf16x8*>(w + swz(wrow[nb], ch));
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      af[fb][mb] = *reinterpret_cast<const frag_t*>(a + swz(arow_l[mb], ch));
+  };
+  auto convert = [&](int fb) {
+    if constexpr (MODE == kDown) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) wf[fb][nb] = bf16x8_to_f16x8(wraw[fb][nb]);
+    }
+  };
+  auto mfmas = [&](int fb) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if constexpr (MODE == kDown)
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              wf[fb][nb], af[fb][mb], acc[nb][mb], 0, 0, 0);
+        else
+          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              wf[fb][nb], af[fb][mb], acc[nb][mb], 0, 0, 0);
+      }
+  };
+
+  // Instruction pacing (8 MFMAs and 6 fragment reads per sub-step).  Plain
+  // sub-step: each fragment read of the next sub-step sits between MFMAs of
+  // the current one.  Sub-step 0 also issues the next K tile's direct loads;
+  // a direct load writes LDS, so the compiler keeps fragment reads and
+  // direct loads in program order -- there the reads go first and the loads
+  // are paired with the MFMAs.  The fp16 path places the weight
+  // conversions (about 12 VALU ops per fragment) in the second half.
+  auto pace = [&]() {
+#pragma unroll
+    for (int i = 0; i < NB + MB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+#pragma unroll
+    for (int i = NB + MB; i < NB * MB; ++i) {
+      if (MODE == kDown) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+  };
+  auto pace_loads = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, NB + MB, 0);  // DS read
+#pragma unroll
+    for (int i = 0; i < NB * MB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 * kLoads / (NB * MB), 0);  // VMEM
+      if (MODE == kDown) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    }
+  };
+  auto tile = [&](int kt, auto last_tag) {
+    constexpr bool last = decltype(last_tag)::value;
+    const int cur = kt & 1;
+    read_frags(cur, 1, 1);
+    if constexpr (!last) {
+      issue(kt + 1, cur ^ 1);
+      mfmas(0);
+      convert(1);
+      pace_loads();
+    } else {
+      mfmas(0);
+      convert(1);
+      pace();
+    }
+    read_frags(cur, 2, 0);
+    mfmas(1);
+    convert(0);
+    pace();
+    read_frags(cur, 3, 1);
+    mfmas(0);
+    convert(1);
+    pace();
+    if constexpr (!last) {
+      // every read of this tile is issued: wait for them and for the next
+      // tile's loads, publish the next tile, and read its first fragments
+      // ahead of this tile's last MFMAs
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __syncthreads();
+      read_frags(cur ^ 1, 0, 0);
+      mfmas(1);
+      convert(0);
+      pace();
+    } else {
+      mfmas(1);
     }
   };
 
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) issue(kt + 1, cur ^ 1);
-    const uint8_t* a = sA + cur * kTileBytes;
-    const uint8_t* w = sW + cur * kTileBytes;
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = ks * 2 + fh;
-      if constexpr (MODE == kDown) {
-        // fp16 hidden rows x W_down converted to fp16
-        half8 wf[4], af[4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          wf[nb] = bf16x8_to_f16x8(*reinterpret_cast<const bf16x8*>(w + swz(wrow[nb], ch)));
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          af[mb] = *reinterpret_cast<const half8*>(a + swz(arow_l[mb], ch));
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-            acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                wf[nb], af[mb], acc[nb][mb], 0, 0, 0);
-      } else {
-        bf16x8 wf[4], af[4];
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          wf[nb] = *reinterpret_cast<const bf16x8*>(w + swz(wrow[nb], ch));
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          af[mb] = *reinterpret_cast<const bf16x8*>(a + swz(arow_l[mb], ch));
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb)
-            acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                wf[nb], af[mb], acc[nb][mb], 0, 0, 0);
-      }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
+  read_frags(0, 0, 0);
+  convert(0);
+  for (int kt = 0; kt + 1 < KT; ++kt) tile(kt, std::false_type{});
+  tile(KT - 1, std::true_type{});
 
   // ---------------- epilogue
   // lane holds, for block (nb, mb) and item v: output column
   //   colbase(nb) + 8*(v/4) + 4*(lane/32) + v%4, row arow_l[mb].
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     const int m = m0 + arow_l[mb];
     if (m >= cnt) continue;
     const int64_t orow_off = static_cast<int64_t>(row0 + m) * g.ldo;
@@ -294,27 +377,24 @@ grouped_gemm_kernel(GemmArgs g) {
     float* orow_f = static_cast<float*>(g.out) + orow_off;
     if (MODE == kSwiGLU) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int q = 0; q < 4; ++q) {
+        const int col = nt * (BN / 2) + wn * 32 + 8 * q + 4 * fh;
+        if (col >= g.N) continue;
+        float h[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = nt * (BN / 2) + wn * 64 + nb * 32 + 8 * q + 4 * fh;
-          if (col >= g.N) continue;
-          float h[4];
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            h[v] = silu(acc[nb][mb][4 * q + v]) * acc[nb + 2][mb][4 * q + v];
-          uint2 pk;
-          pk.x = pack_h2(h[0], h[1]);
-          pk.y = pack_h2(h[2], h[3]);
-          *reinterpret_cast<uint2*>(orow + col) = pk;
-        }
+        for (int v = 0; v < 4; ++v)
+          h[v] = silu(acc[0][mb][4 * q + v]) * acc[1][mb][4 * q + v];
+        uint2 pk;
+        pk.x = pack_h2(h[0], h[1]);
+        pk.y = pack_h2(h[2], h[3]);
+        *reinterpret_cast<uint2*>(orow + col) = pk;
       }
     } else {
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = nt * BN + wn * 128 + nb * 32 + 8 * q + 4 * fh;
+          const int col = nt * BN + wn * 64 + nb * 32 + 8 * q + 4 * fh;
           if (col >= g.N) continue;
           if (MODE == kDown) {
             *reinterpret_cast<float4*>(orow_f + col) =
@@ -348,7 +428,7 @@ hipError_t launch_one(int mode, bool gather, const GemmArgs& g, int64_t mt_upper
   int64_t n = mt_upper * g.NT;
   n = (n + 7) / 8 * 8;
   if (n <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(n)), block(256);
+  const dim3 grid(static_cast<unsigned>(n)), block(kThreads);
   if (mode == kSwiGLU && gather)
     hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, true>), grid, block, 0, s, g);
   else if (mode == kSwiGLU)

@@ -122,6 +122,67 @@ logits_tiled_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
   }
 }
 
+// Few experts (E <= 16): each wave owns 4 tokens; lanes split K 8 elements
+// at a time (16-byte loads of x), the router rows are staged through LDS in
+// K chunks of 32 KiB, and each lane keeps 4 x EB partial dot products that
+// are reduced across the wave at the end.  16 tokens per block gives
+// T/16 blocks (256 for 4096 tokens) instead of T/64 tiles that would each
+// waste most of their 64 expert columns.
+template <typename XT, typename WT, int EB>
+__global__ void __launch_bounds__(256)
+logits_small_e_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
+                      float* __restrict__ L, int64_t T, int E, int d) {
+  constexpr int TPW = 4;                // tokens per wave
+  constexpr int KC = 8192 / EB;         // K chunk: EB * KC floats = 32 KiB
+  __shared__ __attribute__((aligned(16))) float ws[EB * KC];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int64_t t0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * TPW;
+  float acc[TPW][EB];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int e = 0; e < EB; ++e) acc[i][e] = 0.f;
+  for (int k0 = 0; k0 < d; k0 += KC) {
+    const int kc = min(KC, d - k0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < EB * kc; i += blockDim.x) {
+      const int e = i / kc, k = i % kc;
+      ws[e * KC + k] = e < E ? ld1(wr, static_cast<int64_t>(e) * d + k0 + k) : 0.f;
+    }
+    __syncthreads();
+    for (int k = lane * 8; k < kc; k += kWave * 8) {
+      float xv[TPW][8];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        if (t0 + i < T) {
+          ld8(x, (t0 + i) * d + k0 + k, xv[i]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xv[i][j] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        const float4 w0 = *reinterpret_cast<const float4*>(&ws[e * KC + k]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&ws[e * KC + k + 4]);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][e] = fmaf(xv[i][j], wv[j], acc[i][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int e = 0; e < EB; ++e) {
+      const float v = wave_sum(acc[i][e]);
+      if (lane == e && e < E && t0 + i < T) L[(t0 + i) * E + e] = v;
+    }
+}
+
 // Few tokens (decode): one wave per expert row, lanes split K, 4 tokens at
 // a time; the expert's router row is read once per 4 tokens (then cached).
 template <typename XT, typename WT>
@@ -342,6 +403,14 @@ hipError_t logits_dispatch(const Dims& D, const void* x, const void* wr,
     dim3 grid((D.E + 3) / 4);
     hipLaunchKernelGGL((logits_rowdot_kernel<XT, WT>), grid, dim3(256), 0, s,
                        xp, wp, L, D.T, D.E, D.d);
+  } else if (D.E <= 16 && (D.d % 8) == 0) {
+    dim3 grid(static_cast<unsigned>((D.T + 15) / 16));
+    if (D.E <= 8)
+      hipLaunchKernelGGL((logits_small_e_kernel<XT, WT, 8>), grid, dim3(256), 0,
+                         s, xp, wp, L, D.T, D.E, D.d);
+    else
+      hipLaunchKernelGGL((logits_small_e_kernel<XT, WT, 16>), grid, dim3(256), 0,
+                         s, xp, wp, L, D.T, D.E, D.d);
   } else {
     dim3 grid(static_cast<unsigned>((D.T + LT - 1) / LT), (D.E + LE - 1) / LE);
     hipLaunchKernelGGL((logits_tiled_kernel<XT, WT>), grid, dim3(256), 0, s,

@@ -28,7 +28,7 @@ def test_full_size_config(cfg_id):
         rs = np.random.default_rng(cfg_id)
         toks = sorted(rs.choice(cfg.T, size=n, replace=False).tolist())
     ids_g, disp = gu.full_check(cfg, inp, r, tokens=toks)
-    gu.check_end_to_end_routing(cfg, inp, ids_g)
+    gu.check_end_to_end_routing(cfg, inp, ids_g, r["logits"].cpu().numpy())
     if cfg.capacity_factor:
         kept = disp["kept"]
         gu.log(f"  load: max count_pre {int(disp['count_pre'].max())}, capacity "

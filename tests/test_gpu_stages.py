@@ -61,7 +61,7 @@ def test_layer_parity_medium(name):
     inp = gu.make_inputs(cfg)
     r = gu.run_layer(cfg, inp)
     ids_g, disp = gu.full_check(cfg, inp, r)
-    gu.check_end_to_end_routing(cfg, inp, ids_g)
+    gu.check_end_to_end_routing(cfg, inp, ids_g, r["logits"].cpu().numpy())
 
 
 @pytest.mark.parametrize("base", range(1234, 1242))
