@@ -140,8 +140,8 @@ typedef void* moe_stream_t;
  *   MOE_ERR_UNSUPPORTED         F32 activations with non-F32 weights;
  *     d not a multiple of 8; BF16 activations whose d, F or shared_ffn is
  *     not a multiple of 64; E > 1024; k > 64; n_group > 64; U4_AFFINE with
- *     ReLU or with d or F above 4096; bf16 tensors (x, the hidden rows, one
- *     expert matrix) of 4 GiB or more */
+ *     ReLU, or with d or F not a power of two in [64, 2048]; bf16 tensors
+ *     (x, the hidden rows, one expert matrix) of 4 GiB or more */
 moe_status moe_spec_validate(const moe_spec* spec, int64_t T);
 
 /* Per-expert capacity, "Mixture of Experts" blog page, first program's

@@ -7,11 +7,14 @@
 //   2. scan    -- one block turns the [blocks x E] histogram into each
 //                 block's per-expert base rank (exclusive over blocks),
 //                 applies the capacity, and writes counts, offsets, the
-//                 drop count and the per-expert M-tile prefix of the GEMMs;
+//                 drop count and the per-expert M-tile prefix of the GEMMs
+//                 (block-wide prefix sums over experts);
 //   3. scatter -- each block walks its chunk in slot order, 256 slots per
 //                 round; inside a wave, lanes holding the same expert are
 //                 found by matching expert-id bits with ballots, so every
 //                 slot gets its exact rank in token order without atomics.
+// When all slots fit one chunk (decode-sized batches) a single block does
+// the three steps in one launch.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -34,49 +37,87 @@ count_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
     hist[static_cast<int64_t>(blockIdx.x) * E + e] = h[e];
 }
 
-// One block of 1024 threads.  hist[b][e] becomes the exclusive base of
-// expert e at block b.
+// Exclusive prefix sum of one int per thread over the block (blockDim a
+// multiple of 64, at most 1024).  `wsum` is LDS scratch of 16 ints.
+// Returns the exclusive prefix; *total receives the block sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int s = wsum[w];
+    if (w < wv) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x - v;
+}
+
+// Kept count, per-expert capacity and M-tile counts of one expert, written
+// as exclusive prefixes over experts (thread e handles expert e; E <= 1024).
+__device__ __forceinline__ int expert_prefixes(int e, int E, int32_t cnt, int64_t S,
+                                                int64_t cap, int32_t* __restrict__ counts,
+                                                int32_t* __restrict__ offsets,
+                                                int32_t* __restrict__ dropped,
+                                                int32_t* __restrict__ tiles1, int bm1,
+                                                int32_t* __restrict__ tiles2, int bm2,
+                                                int* wsum) {
+  const bool on = e < E;
+  const int32_t kp = on ? (static_cast<int64_t>(cnt) < cap ? cnt : static_cast<int32_t>(cap)) : 0;
+  int tot;
+  const int off = block_exclusive_scan(kp, wsum, &tot);
+  if (on) {
+    counts[e] = cnt;
+    offsets[e] = off;
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = tot;
+    dropped[0] = static_cast<int32_t>(S - tot);
+  }
+  if (tiles1) {
+    int t;
+    const int o1 = block_exclusive_scan(on ? (kp + bm1 - 1) / bm1 : 0, wsum, &t);
+    if (on) tiles1[e] = o1;
+    if (threadIdx.x == 0) tiles1[E] = t;
+  }
+  if (tiles2) {
+    int t;
+    const int o2 = block_exclusive_scan(on ? (kp + bm2 - 1) / bm2 : 0, wsum, &t);
+    if (on) tiles2[e] = o2;
+    if (threadIdx.x == 0) tiles2[E] = t;
+  }
+  return off;
+}
+
+// One block of 1024 threads (thread e = expert e).  hist[b][e] becomes the
+// exclusive base of expert e at block b.
 __global__ void __launch_bounds__(1024)
 scan_kernel(int32_t* __restrict__ hist, int nb, int E, int64_t S, int64_t cap,
             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
             int32_t* __restrict__ dropped, int32_t* __restrict__ tiles1,
             int bm1, int32_t* __restrict__ tiles2, int bm2) {
-  extern __shared__ int32_t sm[];
-  int32_t* kept = sm;           // [E]
-  int32_t* t1 = sm + E;         // [E]
-  int32_t* t2 = sm + 2 * E;     // [E]
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int32_t run = 0;
+  __shared__ int wsum[16];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
     for (int b = 0; b < nb; ++b) {
       const int64_t i = static_cast<int64_t>(b) * E + e;
       const int32_t c = hist[i];
       hist[i] = run;
       run += c;
     }
-    counts[e] = run;
-    const int32_t kp = static_cast<int64_t>(run) < cap ? run : static_cast<int32_t>(cap);
-    kept[e] = kp;
-    t1[e] = (kp + bm1 - 1) / bm1;
-    t2[e] = (kp + bm2 - 1) / bm2;
   }
-  __syncthreads();
-  // exclusive prefix over experts (E is at most a few thousand: thread 0
-  // walks it; this kernel is launch-bound anyway)
-  if (threadIdx.x == 0) {
-    int32_t a = 0, b1 = 0, b2 = 0;
-    for (int e = 0; e < E; ++e) {
-      offsets[e] = a;
-      if (tiles1) tiles1[e] = b1;
-      if (tiles2) tiles2[e] = b2;
-      a += kept[e];
-      b1 += t1[e];
-      b2 += t2[e];
-    }
-    offsets[E] = a;
-    if (tiles1) tiles1[E] = b1;
-    if (tiles2) tiles2[E] = b2;
-    dropped[0] = static_cast<int32_t>(S - a);
-  }
+  expert_prefixes(e, E, run, S, cap, counts, offsets, dropped, tiles1, bm1,
+                  tiles2, bm2, wsum);
 }
 
 __global__ void __launch_bounds__(256)
@@ -145,20 +186,106 @@ scatter_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
   }
 }
 
-__global__ void tile_prefix_kernel(const int32_t* __restrict__ offsets, int E,
-                                   int32_t* __restrict__ tiles1, int bm1,
-                                   int32_t* __restrict__ tiles2, int bm2) {
-  if (threadIdx.x != 0) return;
-  int32_t b1 = 0, b2 = 0;
-  for (int e = 0; e < E; ++e) {
-    const int32_t n = offsets[e + 1] - offsets[e];
-    tiles1[e] = b1;
-    tiles2[e] = b2;
-    b1 += (n + bm1 - 1) / bm1;
-    b2 += (n + bm2 - 1) / bm2;
+__global__ void __launch_bounds__(1024)
+tile_prefix_kernel(const int32_t* __restrict__ offsets, int E,
+                   int32_t* __restrict__ tiles1, int bm1,
+                   int32_t* __restrict__ tiles2, int bm2) {
+  __shared__ int wsum[16];
+  const int e = threadIdx.x;
+  const int32_t n = e < E ? offsets[e + 1] - offsets[e] : 0;
+  int t;
+  const int o1 = block_exclusive_scan(e < E ? (n + bm1 - 1) / bm1 : 0, wsum, &t);
+  if (e < E) tiles1[e] = o1;
+  if (e == 0) tiles1[E] = t;
+  const int o2 = block_exclusive_scan(e < E ? (n + bm2 - 1) / bm2 : 0, wsum, &t);
+  if (e < E) tiles2[e] = o2;
+  if (e == 0) tiles2[E] = t;
+}
+
+// All of the dispatch in one block when the slots fit one chunk (decode-
+// sized batches): LDS histogram, prefixes, then the stable rank/scatter of
+// scatter_kernel with block base 0.
+__global__ void __launch_bounds__(1024)
+dispatch_small_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
+                      int64_t S, int k, int E, int64_t cap, int nbits,
+                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                      int32_t* __restrict__ dropped, int32_t* __restrict__ tiles1,
+                      int bm1, int32_t* __restrict__ tiles2, int bm2,
+                      int32_t* __restrict__ sorted_token, float* __restrict__ sorted_w,
+                      int32_t* __restrict__ slot_row) {
+  __shared__ int wsum[16];
+  __shared__ int32_t h[1024];
+  __shared__ int32_t run[1024];
+  __shared__ int32_t offs[1024];
+  __shared__ int32_t wcnt[16][64];  // per-wave counts of a 64-expert window
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += blockDim.x) h[e] = 0;
+  __syncthreads();
+  for (int64_t s = tid; s < S; s += blockDim.x) {
+    const int e = ids[s];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
   }
-  tiles1[E] = b1;
-  tiles2[E] = b2;
+  __syncthreads();
+  const int32_t cnt = tid < E ? h[tid] : 0;
+  const int off = expert_prefixes(tid, E, cnt, S, cap, counts, offsets, dropped,
+                                  tiles1, bm1, tiles2, bm2, wsum);
+  if (tid < E) offs[tid] = off;
+  __syncthreads();
+  // ranks: slots in flat order; inside a wave, lanes with the same expert
+  // are matched on the expert-id bits; across waves, earlier waves' counts
+  // are added through LDS (experts are visited in windows of 64)
+  const int lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  for (int e = tid; e < E; e += blockDim.x) run[e] = 0;
+  __syncthreads();
+  for (int64_t r0 = 0; r0 < S; r0 += blockDim.x) {
+    const int64_t s = r0 + tid;
+    int e = -1;
+    if (s < S) {
+      const int v = ids[s];
+      if (v >= 0 && v < E) e = v;
+    }
+    const bool valid = e >= 0;
+    uint64_t mask = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t bal = __ballot(bit);
+      mask &= bit ? bal : ~bal;
+    }
+    const int within = __popcll(mask & lt_mask);
+    const int mine = __popcll(mask);
+    int32_t rank = 0;
+    // process experts in windows of 64 so the per-wave table stays small
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      for (int i = tid; i < nw * 64; i += blockDim.x) wcnt[i / 64][i % 64] = 0;
+      __syncthreads();
+      const bool here = valid && e >= e0 && e < e0 + 64;
+      if (here && within == 0) wcnt[wv][e - e0] = mine;
+      __syncthreads();
+      if (here) {
+        rank = run[e] + within;
+        for (int q = 0; q < wv; ++q) rank += wcnt[q][e - e0];
+      }
+      __syncthreads();
+      for (int i = tid; i < 64; i += blockDim.x) {
+        if (e0 + i < E) {
+          int32_t add = 0;
+          for (int q = 0; q < nw; ++q) add += wcnt[q][i];
+          run[e0 + i] += add;
+        }
+      }
+      __syncthreads();
+    }
+    if (s < S) {
+      int32_t row = -1;
+      if (valid && static_cast<int64_t>(rank) < cap) {
+        row = offs[e] + rank;
+        sorted_token[row] = static_cast<int32_t>(s / k);
+        sorted_w[row] = w[s];
+      }
+      slot_row[s] = row;
+    }
+  }
 }
 
 template <typename T>
@@ -184,13 +311,20 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
                            float* sorted_w, int32_t* slot_row, int32_t* dropped,
                            int32_t* tiles1, int32_t* tiles2, hipStream_t s) {
   const size_t hsz = static_cast<size_t>(D.E) * sizeof(int32_t);
-  hipLaunchKernelGGL(count_kernel, dim3(nblocks), dim3(256), hsz, s, ids,
-                     D.slots, D.E, hist);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 3 * hsz, s, hist,
-                     nblocks, D.E, D.slots, D.cap, counts, offsets, dropped,
-                     tiles1, kGemm1BM, tiles2, kGemm2BM);
   int nbits = 0;
   while ((1 << nbits) < D.E) ++nbits;
+  if (D.slots <= kDispatchChunk) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, ids, w,
+                       D.slots, D.k, D.E, D.cap, nbits, counts, offsets, dropped,
+                       tiles1, kGemm1BM, tiles2, kGemm2BM, sorted_token, sorted_w,
+                       slot_row);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(count_kernel, dim3(nblocks), dim3(256), hsz, s, ids,
+                     D.slots, D.E, hist);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, hist,
+                     nblocks, D.E, D.slots, D.cap, counts, offsets, dropped,
+                     tiles1, kGemm1BM, tiles2, kGemm2BM);
   hipLaunchKernelGGL(scatter_kernel, dim3(nblocks), dim3(256), 5 * hsz, s, ids,
                      w, D.slots, D.k, D.E, D.cap, nbits, hist, offsets,
                      sorted_token, sorted_w, slot_row);
@@ -199,7 +333,7 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
 
 hipError_t launch_tile_prefix(const Dims& D, const int32_t* offsets,
                               int32_t* tiles1, int32_t* tiles2, hipStream_t s) {
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, offsets, D.E,
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, D.E,
                      tiles1, kGemm1BM, tiles2, kGemm2BM);
   return hipGetLastError();
 }

@@ -8,14 +8,16 @@
 // registers for all of the expert's rows, which sit in LDS.  The affine
 // dequantisation is factored per group so no dequantised weight is formed:
 //   sum_j x_j (s q_j + b) = s * sum_j x_j q_j + b * sum_j x_j
-// over each 32-element run a lane owns (always inside one group of 64).
+// over the 32-element run a lane owns (always inside one group of 64), and
+// the codes enter v_dot2_f32_f16 as the exact fp16 values 1024 + q, two per
+// instruction, against the lane's activations pre-packed as fp16 pairs.
 //
 // One kernel serves both products:
 //   up   : unit = hidden column f; the lane loads the gate row f and the up
 //          row f, the epilogue writes H = silu(gate) * up (fp16, as on the
 //          matrix-core path)
 //   down : unit = output column n of W_down, writes Y (fp32)
-// LPR lanes share one unit and each lane streams VPL 16-byte vectors of it
+// LPR lanes share one unit and each lane streams one 16-byte vector of it
 // per pass; a wave works on 64/LPR units at once and reduces inside each
 // lane group.
 #include "moe_internal.hpp"
@@ -25,22 +27,70 @@ namespace {
 
 constexpr int kRC = 8;            // expert rows staged in LDS per pass
 constexpr int kUnitsPerBlock = 64;
-constexpr int kMaxK = 4096;  // kRC rows of K bf16 stay within 64 KiB of LDS
+constexpr int kMaxK = 2048;  // one pass of 64 lanes x 32 elements per row
 
-__device__ __forceinline__ void unpack8(uint32_t w, float* q) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;         // nibbles 0,2,4,6
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // nibbles 1,3,5,7
-  q[0] = static_cast<float>(lo & 0xFFu);
-  q[1] = static_cast<float>(hi & 0xFFu);
-  q[2] = static_cast<float>((lo >> 8) & 0xFFu);
-  q[3] = static_cast<float>((hi >> 8) & 0xFFu);
-  q[4] = static_cast<float>((lo >> 16) & 0xFFu);
-  q[5] = static_cast<float>((hi >> 16) & 0xFFu);
-  q[6] = static_cast<float>(lo >> 24);
-  q[7] = static_cast<float>(hi >> 24);
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// Codes as fp16: OR-ing a code q (0..15) into the mantissa of 1024.0
+// (0x6400) gives exactly 1024 + q, two codes per 32-bit word.  Word w holds
+// elements 0..7 in nibbles 0..7, so (w >> 4j) & 0x000F000F carries elements
+// j and j+4 into the two halves.
+__device__ __forceinline__ half2_t code_pair(uint32_t w, int j) {
+  return __builtin_bit_cast(half2_t, ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u);
 }
 
-template <bool PAIR, int LPR, int VPL>
+// sum over one lane's 32 elements of x_i * (1024 + q_i), two products per
+// v_dot2 (fp16 products are exact in fp32); xp[m*4 + j] = (x_{8m+j},
+// x_{8m+j+4})
+__device__ __forceinline__ float dot32(const uint4& w, const half2_t* xp) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_fdot2(code_pair(ws[m], j), xp[m * 4 + j], acc, false);
+  return acc;
+}
+
+// a lane's 32 activation values of one row (bf16 tokens or fp16 hidden
+// rows, from LDS) as fp16 pairs matching code_pair, and their fp32 sum
+template <bool BF16>
+__device__ __forceinline__ float load_pairs(const uint16_t* p, half2_t* xp) {
+  float sum = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint4 t = *reinterpret_cast<const uint4*>(p + 8 * m);
+    const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
+    _Float16 h[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (BF16) {
+        h[2 * i] = static_cast<_Float16>(__uint_as_float(tw[i] << 16));
+        h[2 * i + 1] = static_cast<_Float16>(__uint_as_float(tw[i] & 0xffff0000u));
+      } else {
+        h[2 * i] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(tw[i] & 0xffffu));
+        h[2 * i + 1] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(tw[i] >> 16));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      half2_t v;
+      v[0] = h[j];
+      v[1] = h[j + 4];
+      xp[m * 4 + j] = v;
+      sum += static_cast<float>(h[j]) + static_cast<float>(h[j + 4]);
+    }
+  }
+  return sum;
+}
+
+constexpr int kRowsPerPass = 2;  // expert rows multiplied per weight pass
+
+// One lane owns 32 consecutive K elements (inside one quantisation group);
+// LPR = lanes per unit.  sum_i x_i (s q_i + b) = s (sum x_i (1024 + q_i)
+// - 1024 sum x_i) + b sum x_i.
+template <bool PAIR, int LPR>
 __global__ void __launch_bounds__(256)
 u4_kernel(const int32_t* __restrict__ offsets,
           const int32_t* __restrict__ sorted_token,  // nullptr: a rows direct
@@ -60,8 +110,7 @@ u4_kernel(const int32_t* __restrict__ offsets,
   const int u_base = blockIdx.y * kUnitsPerBlock;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  constexpr int UPW = 64 / LPR;   // units per wave pass
-  constexpr int SPAN = 32 * VPL;  // elements per lane per K pass
+  constexpr int UPW = 64 / LPR;  // units per wave pass
   const int sg = lane / LPR, kl = lane % LPR;
   const int words = K / 8, groups = K / G;
 
@@ -78,110 +127,77 @@ u4_kernel(const int32_t* __restrict__ offsets,
           reinterpret_cast<const uint4*>(a + src * K)[c];
     }
     __syncthreads();
-    for (int ub = wave * UPW; ub < kUnitsPerBlock; ub += 4 * UPW) {
-      const int u = u_base + ub + sg;
-      const bool live = u < N;
-      const int uu = live ? u : N - 1;
-      const int64_t wrow = static_cast<int64_t>(e) * N + uu;
-      float acc0[kRC], acc1[kRC];
+    // K <= 32 * LPR (the launcher checks), so this runs once
+#pragma unroll 1
+    for (int kc = 0; kc < K; kc += 32 * LPR) {
+      const int kb = kc + 32 * kl;  // first element owned by this lane
+      const int gi = kb / G;
+#pragma unroll 1
+      for (int rp = 0; rp < nr; rp += kRowsPerPass) {
+        half2_t xp[kRowsPerPass][16];
+        float xsum[kRowsPerPass];
 #pragma unroll
-      for (int r = 0; r < kRC; ++r) acc0[r] = acc1[r] = 0.f;
-      for (int kc = 0; kc < K; kc += SPAN * LPR) {
-        const int kb = kc + SPAN * kl;  // first element owned by this lane
-        uint4 w0[VPL], w1[VPL];
-        float sc0[VPL], bi0[VPL], sc1[VPL], bi1[VPL];
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          w0[v] = *reinterpret_cast<const uint4*>(q0 + wrow * words + kb / 8 + 4 * v);
-          if (PAIR) w1[v] = *reinterpret_cast<const uint4*>(q1 + wrow * words + kb / 8 + 4 * v);
-        }
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) {
-          const int gi = (kb + 32 * v) / G;
-          sc0[v] = bf16_to_f32(s0[wrow * groups + gi]);
-          bi0[v] = bf16_to_f32(b0[wrow * groups + gi]);
+        for (int r = 0; r < kRowsPerPass; ++r)
+          xsum[r] = (rp + r < nr)
+                        ? load_pairs<PAIR>(xs + static_cast<int64_t>(rp + r) * K + kb, xp[r])
+                        : 0.f;
+#pragma unroll 4
+        for (int ub = wave * UPW; ub < kUnitsPerBlock; ub += 4 * UPW) {
+          const int u = u_base + ub + sg;
+          const bool live = u < N;
+          const int uu = live ? u : N - 1;
+          const int64_t wrow = static_cast<int64_t>(e) * N + uu;
+          const uint4 w0 = *reinterpret_cast<const uint4*>(q0 + wrow * words + kb / 8);
+          uint4 w1 = make_uint4(0, 0, 0, 0);
+          if (PAIR) w1 = *reinterpret_cast<const uint4*>(q1 + wrow * words + kb / 8);
+          const float sc0 = bf16_to_f32(s0[wrow * groups + gi]);
+          const float bi0 = bf16_to_f32(b0[wrow * groups + gi]);
+          float sc1 = 0.f, bi1 = 0.f;
           if (PAIR) {
-            sc1[v] = bf16_to_f32(s1[wrow * groups + gi]);
-            bi1[v] = bf16_to_f32(b1[wrow * groups + gi]);
+            sc1 = bf16_to_f32(s1[wrow * groups + gi]);
+            bi1 = bf16_to_f32(b1[wrow * groups + gi]);
           }
-        }
+          float acc0[kRowsPerPass], acc1[kRowsPerPass];
 #pragma unroll
-        for (int r = 0; r < kRC; ++r) {
-          if (r >= nr) break;
-          const uint4* xv = reinterpret_cast<const uint4*>(xs + static_cast<int64_t>(r) * K + kb);
-#pragma unroll
-          for (int v = 0; v < VPL; ++v) {
-            float qa[32], qb[32], xf[32];
-            unpack8(w0[v].x, qa); unpack8(w0[v].y, qa + 8);
-            unpack8(w0[v].z, qa + 16); unpack8(w0[v].w, qa + 24);
+          for (int r = 0; r < kRowsPerPass; ++r) {
+            const float d0 = dot32(w0, xp[r]) - 1024.f * xsum[r];
+            acc0[r] = sc0 * d0 + bi0 * xsum[r];
             if (PAIR) {
-              unpack8(w1[v].x, qb); unpack8(w1[v].y, qb + 8);
-              unpack8(w1[v].z, qb + 16); unpack8(w1[v].w, qb + 24);
+              const float d1 = dot32(w1, xp[r]) - 1024.f * xsum[r];
+              acc1[r] = sc1 * d1 + bi1 * xsum[r];
             }
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-              const uint4 t = xv[4 * v + h];
-              const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
+            for (int o = LPR / 2; o > 0; o >>= 1) {
+              acc0[r] += __shfl_xor(acc0[r], o, 64);
+              if (PAIR) acc1[r] += __shfl_xor(acc1[r], o, 64);
+            }
+          }
+          if (kl == 0 && live) {
 #pragma unroll
-              for (int m = 0; m < 4; ++m) {
-                if (PAIR) {  // bf16 tokens
-                  xf[8 * h + 2 * m] = __uint_as_float(tw[m] << 16);
-                  xf[8 * h + 2 * m + 1] = __uint_as_float(tw[m] & 0xffff0000u);
-                } else {     // fp16 hidden rows
-                  xf[8 * h + 2 * m] = static_cast<float>(
-                      __builtin_bit_cast(_Float16, static_cast<uint16_t>(tw[m] & 0xffffu)));
-                  xf[8 * h + 2 * m + 1] = static_cast<float>(
-                      __builtin_bit_cast(_Float16, static_cast<uint16_t>(tw[m] >> 16)));
-                }
+            for (int r = 0; r < kRowsPerPass; ++r) {
+              if (rp + r >= nr) break;
+              const int64_t o = static_cast<int64_t>(row0 + rc0 + rp + r) * N + u;
+              if (PAIR) {  // hidden activation, fp16 (saturating)
+                float h = acc0[r] / (1.f + __expf(-acc0[r])) * acc1[r];
+                h = fminf(fmaxf(h, -65504.f), 65504.f);
+                static_cast<_Float16*>(out)[o] = static_cast<_Float16>(h);
+              } else {  // expert output, fp32
+                static_cast<float*>(out)[o] = acc0[r];
               }
             }
-            float xsum = 0.f, pa = 0.f, pb = 0.f;
-#pragma unroll
-            for (int j = 0; j < 32; ++j) {
-              xsum += xf[j];
-              pa = fmaf(xf[j], qa[j], pa);
-              if (PAIR) pb = fmaf(xf[j], qb[j], pb);
-            }
-            acc0[r] += sc0[v] * pa + bi0[v] * xsum;
-            if (PAIR) acc1[r] += sc1[v] * pb + bi1[v] * xsum;
           }
-        }
-      }
-      // reduce inside the LPR-lane group
-#pragma unroll
-      for (int r = 0; r < kRC; ++r) {
-#pragma unroll
-        for (int o = LPR / 2; o > 0; o >>= 1) {
-          acc0[r] += __shfl_xor(acc0[r], o, 64);
-          if (PAIR) acc1[r] += __shfl_xor(acc1[r], o, 64);
-        }
-      }
-      if (kl == 0 && live) {
-#pragma unroll
-        for (int r = 0; r < kRC; ++r) {
-          if (r >= nr) break;
-          const int64_t o = static_cast<int64_t>(row0 + rc0 + r) * N + u;
-          if (PAIR) {  // hidden activation, fp16 (saturating)
-            float h = acc0[r] / (1.f + __expf(-acc0[r])) * acc1[r];
-            h = fminf(fmaxf(h, -65504.f), 65504.f);
-            static_cast<_Float16*>(out)[o] = static_cast<_Float16>(h);
-          }
-          else  // expert output, fp32
-            static_cast<float*>(out)[o] = acc0[r];
         }
       }
     }
   }
 }
 
-// lanes per unit and 16-byte vectors per lane for reduction length K
-// (K is a multiple of 64): VPL = 4 when K % 128 == 0, else 2; LPR the largest
-// power of two <= 64 with 32*VPL*LPR dividing K.
-void pick_shape(int K, int* lpr, int* vpl) {
-  *vpl = (K % 128 == 0) ? 4 : 2;
+// lanes per unit: each lane owns 32 elements of K, so LPR = K/32 (K is a
+// multiple of 64 and at most 2048)
+int pick_lpr(int K) {
   int l = 64;
-  while (l > 1 && K % (32 * *vpl * l) != 0) l >>= 1;
-  *lpr = l;
+  while (l > 1 && K % (32 * l) != 0) l >>= 1;
+  return l;
 }
 
 template <bool PAIR>
@@ -190,22 +206,17 @@ hipError_t launch_u4(int K, dim3 grid, size_t lds, hipStream_t s,
                      const uint16_t* a, const uint32_t* q0, const uint16_t* s0,
                      const uint16_t* b0, const uint32_t* q1, const uint16_t* s1,
                      const uint16_t* b1, void* out, int N, int G) {
-  int lpr, vpl;
-  pick_shape(K, &lpr, &vpl);
-#define MOE_U4(L, V)                                                          \
-  hipLaunchKernelGGL((u4_kernel<PAIR, L, V>), grid, dim3(256), lds, s,        \
-                     offsets, st, a, q0, s0, b0, q1, s1, b1, out, N, K, G)
-#define MOE_U4V(L) if (vpl == 4) MOE_U4(L, 4); else MOE_U4(L, 2)
-  switch (lpr) {
-    case 64: MOE_U4V(64); break;
-    case 32: MOE_U4V(32); break;
-    case 16: MOE_U4V(16); break;
-    case 8: MOE_U4V(8); break;
-    case 4: MOE_U4V(4); break;
-    case 2: MOE_U4V(2); break;
-    default: MOE_U4V(1); break;
+#define MOE_U4(L)                                                              \
+  hipLaunchKernelGGL((u4_kernel<PAIR, L>), grid, dim3(256), lds, s, offsets,   \
+                     st, a, q0, s0, b0, q1, s1, b1, out, N, K, G)
+  switch (pick_lpr(K)) {
+    case 64: MOE_U4(64); break;
+    case 32: MOE_U4(32); break;
+    case 16: MOE_U4(16); break;
+    case 8: MOE_U4(8); break;
+    case 4: MOE_U4(4); break;
+    default: MOE_U4(2); break;
   }
-#undef MOE_U4V
 #undef MOE_U4
   return hipGetLastError();
 }
@@ -216,7 +227,9 @@ hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
                          const int32_t* sorted_token, const void* x,
                          const moe_expert_weights& w, void* H, void* Y,
                          hipStream_t s) {
-  if (D.d > kMaxK || D.F > kMaxK || !D.swiglu) return hipErrorInvalidValue;
+  if (D.d > kMaxK || D.F > kMaxK || !D.swiglu ||
+      D.d != 32 * pick_lpr(D.d) || D.F != 32 * pick_lpr(D.F))
+    return hipErrorInvalidValue;
   {
     const dim3 grid(D.E, (D.F + kUnitsPerBlock - 1) / kUnitsPerBlock);
     const size_t lds = static_cast<size_t>(kRC) * D.d * 2;

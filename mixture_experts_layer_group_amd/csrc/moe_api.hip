@@ -70,7 +70,8 @@ moe_status validate(const moe_spec* sp, int64_t T) {
        (s.shared_experts > 0 && s.shared_ffn % 64 != 0)))
     return MOE_ERR_UNSUPPORTED;
   if (s.weight_dtype == MOE_DTYPE_U4_AFFINE &&
-      (s.act != MOE_ACT_SWIGLU || s.hidden > 4096 || s.ffn > 4096))
+      (s.act != MOE_ACT_SWIGLU || s.hidden > 2048 || s.ffn > 2048 ||
+       (s.hidden & (s.hidden - 1)) != 0 || (s.ffn & (s.ffn - 1)) != 0))
     return MOE_ERR_UNSUPPORTED;
   if (s.num_experts > 1024 || s.top_k > 64) return MOE_ERR_UNSUPPORTED;
   // the bf16 matrix-core kernels address activations, hidden rows and one

@@ -183,8 +183,9 @@ logits_small_e_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
     }
 }
 
-// Few tokens (decode): one wave per expert row, lanes split K, 4 tokens at
-// a time; the expert's router row is read once per 4 tokens (then cached).
+// Few tokens (decode): one wave per (expert row, 8 tokens), lanes split K,
+// 4 tokens at a time; the expert's router row is read once per 4 tokens
+// (then cached).
 template <typename XT, typename WT>
 __global__ void __launch_bounds__(256)
 logits_rowdot_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
@@ -193,7 +194,8 @@ logits_rowdot_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
   const int e = blockIdx.x * 4 + threadIdx.x / kWave;
   if (e >= E) return;
   const WT* wrow = wr + static_cast<int64_t>(e) * d;
-  for (int64_t t0 = 0; t0 < T; t0 += 4) {
+  const int64_t tb = static_cast<int64_t>(blockIdx.y) * 8;
+  for (int64_t t0 = tb; t0 < T && t0 < tb + 8; t0 += 4) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int k = lane * 8; k < d; k += kWave * 8) {
       float wv[8];
@@ -400,7 +402,7 @@ hipError_t logits_dispatch(const Dims& D, const void* x, const void* wr,
   const XT* xp = static_cast<const XT*>(x);
   const WT* wp = static_cast<const WT*>(wr);
   if (D.T <= 64 && (D.d % 8) == 0) {
-    dim3 grid((D.E + 3) / 4);
+    dim3 grid((D.E + 3) / 4, static_cast<unsigned>((D.T + 7) / 8));
     hipLaunchKernelGGL((logits_rowdot_kernel<XT, WT>), grid, dim3(256), 0, s,
                        xp, wp, L, D.T, D.E, D.d);
   } else if (D.E <= 16 && (D.d % 8) == 0) {

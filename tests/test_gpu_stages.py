@@ -40,7 +40,7 @@ MEDIUM = {
                                     norm_topk_prob=False, bias_range=0.05),
     # 4-bit affine weights, decode-shaped; K % 128 == 0 and == 64 variants
     "u4-decode": C("u4-decode", 109, T=20, d=512, E=64, top_k=4, F=256, weight_dtype=synth.U4),
-    "u4-k64": C("u4-k64", 110, T=37, d=576, E=16, top_k=2, F=192, weight_dtype=synth.U4),
+    "u4-small-k": C("u4-small-k", 110, T=37, d=256, E=16, top_k=2, F=64, weight_dtype=synth.U4),
     # fp32 path, SwiGLU and a shared expert
     "f32-swiglu-shared": C("f32-swiglu-shared", 111, T=150, d=48, E=5, top_k=2, F=40,
                            act_dtype=synth.F32, weight_dtype=synth.F32, shared_experts=2,

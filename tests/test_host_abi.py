@@ -53,6 +53,8 @@ def base(**kw):
     ({"shared_experts": 1, "shared_F": 0}, 1),
     ({"weight_dtype": "u4", "quant_group": 32}, 1),
     ({"weight_dtype": "u4", "d": 96}, 1),
+    ({"weight_dtype": "u4", "d": 4096}, 7),      # 4-bit path: d, F <= 2048
+    ({"weight_dtype": "u4", "F": 192}, 7),       # ... powers of two
     ({"weight_dtype": "f32"}, 1),                 # bf16 activations, f32 weights
     ({"act_dtype": "f32", "weight_dtype": "bf16"}, 7),
     ({"d": 100}, 7),
