@@ -6,6 +6,8 @@
 // shared expert).  Written as a gather -- each token reads its own kept rows
 // through slot_row -- so the sum has a fixed order (slot 0..k-1, then the
 // shared experts) and needs no atomics.  Dropped slots (row -1) add nothing.
+#include <algorithm>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -36,7 +38,8 @@ constexpr int kMaxSlots = 64;
 // the output type.
 template <typename OutT>
 __global__ void __launch_bounds__(256)
-combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ slot_row,
+combine_kernel(const float* __restrict__ y, const float* __restrict__ ypart,
+               const int32_t* __restrict__ slot_row,
                const float* __restrict__ topk_w, const float* __restrict__ ysh,
                OutT* __restrict__ out, int64_t Tn, int k, int S, int d) {
   __shared__ int32_t rows[kMaxSlots];
@@ -54,6 +57,12 @@ combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ slot_row
       if (r < 0) continue;
       float v[8];
       load8(y + static_cast<int64_t>(r) * d + c, v);
+      if (ypart) {
+        float u[8];
+        load8(ypart + static_cast<int64_t>(r) * d + c, u);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] += u[j];
+      }
       const float wi = wts[i];
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = fmaf(wi, v[j], acc[j]);
@@ -68,9 +77,34 @@ combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ slot_row
   }
 }
 
+// one block per row band; rows at or past the kept count are skipped
+__global__ void __launch_bounds__(256)
+fold_split_kernel(const int32_t* __restrict__ offsets, int E, float* __restrict__ y,
+                  const float* __restrict__ ypart, int d) {
+  const int64_t r = blockIdx.x;
+  if (r >= offsets[E]) return;
+  for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
+    float v[8], u[8];
+    load8(y + r * d + c, v);
+    load8(ypart + r * d + c, u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] += u[j];
+    store8(y + r * d + c, v);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_combine(const Dims& D, const void* y_rows,
+hipError_t launch_fold_split(const Dims& D, const int32_t* offsets, float* Y,
+                             const float* Ypart, hipStream_t s) {
+  const int64_t rows = std::min<int64_t>(D.slots, D.cap * D.E);
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fold_split_kernel, dim3(static_cast<unsigned>(rows)), dim3(256), 0, s,
+                     offsets, D.E, Y, Ypart, D.d);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const Dims& D, const void* y_rows, const float* y_part,
                           const int32_t* slot_row, const float* topk_w,
                           const void* y_shared, void* out, hipStream_t s) {
   if (D.k > kMaxSlots) return hipErrorInvalidValue;
@@ -79,11 +113,11 @@ hipError_t launch_combine(const Dims& D, const void* y_rows,
   const float* y = static_cast<const float*>(y_rows);
   const float* ys = static_cast<const float*>(y_shared);
   if (D.out_bf16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, y,
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, y, y_part,
                        slot_row, topk_w, ys, static_cast<uint16_t*>(out), D.T,
                        D.k, S, D.d);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, y, slot_row,
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, y, y_part, slot_row,
                        topk_w, ys, static_cast<float*>(out), D.T, D.k, S, D.d);
   return hipGetLastError();
 }

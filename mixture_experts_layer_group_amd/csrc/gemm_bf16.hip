@@ -21,18 +21,22 @@
 // Kernel shape (gfx950):
 //   * a 256 x 256 output tile per 512-thread workgroup, K steps of 64;
 //     each of the 8 waves (2 per SIMD, so one fills the other's issue gaps)
-//     owns a 128 x 64 sub-tile = 4 x 2 blocks of v_mfma_f32_32x32x16;  The weight tile is the MFMA A operand
-//     (rows = output columns) and the activation tile the B operand, so a
-//     lane's accumulators hold 4 consecutive output columns of one row;
+//     owns a 128 x 64 sub-tile = 4 x 2 blocks of v_mfma_f32_32x32x16.  The
+//     weight tile is the MFMA A operand (rows = output columns) and the
+//     activation tile the B operand, so a lane's accumulators hold 4
+//     consecutive output columns of one row;
 //   * both operands are K-contiguous in HBM (weights are [out, in]) and go
 //     straight from HBM to LDS (buffer_load_dwordx4 ... lds, no staging
-//     registers) into double-buffered tiles (2 x 64 KiB); the next K step is
-//     in flight while the current one is multiplied.  The 16-byte chunks of
-//     each 128-byte LDS row are XOR-swizzled (conflict-free for 8- and
-//     16-lane LDS phases); the swizzle is applied on the global side, since
-//     a direct load writes LDS at lane*16;
+//     registers) into double-buffered tiles (2 x 64 KiB).  The loads of K
+//     step t+1 start right after the barrier that ends step t-1 (half
+//     there, half in step t's first sub-step), so the memory pipe is busy
+//     across the barrier.  The 16-byte chunks of each 128-byte LDS row are
+//     XOR-swizzled (conflict-free for 8- and 16-lane LDS phases); the
+//     swizzle is applied on the global side, since a direct load writes LDS
+//     at lane*16;
 //   * activation rows are gathered on load through sorted_token (no
-//     permuted copy of x);
+//     permuted copy of x); rows past the end of a group are given an
+//     out-of-range offset, so a ragged tile fetches only its real rows;
 //   * SwiGLU: a tile's 256 weight rows are 128 gate rows then the same 128
 //     up rows; each wave holds gate and up accumulators of the same
 //     (row, column) in the same lanes, so the epilogue fuses silu(g) * u;
@@ -40,9 +44,12 @@
 //     tile count; each workgroup reads the per-expert M-tile prefix written
 //     by the dispatch and exits if surplus.  Workgroup ids are remapped so
 //     that each of the 8 XCDs (hardware dispatch is round-robin over XCDs)
-//     gets a contiguous range of tiles, ordered 8 N-tiles fastest inside an
-//     expert's M-tiles, so concurrently running tiles on one XCD share
-//     weight and activation tiles in its L2.
+//     gets a contiguous range of tiles, ordered per expert in groups of 8
+//     N-tiles with the expert's M-tiles fastest, so the tiles running
+//     together on one XCD share weight and activation lines in its L2;
+//   * the down projection may split its reduction in two K halves (more,
+//     shorter tiles when the tile count would leave the last round of
+//     workgroups mostly idle); the second half goes to a partial buffer.
 #include <algorithm>
 #include <type_traits>
 
@@ -64,12 +71,14 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kWavesN = 4;                  // waves along N (2 along M)
 constexpr int MB = 4, NB = 2;               // 32x32 blocks per wave: 128 x 64
 constexpr int kLoads = 32 / kWaves;         // 1 KiB direct loads per operand per wave
+constexpr int kTailJ = 4;                   // load pairs issued after the barrier (rest: sub-step 0)
 static_assert(BM == kGemm1BM && BM == kGemm2BM, "tile prefix BM mismatch");
 
 enum Mode { kSwiGLU = 0, kReLU = 1, kDown = 2 };
 
 struct GemmArgs {
   const uint16_t* a;            // activation rows (x or H)
+  uint32_t a_bytes;             // size of the activation buffer in bytes
   const int32_t* sorted_token;  // gather table (nullptr: row = group row)
   const int32_t* offsets;       // [E+1] group row offsets (nullptr: one group)
   const int32_t* tiles;         // [E+1] group M-tile prefix (nullptr: one group)
@@ -80,6 +89,8 @@ struct GemmArgs {
   int N;                        // weight rows per expert
   int K;                        // reduction length (row length of a and w)
   void* out;                    // [rows][ldo]: bf16 H (up), fp32 Y (down)
+  float* part;                  // down, second K split: fp32 partial rows
+  int ksplit;                   // K splits (1 or 2; 2 only for down)
   int ldo;                      // output row length (F or d)
   int NT;                       // N tiles
 };
@@ -137,37 +148,46 @@ grouped_gemm_kernel(GemmArgs g) {
   // ---------------- tile scheduling
   const int total_mt = g.tiles ? g.tiles[g.E] : (g.single_rows + BM - 1) / BM;
   const int real = total_mt * g.NT;
-  const int share = (real + 7) >> 3;
+  const int share = (real * g.ksplit + 7) >> 3;
   const int bid = blockIdx.x;
   const int local = bid >> 3;
   if (local >= share) return;
-  const int L = (bid & 7) * share + local;
-  if (L >= real) return;
-  int gm, nt;
+  int L = (bid & 7) * share + local;
+  if (L >= real * g.ksplit) return;
+  const int split = L / real;  // K split (slowest, so each split's tiles keep their order)
+  L -= split * real;
+  int e = 0, row0, cnt, mt, nt;
   {
-    const int full = g.NT / kNG;
-    const int colgrp = L / (total_mt * kNG);
-    if (colgrp < full) {
-      const int rem = L - colgrp * total_mt * kNG;
-      gm = rem / kNG;
-      nt = colgrp * kNG + rem % kNG;
-    } else {
-      const int ng = g.NT - full * kNG;
-      const int rem = L - full * total_mt * kNG;
-      gm = rem / ng;
-      nt = full * kNG + rem % ng;
+    // expert-major order: per expert, groups of kNG N-tiles; inside a group
+    // the expert's M-tiles run fastest, so the workgroups that run together
+    // on one XCD share each weight tile and the expert's activation rows
+    const int32_t* tp = g.tiles;
+    int t0 = 0, t1 = total_mt;
+    if (tp) {
+      e = largest_le(tp, g.E, L / g.NT);
+      t0 = tp[e];
+      t1 = tp[e + 1];
     }
-  }
-  int e = 0, row0, cnt, mt;
-  if (g.tiles) {
-    e = largest_le(g.tiles, g.E, gm);
-    mt = gm - g.tiles[e];
-    row0 = g.offsets[e];
-    cnt = g.offsets[e + 1] - row0;
-  } else {
-    mt = gm;
-    row0 = 0;
-    cnt = g.single_rows;
+    const int mte = t1 - t0;
+    const int rem = L - t0 * g.NT;
+    const int full = g.NT / kNG;
+    const int grp = rem / (mte * kNG);
+    if (grp < full) {
+      const int r2 = rem - grp * mte * kNG;
+      nt = grp * kNG + r2 / mte;
+      mt = r2 % mte;
+    } else {
+      const int r2 = rem - full * mte * kNG;
+      nt = full * kNG + r2 / mte;
+      mt = r2 % mte;
+    }
+    if (tp) {
+      row0 = g.offsets[e];
+      cnt = g.offsets[e + 1] - row0;
+    } else {
+      row0 = 0;
+      cnt = g.single_rows;
+    }
   }
   const int m0 = mt * BM;  // first row of this tile inside the group
 
@@ -182,8 +202,12 @@ grouped_gemm_kernel(GemmArgs g) {
   // swizzle places at position l%8 of row l/8.  Wave w issues blocks
   // j*kWaves + w of each 32 KiB operand tile.
   const int64_t K = g.K;
+  // The activation descriptor carries the buffer size: rows past the end
+  // of the group get the offset a_bytes, which the buffer range check turns
+  // into loads that fetch nothing (the LDS rows they would fill only feed
+  // output rows that are never stored).
   const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(g.a), (short)0, -1, 0x00020000);
+      const_cast<uint16_t*>(g.a), (short)0, static_cast<int>(g.a_bytes), 0x00020000);
   const uint16_t* wbase0 = g.w0 + static_cast<int64_t>(e) * g.N * K;
   const uint16_t* wbase1 = (MODE == kSwiGLU ? g.w1 : g.w0) + static_cast<int64_t>(e) * g.N * K;
   const __amdgpu_buffer_rsrc_t rsW0 = __builtin_amdgcn_make_buffer_rsrc(
@@ -195,11 +219,14 @@ grouped_gemm_kernel(GemmArgs g) {
   for (int j = 0; j < kLoads; ++j) {
     const int r = (j * kWaves + wave) * 8 + (lane >> 3);  // tile row
     const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);     // chunk at position lane%8
-    int m = m0 + r;
-    if (m > cnt - 1) m = cnt - 1;  // clamp ragged tail to a valid row
-    const int64_t arow = GATHER ? static_cast<int64_t>(g.sorted_token[row0 + m])
-                                : static_cast<int64_t>(row0 + m);
-    voffA[j] = static_cast<uint32_t>(arow * K * 2 + c * 16);
+    const int m = m0 + r;
+    if (m < cnt) {
+      const int64_t arow = GATHER ? static_cast<int64_t>(g.sorted_token[row0 + m])
+                                  : static_cast<int64_t>(row0 + m);
+      voffA[j] = static_cast<uint32_t>(arow * K * 2 + c * 16);
+    } else {
+      voffA[j] = g.a_bytes;  // past the group: out of range, no fetch
+    }
     int n = (MODE == kSwiGLU) ? nt * (BN / 2) + (r & 127) : nt * BN + r;
     if (n > g.N - 1) n = g.N - 1;
     voffW[j] = static_cast<uint32_t>(static_cast<int64_t>(n) * K * 2 + c * 16);
@@ -230,13 +257,14 @@ grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int KT = g.K / BK;
-  auto issue = [&](int kt, int buf) {
-    const int soff = kt * kRowBytes;  // K advance in bytes
+  const int KT = g.K / BK / g.ksplit;  // K steps of this split
+  const int kbase = split * KT;
+  auto issue = [&](int kt, int buf, int j0, int j1) {
+    const int soff = (kbase + kt) * kRowBytes;  // K advance in bytes
     uint8_t* a = sA + buf * kTileBytes;
     uint8_t* w = sW + buf * kTileBytes;
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
+    for (int j = j0; j < j1; ++j) {
       const int blk = (j * kWaves + wave) * 1024;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsA, (__attribute__((address_space(3))) void*)(a + blk), 16, voffA[j],
@@ -311,24 +339,36 @@ grouped_gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
   };
-  auto pace_loads = [&]() {
+  // sub-step with NJ load pairs (2*NJ direct loads) spread over its MFMAs
+  auto pace_loads = [&](auto nj_tag) {
+    constexpr int NJ = decltype(nj_tag)::value;
+    constexpr int kV = 2 * NJ > 0 ? 2 * NJ : 1;  // direct loads in this sub-step
+    static_assert(kV <= NB * MB && (NB * MB) % kV == 0, "load spread");
+    constexpr int kEvery = NB * MB / kV;
     __builtin_amdgcn_sched_group_barrier(0x100, NB + MB, 0);  // DS read
 #pragma unroll
     for (int i = 0; i < NB * MB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 2 * kLoads / (NB * MB), 0);  // VMEM
+      if (i % kEvery == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
       if (MODE == kDown) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
   };
-  auto tile = [&](int kt, auto last_tag) {
-    constexpr bool last = decltype(last_tag)::value;
+  // Load pipeline.  The loads of K tile t+1 go into the buffer that tile
+  // t-1 used: kTailJ load pairs are issued right after the barrier that
+  // ends tile t-1 (that buffer is free from then on), during tile t-1's
+  // last MFMAs, and the remaining pairs during tile t's first sub-step.  So
+  // the memory pipe never idles across the barrier, and tile t+1 has nearly
+  // a whole tile of MFMAs to arrive in.
+  constexpr int kSubJ = kLoads - kTailJ;
+  auto tile = [&](int kt, auto kind_tag) {
+    constexpr int kind = decltype(kind_tag)::value;  // 0 full, 1 no tail loads, 2 last
     const int cur = kt & 1;
     read_frags(cur, 1, 1);
-    if constexpr (!last) {
-      issue(kt + 1, cur ^ 1);
+    if constexpr (kind != 2 && kSubJ > 0) {
+      issue(kt + 1, cur ^ 1, kTailJ, kLoads);
       mfmas(0);
       convert(1);
-      pace_loads();
+      pace_loads(std::integral_constant<int, kSubJ>{});
     } else {
       mfmas(0);
       convert(1);
@@ -342,28 +382,37 @@ grouped_gemm_kernel(GemmArgs g) {
     mfmas(0);
     convert(1);
     pace();
-    if constexpr (!last) {
+    if constexpr (kind != 2) {
       // every read of this tile is issued: wait for them and for the next
-      // tile's loads, publish the next tile, and read its first fragments
-      // ahead of this tile's last MFMAs
+      // tile's loads, publish the next tile, read its first fragments ahead
+      // of this tile's last MFMAs, and start the loads of the tile after it
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __syncthreads();
       read_frags(cur ^ 1, 0, 0);
-      mfmas(1);
-      convert(0);
-      pace();
+      if constexpr (kind == 0 && kTailJ > 0) {
+        issue(kt + 2, cur, 0, kTailJ);
+        mfmas(1);
+        convert(0);
+        pace_loads(std::integral_constant<int, kTailJ>{});
+      } else {
+        mfmas(1);
+        convert(0);
+        pace();
+      }
     } else {
       mfmas(1);
     }
   };
 
-  issue(0, 0);
+  issue(0, 0, 0, kLoads);
+  if (KT > 1) issue(1, 1, 0, kTailJ);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   read_frags(0, 0, 0);
   convert(0);
-  for (int kt = 0; kt + 1 < KT; ++kt) tile(kt, std::false_type{});
-  tile(KT - 1, std::true_type{});
+  for (int kt = 0; kt + 2 < KT; ++kt) tile(kt, std::integral_constant<int, 0>{});
+  if (KT > 1) tile(KT - 2, std::integral_constant<int, 1>{});
+  tile(KT - 1, std::integral_constant<int, 2>{});
 
   // ---------------- epilogue
   // lane holds, for block (nb, mb) and item v: output column
@@ -374,7 +423,7 @@ grouped_gemm_kernel(GemmArgs g) {
     if (m >= cnt) continue;
     const int64_t orow_off = static_cast<int64_t>(row0 + m) * g.ldo;
     uint16_t* orow = static_cast<uint16_t*>(g.out) + orow_off;
-    float* orow_f = static_cast<float*>(g.out) + orow_off;
+    float* orow_f = (split ? g.part : static_cast<float*>(g.out)) + orow_off;
     if (MODE == kSwiGLU) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -425,7 +474,7 @@ int ntiles(int mode, int N) {
 
 hipError_t launch_one(int mode, bool gather, const GemmArgs& g, int64_t mt_upper,
                       hipStream_t s) {
-  int64_t n = mt_upper * g.NT;
+  int64_t n = mt_upper * g.NT * g.ksplit;
   n = (n + 7) / 8 * 8;
   if (n <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(n)), block(kThreads);
@@ -444,6 +493,18 @@ hipError_t launch_one(int mode, bool gather, const GemmArgs& g, int64_t mt_upper
 
 }  // namespace
 
+int down_splits(const Dims& D) {
+  if (!D.bf16 || D.u4) return 1;
+  const int KT = D.F / BK;
+  if (KT % 2 != 0 || KT < 16) return 1;
+  const int64_t nmax = std::min<int64_t>(D.slots, D.cap * D.E);
+  const int64_t t = (nmax / BM + D.E) * ntiles(kDown, D.d);  // tile upper bound
+  constexpr int64_t kCUs = 256;
+  const int64_t half_rounds1 = (t + kCUs - 1) / kCUs * 2;
+  const int64_t half_rounds2 = (2 * t + kCUs - 1) / kCUs;
+  return half_rounds2 * 10 < half_rounds1 * 9 ? 2 : 1;
+}
+
 hipError_t launch_shared_bf16(const Dims& D, const void* x,
                               const moe_expert_weights& w, void* Hs, void* Ys,
                               hipStream_t s) {
@@ -453,6 +514,7 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
     const int64_t wo = static_cast<int64_t>(sh) * D.Fs * D.d;
     GemmArgs g{};
     g.a = static_cast<const uint16_t*>(x);
+    g.a_bytes = static_cast<uint32_t>(D.T * D.d * 2);
     g.E = 1;
     g.single_rows = static_cast<int32_t>(D.T);
     g.w0 = static_cast<const uint16_t*>(w.shared_gate) + wo;
@@ -462,10 +524,12 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
     g.out = Hs;
     g.ldo = D.Fs;
     g.NT = ntiles(up_mode, D.Fs);
+    g.ksplit = 1;
     hipError_t err = launch_one(up_mode, false, g, mt, s);
     if (err != hipSuccess) return err;
     GemmArgs h{};
     h.a = static_cast<const uint16_t*>(Hs);
+    h.a_bytes = static_cast<uint32_t>(D.T * D.Fs * 2);
     h.E = 1;
     h.single_rows = static_cast<int32_t>(D.T);
     h.w0 = static_cast<const uint16_t*>(w.shared_down) + wo;
@@ -474,6 +538,7 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
     h.out = static_cast<float*>(Ys) + static_cast<int64_t>(sh) * D.T * D.d;
     h.ldo = D.d;
     h.NT = ntiles(kDown, D.d);
+    h.ksplit = 1;
     err = launch_one(kDown, false, h, mt, s);
     if (err != hipSuccess) return err;
   }
@@ -484,13 +549,14 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
                            const int32_t* tiles1, const int32_t* tiles2,
                            const int32_t* sorted_token, const void* x,
                            const moe_expert_weights& w, void* H, void* Hs,
-                           void* Y, void* Ys, hipStream_t s) {
+                           void* Y, float* Ypart, void* Ys, hipStream_t s) {
   const int up_mode = D.swiglu ? kSwiGLU : kReLU;
   // kept rows are at most min(T*k, E*capacity); cap is already <= T*k
   const int64_t nmax = std::min<int64_t>(D.slots, D.cap * D.E);
   {
     GemmArgs g{};
     g.a = static_cast<const uint16_t*>(x);
+    g.a_bytes = static_cast<uint32_t>(D.T * D.d * 2);
     g.sorted_token = sorted_token;
     g.offsets = offsets;
     g.tiles = tiles1;
@@ -502,12 +568,14 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
     g.out = H;
     g.ldo = D.F;
     g.NT = ntiles(up_mode, D.F);
+    g.ksplit = 1;
     hipError_t err = launch_one(up_mode, true, g, nmax / BM + D.E, s);
     if (err != hipSuccess) return err;
   }
   {
     GemmArgs g{};
     g.a = static_cast<const uint16_t*>(H);
+    g.a_bytes = static_cast<uint32_t>(D.slots * D.F * 2);
     g.offsets = offsets;
     g.tiles = tiles2;
     g.E = D.E;
@@ -517,6 +585,9 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
     g.out = Y;
     g.ldo = D.d;
     g.NT = ntiles(kDown, D.d);
+    g.ksplit = down_splits(D);
+    g.part = Ypart;
+    if (g.ksplit > 1 && Ypart == nullptr) return hipErrorInvalidValue;
     hipError_t err = launch_one(kDown, false, g, nmax / BM + D.E, s);
     if (err != hipSuccess) return err;
   }

@@ -147,6 +147,7 @@ WsLayout layout_of(const Dims& D) {
   L.H = take(S * D.F * es);
   L.Hs = take(static_cast<size_t>(D.S) * T * D.Fs * es);
   L.Y = take(S * D.d * 4);
+  L.Ypart = take(down_splits(D) > 1 ? S * D.d * 4 : 0);
   L.Ys = take(static_cast<size_t>(D.S) * T * D.d * 4);
   L.total = o;
   return L;
@@ -197,7 +198,7 @@ moe_status do_route(const moe_spec& sp, const Dims& D, const WsLayout& L,
 moe_status do_ffn(const moe_spec& sp, const Dims& D, const WsLayout& L,
                   const int32_t* offsets, const int32_t* sorted_token,
                   const void* x, const moe_expert_weights& w, void* y_rows,
-                  void* y_shared, void* ws, bool tiles_ready, hipStream_t s) {
+                  void* y_shared, void* ws, bool fused, hipStream_t s) {
   void* H = at<void>(ws, L.H);
   void* Hs = at<void>(ws, L.Hs);
   if (!D.bf16) {
@@ -213,12 +214,19 @@ moe_status do_ffn(const moe_spec& sp, const Dims& D, const WsLayout& L,
   }
   int32_t* t1 = at<int32_t>(ws, L.tiles1);
   int32_t* t2 = at<int32_t>(ws, L.tiles2);
-  if (!tiles_ready) {
+  if (!fused) {  // the fused layer's dispatch already wrote the tile prefixes
     hipError_t e = launch_tile_prefix(D, offsets, t1, t2, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  return hip_status(launch_ffn_bf16(D, offsets, t1, t2, sorted_token, x, w, H,
-                                    Hs, y_rows, y_shared, s));
+  float* part = down_splits(D) > 1 ? at<float>(ws, L.Ypart) : nullptr;
+  hipError_t e = launch_ffn_bf16(D, offsets, t1, t2, sorted_token, x, w, H, Hs,
+                                 y_rows, part, y_shared, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  // the stage API returns whole expert rows; the fused layer lets the
+  // combine add the second split instead
+  if (part && !fused)
+    return hip_status(launch_fold_split(D, offsets, static_cast<float*>(y_rows), part, s));
+  return MOE_OK;
 }
 
 }  // namespace
@@ -327,7 +335,7 @@ moe_status moe_combine(const moe_spec* spec, int64_t T, const void* y_rows,
   if (spec->shared_experts > 0 && (!y_shared || !aligned16(y_shared)))
     return MOE_ERR_SHAPE;
   const Dims D = dims_of(*spec, T);
-  return hip_status(launch_combine(D, y_rows, slot_row, topk_w,
+  return hip_status(launch_combine(D, y_rows, nullptr, slot_row, topk_w,
                                    spec->shared_experts > 0 ? y_shared : nullptr,
                                    out, static_cast<hipStream_t>(stream)));
 }
@@ -377,7 +385,8 @@ moe_status moe_layer_forward(const moe_spec* spec, int64_t T, const void* x,
   st = do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, Y, Ys, ws,
               mfma_path, s);
   if (st != MOE_OK) return st;
-  return hip_status(launch_combine(D, Y, slot_row, tw, D.S > 0 ? Ys : nullptr,
+  const float* part = (mfma_path && down_splits(D) > 1) ? at<float>(ws, L.Ypart) : nullptr;
+  return hip_status(launch_combine(D, Y, part, slot_row, tw, D.S > 0 ? Ys : nullptr,
                                    out, s));
 }
 

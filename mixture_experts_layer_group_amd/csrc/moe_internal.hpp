@@ -52,7 +52,7 @@ struct WsLayout {
   size_t logits, probpart, hist, tiles1, tiles2;
   size_t topk_ids, topk_w, counts, offsets, sorted_token, sorted_w, slot_row,
       dropped;
-  size_t H, Hs, Y, Ys;
+  size_t H, Hs, Y, Ypart, Ys;
   size_t total;
   int route_blocks;     // selection kernel grid (prob partial rows)
   int dispatch_blocks;  // count / scatter grid (histogram rows)
@@ -65,6 +65,15 @@ constexpr int kSelectWaves = 4;       // tokens in flight per select block
 // the per-expert M-tile prefix for them.
 constexpr int kGemm1BM = 256;
 constexpr int kGemm2BM = 256;
+
+// K splits of the grouped down projection (1 or 2).  Too few output tiles
+// for the chip leave its last round of workgroups mostly idle; splitting
+// the reduction in two halves the tile length and doubles the tile count.
+// Split 1 writes its fp32 partial to a workspace buffer, which the combine
+// adds to split 0's rows (in that order) before weighting.  The choice
+// depends only on the shapes (sized for a 256-CU part), so the workspace
+// layout does not depend on the device.
+int down_splits(const Dims& D);
 
 // ---------------------------------------------------------------- launchers
 // router.hip
@@ -95,7 +104,11 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
                            const int32_t* tiles1, const int32_t* tiles2,
                            const int32_t* sorted_token, const void* x,
                            const moe_expert_weights& w, void* H, void* Hs,
-                           void* Y, void* Ys, hipStream_t s);
+                           void* Y, float* Ypart, void* Ys, hipStream_t s);
+// Y[r] += Ypart[r] for the kept rows (r < offsets[E]): folds the second K
+// split into the expert outputs with the combine's own fp32 addition
+hipError_t launch_fold_split(const Dims& D, const int32_t* offsets, float* Y,
+                             const float* Ypart, hipStream_t s);
 // gemm_f32.hip (fp32 activations and weights, VALU)
 hipError_t launch_ffn_f32(const Dims& D, const int32_t* offsets,
                           const int32_t* sorted_token, const void* x,
@@ -112,7 +125,8 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
                               hipStream_t s);
 
 // combine.hip (expert outputs are fp32)
-hipError_t launch_combine(const Dims& D, const void* y_rows,
+// y_part (may be null): second K split of the expert rows, added to y_rows
+hipError_t launch_combine(const Dims& D, const void* y_rows, const float* y_part,
                           const int32_t* slot_row, const float* topk_w,
                           const void* y_shared, void* out, hipStream_t s);
 

@@ -45,6 +45,10 @@ MEDIUM = {
     "f32-swiglu-shared": C("f32-swiglu-shared", 111, T=150, d=48, E=5, top_k=2, F=40,
                            act_dtype=synth.F32, weight_dtype=synth.F32, shared_experts=2,
                            shared_F=24, capacity_factor=1.5),
+    # down projection long enough (F >= 1024) and with few enough tiles that
+    # its reduction is split in two K halves, with capacity drops
+    "swiglu-bf16-splitk": C("swiglu-bf16-splitk", 113, T=600, d=256, E=4, top_k=2,
+                            F=1024, capacity_factor=1.25),
     # bf16 shared expert with ReLU and many tokens (several M tiles)
     "relu-shared-tiles": C("relu-shared-tiles", 112, T=1100, d=256, E=8, top_k=2, F=256,
                            act=synth.RELU, shared_experts=1, shared_F=320),
@@ -103,12 +107,15 @@ def test_single_token_and_empty_batch():
     assert torch.all(out == 7.0)
 
 
-def test_stagewise_api_matches_layer():
+@pytest.mark.parametrize("name", ["sigmoid-group-shared", "swiglu-bf16-splitk"])
+def test_stagewise_api_matches_layer(name):
     """moe_route -> moe_dispatch (with the permuted copy) -> moe_grouped_ffn
     -> moe_combine, called one by one, equal the fused moe_layer_forward
-    bit for bit, and each stage matches the oracle."""
+    bit for bit, and each stage matches the oracle.  The second case splits
+    the down projection's reduction: the stage API folds the halves into
+    its expert rows, the fused layer adds them in the combine."""
     import mixture_experts_layer_group_amd as moe
-    cfg = MEDIUM["sigmoid-group-shared"]
+    cfg = MEDIUM[name]
     inp = gu.make_inputs(cfg)
     spec = moe.spec_from_config(cfg)
     T, k, E, d = cfg.T, cfg.top_k, cfg.E, cfg.d
