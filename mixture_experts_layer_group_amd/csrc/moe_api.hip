@@ -114,6 +114,7 @@ Dims dims_of(const moe_spec& s, int64_t T) {
   D.u4 = s.weight_dtype == MOE_DTYPE_U4_AFFINE;
   D.swiglu = s.act == MOE_ACT_SWIGLU;
   D.out_bf16 = s.out_dtype == MOE_DTYPE_BF16;
+  D.router_dtype = s.router_dtype;
   return D;
 }
 
@@ -131,7 +132,9 @@ WsLayout layout_of(const Dims& D) {
     o = align_up(o + bytes);
     return at;
   };
-  L.logits = take(T * E * 4);
+  const RouterPlan rp = router_plan(D, D.router_dtype);
+  L.logits = take(static_cast<size_t>(rp.S) * T * E * 4);
+  L.w3 = take(rp.mfma && rp.npass == 3 ? 3 * E * static_cast<size_t>(D.d) * 2 : 0);
   L.probpart = take(static_cast<size_t>(L.route_blocks) * E * 4);
   L.hist = take(static_cast<size_t>(L.dispatch_blocks) * E * 4);
   L.tiles1 = take((E + 1) * 4);
@@ -184,12 +187,25 @@ moe_status do_route(const moe_spec& sp, const Dims& D, const WsLayout& L,
                     const void* x, const void* wr, const float* bias,
                     int32_t* ids, float* w, float* logits, float* prob_sum,
                     void* ws, hipStream_t s) {
-  float* Lg = logits ? logits : at<float>(ws, L.logits);
-  hipError_t e = launch_router_logits(D, sp.act_dtype, sp.router_dtype, x, wr, Lg, s);
+  const RouterPlan rp = router_plan(D, sp.router_dtype);
+  hipError_t e;
+  float* Lg;
+  float* Lout = nullptr;
+  if (rp.mfma) {
+    // partial logits in the workspace; the selection adds them and hands
+    // the sums to the caller's buffer if one was given
+    Lg = at<float>(ws, L.logits);
+    Lout = logits;
+    e = launch_router_mfma(D, rp, x, wr, at<uint16_t>(ws, L.w3), Lg, s);
+  } else {
+    Lg = logits ? logits : at<float>(ws, L.logits);
+    e = launch_router_logits(D, sp.act_dtype, sp.router_dtype, x, wr, Lg, s);
+  }
   if (e != hipSuccess) return MOE_ERR_HIP;
   const bool want_p = prob_sum != nullptr && sp.router == MOE_ROUTER_SOFTMAX_TOPK;
   float* part = want_p ? at<float>(ws, L.probpart) : nullptr;
-  e = launch_router_select(D, sp, Lg, bias, ids, w, part, L.route_blocks, s);
+  e = launch_router_select(D, sp, Lg, rp.mfma ? rp.S : 1, Lout, bias, ids, w, part,
+                           L.route_blocks, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (want_p) return hip_status(launch_prob_finalize(D, part, L.route_blocks, prob_sum, s));
   return MOE_OK;

@@ -45,11 +45,23 @@ struct Dims {
   bool u4;            // 4-bit routed weights
   bool swiglu;
   bool out_bf16;      // layer output in bf16 (else fp32)
+  int router_dtype;   // MOE_DTYPE_* of the router weights
 };
+
+// Router logits plan for bf16 activations (matrix cores, router_mfma.hip):
+// tiles of 128 tokens x BN experts, the reduction over d split over S
+// workgroups whose partial logits the selection adds in order; npass = 3
+// when fp32 router weights are split into three bf16 parts.
+struct RouterPlan {
+  bool mfma;       // false: fp32 activations, vector-ALU kernels, S = 1
+  int npass, BN, mtiles, ntiles, kt_total, kt_split, S;
+};
+RouterPlan router_plan(const Dims& D, int router_dtype);
+constexpr int kMaxLogitPlanes = 16;  // largest S
 
 // Workspace carve-up (byte offsets, each 256-aligned).
 struct WsLayout {
-  size_t logits, probpart, hist, tiles1, tiles2;
+  size_t logits, w3, probpart, hist, tiles1, tiles2;  // logits: [S][T][E] partials
   size_t topk_ids, topk_w, counts, offsets, sorted_token, sorted_w, slot_row,
       dropped;
   size_t H, Hs, Y, Ypart, Ys;
@@ -80,10 +92,17 @@ int down_splits(const Dims& D);
 hipError_t launch_router_logits(const Dims& D, int act_dtype, int router_dtype,
                                 const void* x, const void* wr, float* logits,
                                 hipStream_t s);
+// logits: S planes of partial logits [S][T][E], added in plane order;
+// logits_out (may be null) receives the summed logits
 hipError_t launch_router_select(const Dims& D, const moe_spec& sp,
-                                const float* logits, const float* bias,
-                                int32_t* ids, float* w, float* probpart,
-                                int nblocks, hipStream_t s);
+                                const float* logits, int S, float* logits_out,
+                                const float* bias, int32_t* ids, float* w,
+                                float* probpart, int nblocks, hipStream_t s);
+// router_mfma.hip: partial logits of plan p into part ([p.S][T][E]); w3
+// holds 3*E*d bf16 when p.npass == 3
+hipError_t launch_router_mfma(const Dims& D, const RouterPlan& p, const void* x,
+                              const void* wr, uint16_t* w3, float* part,
+                              hipStream_t s);
 hipError_t launch_prob_finalize(const Dims& D, const float* probpart,
                                 int nblocks, float* prob_sum, hipStream_t s);
 

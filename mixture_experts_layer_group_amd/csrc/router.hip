@@ -242,7 +242,8 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
 // One wave per token; EPL = experts per lane (expert lane + 64*j).
 template <int EPL>
 __global__ void __launch_bounds__(256)
-select_kernel(const float* __restrict__ L, const float* __restrict__ bias,
+select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
+              const float* __restrict__ bias,
               int32_t* __restrict__ ids, float* __restrict__ wout,
               float* __restrict__ probpart, int64_t T, int E, int k,
               int router, int norm, float scaling, int n_group,
@@ -265,7 +266,21 @@ select_kernel(const float* __restrict__ L, const float* __restrict__ bias,
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + kWave * j;
-      v[j] = e < E ? L[t * E + e] : 0.f;
+      float lv = 0.f;
+      if (e < E) {
+        // partial logit planes added in plane order
+        // all planes are loaded before the (in-order) additions
+        float pv[kMaxLogitPlanes];
+#pragma unroll
+        for (int q = 0; q < kMaxLogitPlanes; ++q)
+          pv[q] = q < S ? L[(q * T + t) * E + e] : 0.f;
+        lv = pv[0];
+#pragma unroll
+        for (int q = 1; q < kMaxLogitPlanes; ++q)
+          if (q < S) lv += pv[q];
+        if (Lout) Lout[t * E + e] = lv;
+      }
+      v[j] = lv;
       sc[j] = 0.f;
       if (e < E) cand |= 1u << j;
     }
@@ -435,15 +450,16 @@ hipError_t launch_router_logits(const Dims& D, int act_dtype, int router_dtype,
 }
 
 hipError_t launch_router_select(const Dims& D, const moe_spec& sp,
-                                const float* logits, const float* bias,
-                                int32_t* ids, float* w, float* probpart,
-                                int nblocks, hipStream_t s) {
+                                const float* logits, int S, float* logits_out,
+                                const float* bias, int32_t* ids, float* w,
+                                float* probpart, int nblocks, hipStream_t s) {
   const int epl = (D.E + kWave - 1) / kWave;
   const float scaling =
       sp.router == MOE_ROUTER_SIGMOID_GROUP ? sp.routed_scaling : 1.0f;
 #define MOE_SELECT(N)                                                        \
   hipLaunchKernelGGL((select_kernel<N>), dim3(nblocks), dim3(256), 0, s,     \
-                     logits, bias, ids, w, probpart, D.T, D.E, D.k, sp.router, \
+                     logits, S, logits_out, bias, ids, w, probpart, D.T, D.E,  \
+                     D.k, sp.router,                                            \
                      sp.norm_topk_prob, scaling, sp.n_group, sp.topk_group)
   if (epl <= 1) MOE_SELECT(1);
   else if (epl <= 2) MOE_SELECT(2);

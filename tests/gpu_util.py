@@ -94,11 +94,18 @@ def bank_for(cfg, inp) -> oracle.ExpertBank:
 
 
 def logits_bound(x_h, wr_h, d):
+    """Forward error bound of an fp32-accumulated dot product, in any
+    summation order, gamma_n * sum |x||w|.  bf16 activations with fp32
+    router weights are evaluated as 3d exact bf16 products (each weight
+    split into three bf16 parts whose magnitudes add up to at most
+    (1 + 2^-7)|w|), so n = 3d there; otherwise n = d."""
     u = 2.0 ** -24
-    gamma = d * u / (1 - d * u)
+    split = x_h.dtype == np.uint16 and wr_h.dtype == np.float32
+    n = 3 * d if split else d
+    gamma = n * u / (1 - n * u)
     X = np.abs(oracle.as_f64(x_h))
     W = np.abs(oracle.as_f64(wr_h))
-    return gamma * (X @ W.T)
+    return gamma * (1.0 + 2.0 ** -7 if split else 1.0) * (X @ W.T)
 
 
 def check_route(cfg, inp, r, full_logits_check=True):

@@ -49,6 +49,12 @@ MEDIUM = {
     # its reduction is split in two K halves, with capacity drops
     "swiglu-bf16-splitk": C("swiglu-bf16-splitk", 113, T=600, d=256, E=4, top_k=2,
                             F=1024, capacity_factor=1.25),
+    # router tile widths of the matrix-core logits: 37 experts with fp32
+    # router weights (three bf16 parts, 64-wide tile, ragged expert tail) and
+    # 100 experts with bf16 router weights (128-wide tile)
+    "router-e37-fp32": C("router-e37-fp32", 114, T=400, d=192, E=37, top_k=3, F=64),
+    "router-e100-bf16": C("router-e100-bf16", 115, T=300, d=128, E=100, top_k=5, F=64,
+                          router_dtype=synth.BF16),
     # bf16 shared expert with ReLU and many tokens (several M tiles)
     "relu-shared-tiles": C("relu-shared-tiles", 112, T=1100, d=256, E=8, top_k=2, F=256,
                            act=synth.RELU, shared_experts=1, shared_F=320),
