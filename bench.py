@@ -16,6 +16,9 @@ workload (cpu_baseline).
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -39,6 +42,45 @@ def expert_flops(cfg, n_kept: int) -> float:
     if cfg.shared_experts:
         f += 2.0 * mats * cfg.d * cfg.shared_F * cfg.T * cfg.shared_experts
     return f
+
+
+# sources of the kernels one grouped-FFN call runs (tile prefix, both expert
+# GEMMs, the fold of a split down projection): a traffic summary measured on
+# other sources is stale
+TRAFFIC_SOURCES = ("csrc/gemm_bf16.hip", "csrc/dispatch.hip", "csrc/combine.hip")
+COPY_BYTES = 1 << 30  # calibration kernel: reads and writes 1 GiB
+
+
+def sources_digest() -> str:
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_group_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_summary_path(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"grouped_ffn_{workload}_hbm_traffic.md")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per grouped-FFN call from the committed counter summary, or
+    None when there is none or it was taken on other kernel sources."""
+    path = traffic_summary_path(workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                vals[k.strip("`")] = v.strip().strip("`")
+    if vals.get("sources_sha256") != sources_digest():
+        return None
+    try:
+        return float(vals["bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, inp, sample: int):
@@ -74,14 +116,19 @@ def cpu_baseline(cfg, inp, sample: int):
         if inp.get(name) is not None:
             for e in range(inp[name].shape[0]):
                 fetch(name, e)
-    t0 = time.perf_counter()
-    oracle.layer(host["x"], host["w_router"], bank, spec, host.get("expert_bias"),
-                 tokens=toks)
-    dt = time.perf_counter() - t0
-    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": int(threads),
+    # repeat whole oracle calls until about 10 s of CPU work (at most 4)
+    reps, dt = 0, 0.0
+    while reps < 4 and (reps == 0 or dt < 10.0):
+        t0 = time.perf_counter()
+        oracle.layer(host["x"], host["w_router"], bank, spec, host.get("expert_bias"),
+                     tokens=toks)
+        dt += time.perf_counter() - t0
+        reps += 1
+    return {"value": reps * len(toks) / dt, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"routing+dispatch of all {cfg.T} tokens, expert FFN+combine of "
-                      f"{len(toks)} seeded tokens (fp64 NumPy), {dt:.1f} s",
+            "sample": f"{reps} oracle layer calls, each routing+dispatch of all {cfg.T} tokens "
+                      f"and expert FFN+combine of {len(toks)} seeded tokens (fp64 NumPy), "
+                      f"{dt:.1f} s in total",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -91,10 +138,16 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload id (1-5)")
-    ap.add_argument("--cpu-sample", type=int, default=2048,
+    ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens whose expert FFN the CPU oracle evaluates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run a 1 GiB copy and three grouped-FFN calls, for rocprofv3 --pmc")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two --pmc runs of --traffic-probe into the profiles/ summary")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        return summarize_traffic(args)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
@@ -121,6 +174,9 @@ def main() -> int:
     def step():
         moe.moe_layer_forward(spec, T, inp["x"], inp["w_router"], inp["expert_bias"],
                               w, out, stats=stats, workspace=ws)
+
+    if args.traffic_probe:
+        return traffic_probe(torch, moe, spec, cfg, inp, w, offsets, sorted_token, ws, step)
 
     for _ in range(args.warmup):
         step()
@@ -178,15 +234,114 @@ def main() -> int:
         "grouped_gemm_tflops": tflops,
         "grouped_gemm_frac_peak": tflops / PEAK_BF16_TFLOPS,
         "kept_rows": n_kept,
-        "roofline": {"bound": "mfma", "kernel": "grouped expert FFN (GEMM1 gate/up + "
-                     "SwiGLU, GEMM2 down)", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
-                     "flops_per_launch": flops, "avg_launch_ms": ffn_ms,
-                     "traffic": None},
+        "roofline": {"bound": "mfma", "kernel": "grouped expert FFN call (tile prefix, "
+                     "GEMM1 gate/up + SwiGLU, GEMM2 down, split fold)", "achieved": tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_BF16_TFLOPS, "flops_per_launch": flops,
+                     "avg_launch_ms": ffn_ms, "traffic": measured_traffic(cfg.name)},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
     print(json.dumps(res), flush=True)
+    return 0
+
+
+def traffic_probe(torch, moe, spec, cfg, inp, w, offsets, sorted_token, ws, step) -> int:
+    """Kernels for the HBM-traffic counters: an elementwise negation that
+    reads and writes COPY_BYTES (the calibration of FETCH_SIZE and
+    WRITE_SIZE), then three grouped-FFN calls on the routed batch."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    step()  # routing and dispatch for the FFN calls
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    y = torch.empty((cfg.T * cfg.top_k, cfg.d), dtype=torch.float32, device="cuda")
+    ysh = (torch.empty((cfg.shared_experts * cfg.T, cfg.d), dtype=torch.float32,
+                       device="cuda") if cfg.shared_experts else None)
+    for _ in range(3):
+        moe.moe_grouped_ffn(spec, cfg.T, offsets, sorted_token, inp["x"], w, y, ysh, ws)
+    torch.cuda.synchronize()
+    print("traffic probe done", flush=True)
+    return 0
+
+
+FFN_KERNELS = ("grouped_gemm_kernel", "tile_prefix_kernel", "fold_split_kernel")
+
+
+def _counter_rows(d):
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def summarize_traffic(args) -> int:
+    """profiles/ summary of HBM traffic per grouped-FFN call: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) of the FFN kernels, each scaled by the
+    ratio of the calibration kernel's known bytes to what the same counter
+    read for it."""
+    import synth
+    cfg = synth.CONFIGS[args.config]
+    res = {}
+    for counter, d in (("FETCH_SIZE", args.summarize_traffic[0]),
+                       ("WRITE_SIZE", args.summarize_traffic[1])):
+        copy_kib, ffn = [], {}
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == counter]
+        copies = [r for r in rows if "neg_kernel" in r["Kernel_Name"]]
+        # the FFN calls are the dispatches after the last calibration copy
+        last_copy = max((int(r["Dispatch_Id"]) for r in copies), default=None)
+        for r in copies:
+            copy_kib.append(float(r["Counter_Value"]))
+        for r in rows:
+            if last_copy is None or int(r["Dispatch_Id"]) <= last_copy:
+                continue
+            name = r["Kernel_Name"]
+            for k in FFN_KERNELS:
+                if k in name:
+                    key = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+                    ffn.setdefault(key, []).append(float(r["Counter_Value"]))
+        if not copy_kib or not ffn:
+            print(f"no calibration or FFN dispatches for {counter} in {d}", file=sys.stderr)
+            return 1
+        factor = COPY_BYTES / (sum(copy_kib) / len(copy_kib) * 1024.0)
+        # per call: every FFN kernel's mean per dispatch times its dispatches per call
+        per_call = 0.0
+        per_kernel = {}
+        for k, vs in ffn.items():
+            calls = 3
+            kib = sum(vs) / calls
+            per_kernel[k] = kib * 1024.0 * factor
+            per_call += per_kernel[k]
+        res[counter] = {"factor": factor, "copy_kib": copy_kib, "per_call": per_call,
+                        "per_kernel": per_kernel}
+    total = res["FETCH_SIZE"]["per_call"] + res["WRITE_SIZE"]["per_call"]
+    path = traffic_summary_path(cfg.name)
+    rel = os.path.relpath(path, ROOT)
+    with open(path, "w") as f:
+        f.write(f"# HBM traffic of one grouped-FFN call, {cfg.name}\n\n")
+        f.write("Commands (repository root, one MI355X; the probe runs a 1 GiB elementwise "
+                "negation for calibration, then three grouped-FFN calls):\n\n```\n")
+        f.write("cd /tmp && export TMPDIR=/tmp\n")
+        for c, dd in (("FETCH_SIZE", "pmc_fetch"), ("WRITE_SIZE", "pmc_write")):
+            f.write(f"timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d $REPO/gpurun_out/{dd} "
+                    f"-o p -- python3 $REPO/bench.py --config {cfg.cfg_id} --traffic-probe\n")
+        f.write(f"python3 $REPO/bench.py --config {cfg.cfg_id} --summarize-traffic "
+                "$REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write\n```\n\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            r = res[c]
+            f.write(f"{c}: calibration read {sum(r['copy_kib']) / len(r['copy_kib']):.0f} KiB for "
+                    f"{COPY_BYTES >> 10} KiB moved, factor {r['factor']:.4f}\n\n")
+            f.write("| kernel | bytes per call (scaled) |\n|---|---|\n")
+            for k, b in sorted(res[c]["per_kernel"].items()):
+                f.write(f"| `{k}` | {b:.4g} |\n")
+            f.write("\n")
+        f.write(f"- fetch_bytes_per_call: {res['FETCH_SIZE']['per_call']:.6g}\n")
+        f.write(f"- write_bytes_per_call: {res['WRITE_SIZE']['per_call']:.6g}\n")
+        f.write(f"- bytes_per_call: {total:.6g}\n")
+        f.write(f"- sources_sha256: {sources_digest()}\n")
+    print(f"wrote {rel}: {total / 1e9:.3f} GB per call", flush=True)
     return 0
 
 
