@@ -62,17 +62,19 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kRowBytes = BK * 2;           // 128
-constexpr int kTileBytes = BM * kRowBytes;  // 32 KiB per operand per stage
+constexpr int BM = kGemm1BM, BN = 256, BK = 64;
+constexpr int kRowBytes = BK * 2;            // 128
+constexpr int kTileBytesA = BM * kRowBytes;  // activation tile per stage
+constexpr int kTileBytesW = BN * kRowBytes;  // weight tile per stage (32 KiB)
 constexpr int kNG = 8;                      // N-tiles per scheduling column group
 constexpr int kWaves = 8;                   // 2 waves per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr int kWavesN = 4;                  // waves along N (2 along M)
-constexpr int MB = 4, NB = 2;               // 32x32 blocks per wave: 128 x 64
-constexpr int kLoads = 32 / kWaves;         // 1 KiB direct loads per operand per wave
-constexpr int kTailJ = 4;                   // load pairs issued after the barrier (rest: sub-step 0)
-static_assert(BM == kGemm1BM && BM == kGemm2BM, "tile prefix BM mismatch");
+constexpr int MB = BM / 64, NB = 2;         // 32x32 blocks per wave: (BM/2) x 64
+constexpr int kLoadsA = kTileBytesA / 1024 / kWaves;  // 1 KiB direct loads per wave
+constexpr int kLoadsW = kTileBytesW / 1024 / kWaves;
+static_assert(BM == kGemm2BM && BM % 64 == 0, "tile prefix BM mismatch");
+static_assert(kTileBytesA % (1024 * kWaves) == 0, "whole direct loads per wave");
 
 enum Mode { kSwiGLU = 0, kReLU = 1, kDown = 2 };
 
@@ -141,9 +143,9 @@ __device__ __forceinline__ half8 bf16x8_to_f16x8(bf16x8 v) {
 template <int MODE, bool GATHER>
 __global__ void __launch_bounds__(kThreads, 1)
 grouped_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kTileBytes];
-  uint8_t* sA = smem;                   // [2][BM rows][128 B]
-  uint8_t* sW = smem + 2 * kTileBytes;  // [2][BN rows][128 B]
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kTileBytesA + kTileBytesW)];
+  uint8_t* sA = smem;                    // [2][BM rows][128 B]
+  uint8_t* sW = smem + 2 * kTileBytesA;  // [2][BN rows][128 B]
 
   // ---------------- tile scheduling
   const int total_mt = g.tiles ? g.tiles[g.E] : (g.single_rows + BM - 1) / BM;
@@ -214,9 +216,9 @@ grouped_gemm_kernel(GemmArgs g) {
       const_cast<uint16_t*>(wbase0), (short)0, -1, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsW1 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(wbase1), (short)0, -1, 0x00020000);
-  uint32_t voffA[kLoads], voffW[kLoads];
+  uint32_t voffA[kLoadsA], voffW[kLoadsW];
 #pragma unroll
-  for (int j = 0; j < kLoads; ++j) {
+  for (int j = 0; j < kLoadsA; ++j) {
     const int r = (j * kWaves + wave) * 8 + (lane >> 3);  // tile row
     const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);     // chunk at position lane%8
     const int m = m0 + r;
@@ -227,6 +229,11 @@ grouped_gemm_kernel(GemmArgs g) {
     } else {
       voffA[j] = g.a_bytes;  // past the group: out of range, no fetch
     }
+  }
+#pragma unroll
+  for (int j = 0; j < kLoadsW; ++j) {
+    const int r = (j * kWaves + wave) * 8 + (lane >> 3);  // tile row
+    const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);     // chunk at position lane%8
     int n = (MODE == kSwiGLU) ? nt * (BN / 2) + (r & 127) : nt * BN + r;
     if (n > g.N - 1) n = g.N - 1;
     voffW[j] = static_cast<uint32_t>(static_cast<int64_t>(n) * K * 2 + c * 16);
@@ -247,7 +254,7 @@ grouped_gemm_kernel(GemmArgs g) {
       wrow[nb] = wn * 64 + nb * 32 + fr;
   }
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) arow_l[mb] = wm * 128 + mb * 32 + fr;
+  for (int mb = 0; mb < MB; ++mb) arow_l[mb] = wm * (MB * 32) + mb * 32 + fr;
 
   f32x16 acc[NB][MB];
 #pragma unroll
@@ -259,21 +266,21 @@ grouped_gemm_kernel(GemmArgs g) {
 
   const int KT = g.K / BK / g.ksplit;  // K steps of this split
   const int kbase = split * KT;
-  auto issue = [&](int kt, int buf, int j0, int j1) {
+  auto issue = [&](int kt, int buf) {
     const int soff = (kbase + kt) * kRowBytes;  // K advance in bytes
-    uint8_t* a = sA + buf * kTileBytes;
-    uint8_t* w = sW + buf * kTileBytes;
+    uint8_t* a = sA + buf * kTileBytesA;
+    uint8_t* w = sW + buf * kTileBytesW;
 #pragma unroll
-    for (int j = j0; j < j1; ++j) {
-      const int blk = (j * kWaves + wave) * 1024;
+    for (int j = 0; j < kLoadsA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsA, (__attribute__((address_space(3))) void*)(a + blk), 16, voffA[j],
-          soff, 0, 0);
+          rsA, (__attribute__((address_space(3))) void*)(a + (j * kWaves + wave) * 1024), 16,
+          voffA[j], soff, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kLoadsW; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          j < kLoads / 2 ? rsW0 : rsW1,
-          (__attribute__((address_space(3))) void*)(w + blk), 16, voffW[j], soff,
-          0, 0);
-    }
+          j < kLoadsW / 2 ? rsW0 : rsW1,
+          (__attribute__((address_space(3))) void*)(w + (j * kWaves + wave) * 1024), 16,
+          voffW[j], soff, 0, 0);
   };
 
   // fragments are double-buffered in registers: the LDS reads for K
@@ -286,8 +293,8 @@ grouped_gemm_kernel(GemmArgs g) {
   frag_t wf[2][NB], af[2][MB];
   bf16x8 wraw[2][NB];
   auto read_frags = [&](int buf, int ks, int fb) {
-    const uint8_t* a = sA + buf * kTileBytes;
-    const uint8_t* w = sW + buf * kTileBytes;
+    const uint8_t* a = sA + buf * kTileBytesA;
+    const uint8_t* w = sW + buf * kTileBytesW;
     const int ch = ks * 2 + fh;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -339,41 +346,34 @@ grouped_gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
   };
-  // sub-step with NJ load pairs (2*NJ direct loads) spread over its MFMAs
-  auto pace_loads = [&](auto nj_tag) {
-    constexpr int NJ = decltype(nj_tag)::value;
-    constexpr int kV = 2 * NJ > 0 ? 2 * NJ : 1;  // direct loads in this sub-step
-    static_assert(kV <= NB * MB && (NB * MB) % kV == 0, "load spread");
-    constexpr int kEvery = NB * MB / kV;
+  // the sub-step that issues a K step's direct loads: fragment reads first,
+  // then the loads spread evenly over its MFMAs
+  auto pace_loads = [&]() {
+    constexpr int kV = kLoadsA + kLoadsW;  // direct loads in this sub-step
+    constexpr int NM = NB * MB;
+    static_assert(kV <= 2 * NM, "load spread");
     __builtin_amdgcn_sched_group_barrier(0x100, NB + MB, 0);  // DS read
 #pragma unroll
-    for (int i = 0; i < NB * MB; ++i) {
-      if (i % kEvery == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+    for (int i = 0; i < NM; ++i) {
+      const int n_here = ((i + 1) * kV) / NM - (i * kV) / NM;
+      if (n_here >= 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
+      if (n_here >= 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
       if (MODE == kDown) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
   };
   // Load pipeline.  The loads of K tile t+1 go into the buffer that tile
-  // t-1 used: kTailJ load pairs are issued right after the barrier that
-  // ends tile t-1 (that buffer is free from then on), during tile t-1's
-  // last MFMAs, and the remaining pairs during tile t's first sub-step.  So
-  // the memory pipe never idles across the barrier, and tile t+1 has nearly
+  // t-1 used: they are issued right after the barrier that ends tile t-1
+  // (that buffer is free from then on), during tile t-1's last MFMAs, so
+  // the memory pipe never idles across the barrier and tile t+1 has nearly
   // a whole tile of MFMAs to arrive in.
-  constexpr int kSubJ = kLoads - kTailJ;
   auto tile = [&](int kt, auto kind_tag) {
-    constexpr int kind = decltype(kind_tag)::value;  // 0 full, 1 no tail loads, 2 last
+    constexpr int kind = decltype(kind_tag)::value;  // 0 full, 1 no loads, 2 last
     const int cur = kt & 1;
     read_frags(cur, 1, 1);
-    if constexpr (kind != 2 && kSubJ > 0) {
-      issue(kt + 1, cur ^ 1, kTailJ, kLoads);
-      mfmas(0);
-      convert(1);
-      pace_loads(std::integral_constant<int, kSubJ>{});
-    } else {
-      mfmas(0);
-      convert(1);
-      pace();
-    }
+    mfmas(0);
+    convert(1);
+    pace();
     read_frags(cur, 2, 0);
     mfmas(1);
     convert(0);
@@ -389,11 +389,11 @@ grouped_gemm_kernel(GemmArgs g) {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __syncthreads();
       read_frags(cur ^ 1, 0, 0);
-      if constexpr (kind == 0 && kTailJ > 0) {
-        issue(kt + 2, cur, 0, kTailJ);
+      if constexpr (kind == 0) {
+        issue(kt + 2, cur);
         mfmas(1);
         convert(0);
-        pace_loads(std::integral_constant<int, kTailJ>{});
+        pace_loads();
       } else {
         mfmas(1);
         convert(0);
@@ -404,8 +404,8 @@ grouped_gemm_kernel(GemmArgs g) {
     }
   };
 
-  issue(0, 0, 0, kLoads);
-  if (KT > 1) issue(1, 1, 0, kTailJ);
+  issue(0, 0);
+  if (KT > 1) issue(1, 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   read_frags(0, 0, 0);
