@@ -5,7 +5,7 @@
 // Built for decode-shaped batches, where each touched expert sees a handful
 // of rows and the layer is bound by streaming the packed weights from HBM:
 // every weight byte is read once, 16 bytes per lane, and reused from
-// registers for all of the expert's rows, which sit in LDS.  The affine
+// registers for all of the expert's rows.  The affine
 // dequantisation is factored per group so no dequantised weight is formed:
 //   sum_j x_j (s q_j + b) = s * sum_j x_j q_j + b * sum_j x_j
 // over the 32-element run a lane owns (always inside one group of 64), and
@@ -25,8 +25,6 @@
 namespace moe {
 namespace {
 
-constexpr int kRC = 8;            // expert rows staged in LDS per pass
-constexpr int kUnitsPerBlock = 64;
 constexpr int kMaxK = 2048;  // one pass of 64 lanes x 32 elements per row
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -53,8 +51,30 @@ __device__ __forceinline__ float dot32(const uint4& w, const half2_t* xp) {
   return acc;
 }
 
+// sum over one lane's 32 elements of x_i * (1024 + q_i) for R rows at once,
+// each code pair unpacked once: out[r * stride] for row r
+template <int R>
+__device__ __forceinline__ void dots(const uint4& w, const half2_t (*xp)[16], float* out,
+                                     int stride) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half2_t cp = code_pair(ws[m], j);
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        acc[r] = __builtin_amdgcn_fdot2(cp, xp[r][m * 4 + j], acc[r], false);
+    }
+#pragma unroll
+  for (int r = 0; r < R; ++r) out[r * stride] = acc[r];
+}
+
 // a lane's 32 activation values of one row (bf16 tokens or fp16 hidden
-// rows, from LDS) as fp16 pairs matching code_pair, and their fp32 sum
+// rows) as fp16 pairs matching code_pair, and their fp32 sum
 template <bool BF16>
 __device__ __forceinline__ float load_pairs(const uint16_t* p, half2_t* xp) {
   float sum = 0.f;
@@ -85,107 +105,184 @@ __device__ __forceinline__ float load_pairs(const uint16_t* p, half2_t* xp) {
   return sum;
 }
 
-constexpr int kRowsPerPass = 2;  // expert rows multiplied per weight pass
+// In-place reduction of V per-lane values over each group of LPR lanes
+// (LPR and V powers of two).  Butterfly with halving: at distance D the
+// lane with bit D set keeps the upper half of its values and sends the
+// lower half, so each exchange carries half of the values and V values cost
+// about V shuffles in all instead of V*log2(LPR).  On return a lane holds
+// C = max(1, V/LPR) totals in v[0..C): those of indices
+// reduce_index(lane, j), identical on lanes that differ only below the
+// last halving distance.
+template <int D, int CNT, int V>
+__device__ __forceinline__ void reduce_step(float (&v)[V], int lane) {
+  if constexpr (D >= 1) {
+    if constexpr (CNT > 1) {
+      constexpr int kHalf = CNT / 2;
+      const bool upper = (lane & D) != 0;
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) {
+        const float send = upper ? v[i] : v[i + kHalf];
+        const float keep = upper ? v[i + kHalf] : v[i];
+        v[i] = keep + __shfl_xor(send, D, 64);
+      }
+      reduce_step<D / 2, kHalf, V>(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], D, 64);
+      reduce_step<D / 2, 1, V>(v, lane);
+    }
+  }
+}
 
-// One lane owns 32 consecutive K elements (inside one quantisation group);
-// LPR = lanes per unit.  sum_i x_i (s q_i + b) = s (sum x_i (1024 + q_i)
-// - 1024 sum x_i) + b sum x_i.
-template <bool PAIR, int LPR>
+template <int V, int LPR>
+__device__ __forceinline__ void multi_reduce(float (&v)[V], int lane) {
+  reduce_step<LPR / 2, V, V>(v, lane);
+}
+
+// index of v[j] after multi_reduce<V, LPR> on this lane
+template <int V, int LPR>
+__device__ __forceinline__ int reduce_index(int lane, int j) {
+  int idx = j, c = V;
+#pragma unroll
+  for (int d = LPR / 2; d >= 1 && c > 1; d >>= 1) {
+    c /= 2;
+    if (lane & d) idx += c;
+  }
+  return idx;
+}
+
+// lowest lane distance at which multi_reduce<V, LPR> still halves
+template <int V, int LPR>
+constexpr int last_halving_distance() {
+  int c = V, last = LPR;
+  for (int d = LPR / 2; d >= 1 && c > 1; d >>= 1) {
+    c /= 2;
+    last = d;
+  }
+  return last;
+}
+
+// Decode-shaped grouped expert FFN, one workgroup per (expert, block of
+// units).  Each wave owns UB * (64/LPR) consecutive units; LPR lanes share a
+// unit and each lane owns 32 consecutive K elements (inside one
+// quantisation group).  All of a wave's packed weights (UB 16-byte loads
+// per matrix) and their scales and biases are requested before any
+// arithmetic, so a wave keeps 16 B x UB x (1 or 2) per lane in flight; the
+// expert's rows are then taken one at a time (each lane reads its own 32
+// elements of the row) against the weights held in registers, and the
+// per-lane partial sums of every unit and matrix are reduced together by
+// multi_reduce.
+template <bool PAIR, int LPR, int UB>
 __global__ void __launch_bounds__(256)
 u4_kernel(const int32_t* __restrict__ offsets,
           const int32_t* __restrict__ sorted_token,  // nullptr: a rows direct
           const uint16_t* __restrict__ a,             // [.., K] bf16 x or fp16 H
           const uint32_t* __restrict__ q0,            // [E][N][K/8]
-          const uint16_t* __restrict__ s0,            // [E][N][K/G]
+          const uint16_t* __restrict__ s0,            // [E][N][K/64]
           const uint16_t* __restrict__ b0,
           const uint32_t* __restrict__ q1,            // up (PAIR)
           const uint16_t* __restrict__ s1,
           const uint16_t* __restrict__ b1,
-          void* __restrict__ out, int N, int K, int G) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [kRC][K]
+          void* __restrict__ out, int N) {
+  constexpr int K = 32 * LPR;
+  constexpr int UPW = 64 / LPR;     // units per wave-wide load
+  constexpr int UPWB = UB * UPW;    // units per wave
+  constexpr int UPB = 4 * UPWB;     // units per workgroup
+  constexpr int RP = 1;
+  constexpr int M = PAIR ? 2 : 1;   // matrices
+  constexpr int V = UB * RP * M;    // partial sums per lane and pass
+  constexpr int C = V / LPR > 1 ? V / LPR : 1;
   const int e = blockIdx.x;
   const int32_t row0 = offsets[e];
   const int cnt = offsets[e + 1] - row0;
   if (cnt <= 0) return;
-  const int u_base = blockIdx.y * kUnitsPerBlock;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  constexpr int UPW = 64 / LPR;  // units per wave pass
   const int sg = lane / LPR, kl = lane % LPR;
-  const int words = K / 8, groups = K / G;
+  const int ubase = blockIdx.y * UPB + wave * UPWB;
+  constexpr int words = K / 8, groups = K / 64;
+  const int gi = kl / 2;  // this lane's quantisation group
 
-  for (int rc0 = 0; rc0 < cnt; rc0 += kRC) {
-    const int nr = min(kRC, cnt - rc0);
-    __syncthreads();
-    // stage the rows [rc0, rc0+nr) in LDS, 16 bytes per thread
-    const int vec_per_row = K / 8;
-    for (int i = threadIdx.x; i < nr * vec_per_row; i += blockDim.x) {
-      const int r = i / vec_per_row, c = i % vec_per_row;
-      const int64_t src = sorted_token ? sorted_token[row0 + rc0 + r]
-                                       : static_cast<int64_t>(row0 + rc0 + r);
-      reinterpret_cast<uint4*>(xs)[static_cast<int64_t>(r) * vec_per_row + c] =
-          reinterpret_cast<const uint4*>(a + src * K)[c];
+  // ---- all weight requests of the wave first
+  uint4 w0[UB], w1[UB];
+  float sc0[UB], bi0[UB], sc1[UB], bi1[UB];
+#pragma unroll
+  for (int i = 0; i < UB; ++i) {
+    const int u = min(ubase + i * UPW + sg, N - 1);
+    const int64_t wrow = static_cast<int64_t>(e) * N + u;
+    w0[i] = *reinterpret_cast<const uint4*>(q0 + wrow * words + 4 * kl);
+    sc0[i] = bf16_to_f32(s0[wrow * groups + gi]);
+    bi0[i] = bf16_to_f32(b0[wrow * groups + gi]);
+    if (PAIR) {
+      w1[i] = *reinterpret_cast<const uint4*>(q1 + wrow * words + 4 * kl);
+      sc1[i] = bf16_to_f32(s1[wrow * groups + gi]);
+      bi1[i] = bf16_to_f32(b1[wrow * groups + gi]);
     }
-    __syncthreads();
-    // K <= 32 * LPR (the launcher checks), so this runs once
-#pragma unroll 1
-    for (int kc = 0; kc < K; kc += 32 * LPR) {
-      const int kb = kc + 32 * kl;  // first element owned by this lane
-      const int gi = kb / G;
-#pragma unroll 1
-      for (int rp = 0; rp < nr; rp += kRowsPerPass) {
-        half2_t xp[kRowsPerPass][16];
-        float xsum[kRowsPerPass];
+  }
+
+  // the expert's rows, RP at a time: each lane reads its own 32 elements of
+  // a row straight from memory (the row index is uniform, so it comes in
+  // through the scalar cache)
+  for (int rp = 0; rp < cnt; rp += RP) {
+    {
+      half2_t xp[RP][16];
+      float xsum[RP];
 #pragma unroll
-        for (int r = 0; r < kRowsPerPass; ++r)
-          xsum[r] = (rp + r < nr)
-                        ? load_pairs<PAIR>(xs + static_cast<int64_t>(rp + r) * K + kb, xp[r])
-                        : 0.f;
-#pragma unroll 4
-        for (int ub = wave * UPW; ub < kUnitsPerBlock; ub += 4 * UPW) {
-          const int u = u_base + ub + sg;
-          const bool live = u < N;
-          const int uu = live ? u : N - 1;
-          const int64_t wrow = static_cast<int64_t>(e) * N + uu;
-          const uint4 w0 = *reinterpret_cast<const uint4*>(q0 + wrow * words + kb / 8);
-          uint4 w1 = make_uint4(0, 0, 0, 0);
-          if (PAIR) w1 = *reinterpret_cast<const uint4*>(q1 + wrow * words + kb / 8);
-          const float sc0 = bf16_to_f32(s0[wrow * groups + gi]);
-          const float bi0 = bf16_to_f32(b0[wrow * groups + gi]);
-          float sc1 = 0.f, bi1 = 0.f;
-          if (PAIR) {
-            sc1 = bf16_to_f32(s1[wrow * groups + gi]);
-            bi1 = bf16_to_f32(b1[wrow * groups + gi]);
+      for (int r = 0; r < RP; ++r) {
+        const int rr = min(rp + r, cnt - 1);
+        const int64_t src = sorted_token ? sorted_token[row0 + rr]
+                                         : static_cast<int64_t>(row0 + rr);
+        xsum[r] = load_pairs<PAIR>(a + src * K + 32 * kl, xp[r]);
+      }
+      // v[(i*RP + r)*M + m]
+      float v[V];
+#pragma unroll
+      for (int i = 0; i < UB; ++i) {
+        // one unit at a time: its codes are unpacked once for all rows
+        dots<RP>(w0[i], xp, &v[i * RP * M], M);
+        if (PAIR) dots<RP>(w1[i], xp, &v[i * RP * M + 1], M);
+#pragma unroll
+        for (int r = 0; r < RP; ++r) {
+          v[(i * RP + r) * M] = sc0[i] * (v[(i * RP + r) * M] - 1024.f * xsum[r]) +
+                                bi0[i] * xsum[r];
+          if (PAIR)
+            v[(i * RP + r) * M + 1] =
+                sc1[i] * (v[(i * RP + r) * M + 1] - 1024.f * xsum[r]) + bi1[i] * xsum[r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      multi_reduce<V, LPR>(v, lane);
+      // with several totals per lane, the gate and up of one (unit, row)
+      // sit side by side; with one, in the lanes one last-halving distance
+      // apart
+      constexpr int kPartner = last_halving_distance<V, LPR>();
+      // lanes below the last halving distance hold copies: the one with
+      // those bits clear writes
+      const bool writer = (lane & (kPartner - 1)) == 0;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        float g = v[j], upv = 0.f;
+        int idx = reduce_index<V, LPR>(lane, j);
+        if (PAIR) {
+          if (C > 1) {
+            if (j % 2 == 1) continue;
+            upv = v[j + 1];
+          } else {
+            upv = __shfl_xor(v[0], kPartner, 64);
+            if (idx % 2 == 1) continue;
           }
-          float acc0[kRowsPerPass], acc1[kRowsPerPass];
-#pragma unroll
-          for (int r = 0; r < kRowsPerPass; ++r) {
-            const float d0 = dot32(w0, xp[r]) - 1024.f * xsum[r];
-            acc0[r] = sc0 * d0 + bi0 * xsum[r];
-            if (PAIR) {
-              const float d1 = dot32(w1, xp[r]) - 1024.f * xsum[r];
-              acc1[r] = sc1 * d1 + bi1 * xsum[r];
-            }
-#pragma unroll
-            for (int o = LPR / 2; o > 0; o >>= 1) {
-              acc0[r] += __shfl_xor(acc0[r], o, 64);
-              if (PAIR) acc1[r] += __shfl_xor(acc1[r], o, 64);
-            }
-          }
-          if (kl == 0 && live) {
-#pragma unroll
-            for (int r = 0; r < kRowsPerPass; ++r) {
-              if (rp + r >= nr) break;
-              const int64_t o = static_cast<int64_t>(row0 + rc0 + rp + r) * N + u;
-              if (PAIR) {  // hidden activation, fp16 (saturating)
-                float h = acc0[r] / (1.f + __expf(-acc0[r])) * acc1[r];
-                h = fminf(fmaxf(h, -65504.f), 65504.f);
-                static_cast<_Float16*>(out)[o] = static_cast<_Float16>(h);
-              } else {  // expert output, fp32
-                static_cast<float*>(out)[o] = acc0[r];
-              }
-            }
-          }
+        }
+        const int unit_i = idx / (RP * M);
+        const int r = (idx / M) % RP;
+        if (!writer || rp + r >= cnt) continue;
+        const int u = ubase + unit_i * UPW + sg;
+        if (u >= N) continue;
+        const int64_t o = static_cast<int64_t>(row0 + rp + r) * N + u;
+        if (PAIR) {  // hidden activation, fp16 (saturating)
+          float h = g / (1.f + __expf(-g)) * upv;
+          h = fminf(fmaxf(h, -65504.f), 65504.f);
+          static_cast<_Float16*>(out)[o] = static_cast<_Float16>(h);
+        } else {  // expert output, fp32
+          static_cast<float*>(out)[o] = g;
         }
       }
     }
@@ -193,29 +290,38 @@ u4_kernel(const int32_t* __restrict__ offsets,
 }
 
 // lanes per unit: each lane owns 32 elements of K, so LPR = K/32 (K is a
-// multiple of 64 and at most 2048)
+// power of two from 64 to 2048)
 int pick_lpr(int K) {
   int l = 64;
   while (l > 1 && K % (32 * l) != 0) l >>= 1;
   return l;
 }
 
+constexpr int kUB = 4;  // wave-wide weight loads per matrix in flight
+
+template <bool PAIR, int LPR>
+int units_per_block() { return 4 * kUB * (64 / LPR); }
+
 template <bool PAIR>
-hipError_t launch_u4(int K, dim3 grid, size_t lds, hipStream_t s,
-                     const int32_t* offsets, const int32_t* st,
-                     const uint16_t* a, const uint32_t* q0, const uint16_t* s0,
-                     const uint16_t* b0, const uint32_t* q1, const uint16_t* s1,
-                     const uint16_t* b1, void* out, int N, int G) {
-#define MOE_U4(L)                                                              \
-  hipLaunchKernelGGL((u4_kernel<PAIR, L>), grid, dim3(256), lds, s, offsets,   \
-                     st, a, q0, s0, b0, q1, s1, b1, out, N, K, G)
+hipError_t launch_u4(int K, int E, int N, hipStream_t s, const int32_t* offsets,
+                     const int32_t* st, const uint16_t* a, const uint32_t* q0,
+                     const uint16_t* s0, const uint16_t* b0, const uint32_t* q1,
+                     const uint16_t* s1, const uint16_t* b1, void* out) {
+#define MOE_U4(L)                                                                  \
+  {                                                                                \
+    const int upb = 4 * kUB * (64 / L);                                            \
+    const dim3 grid(E, (N + upb - 1) / upb);                                       \
+    hipLaunchKernelGGL((u4_kernel<PAIR, L, kUB>), grid, dim3(256), 0, s, offsets,  \
+                       st, a, q0, s0, b0, q1, s1, b1, out, N);                     \
+    break;                                                                         \
+  }
   switch (pick_lpr(K)) {
-    case 64: MOE_U4(64); break;
-    case 32: MOE_U4(32); break;
-    case 16: MOE_U4(16); break;
-    case 8: MOE_U4(8); break;
-    case 4: MOE_U4(4); break;
-    default: MOE_U4(2); break;
+    case 64: MOE_U4(64)
+    case 32: MOE_U4(32)
+    case 16: MOE_U4(16)
+    case 8: MOE_U4(8)
+    case 4: MOE_U4(4)
+    default: MOE_U4(2)
   }
 #undef MOE_U4
   return hipGetLastError();
@@ -227,32 +333,19 @@ hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
                          const int32_t* sorted_token, const void* x,
                          const moe_expert_weights& w, void* H, void* Y,
                          hipStream_t s) {
-  if (D.d > kMaxK || D.F > kMaxK || !D.swiglu ||
+  if (D.d > kMaxK || D.F > kMaxK || !D.swiglu || group != 64 ||
       D.d != 32 * pick_lpr(D.d) || D.F != 32 * pick_lpr(D.F))
     return hipErrorInvalidValue;
-  {
-    const dim3 grid(D.E, (D.F + kUnitsPerBlock - 1) / kUnitsPerBlock);
-    const size_t lds = static_cast<size_t>(kRC) * D.d * 2;
-    hipError_t err = launch_u4<true>(
-        D.d, grid, lds, s, offsets, sorted_token,
-        static_cast<const uint16_t*>(x), static_cast<const uint32_t*>(w.gate),
-        static_cast<const uint16_t*>(w.gate_scale),
-        static_cast<const uint16_t*>(w.gate_bias),
-        static_cast<const uint32_t*>(w.up), static_cast<const uint16_t*>(w.up_scale),
-        static_cast<const uint16_t*>(w.up_bias), H, D.F,
-        group);
-    if (err != hipSuccess) return err;
-  }
-  {
-    const dim3 grid(D.E, (D.d + kUnitsPerBlock - 1) / kUnitsPerBlock);
-    const size_t lds = static_cast<size_t>(kRC) * D.F * 2;
-    return launch_u4<false>(
-        D.F, grid, lds, s, offsets, nullptr,
-        static_cast<const uint16_t*>(H), static_cast<const uint32_t*>(w.down),
-        static_cast<const uint16_t*>(w.down_scale),
-        static_cast<const uint16_t*>(w.down_bias), nullptr, nullptr, nullptr,
-        Y, D.d, group);
-  }
+  hipError_t err = launch_u4<true>(
+      D.d, D.E, D.F, s, offsets, sorted_token, static_cast<const uint16_t*>(x),
+      static_cast<const uint32_t*>(w.gate), static_cast<const uint16_t*>(w.gate_scale),
+      static_cast<const uint16_t*>(w.gate_bias), static_cast<const uint32_t*>(w.up),
+      static_cast<const uint16_t*>(w.up_scale), static_cast<const uint16_t*>(w.up_bias), H);
+  if (err != hipSuccess) return err;
+  return launch_u4<false>(
+      D.F, D.E, D.d, s, offsets, nullptr, static_cast<const uint16_t*>(H),
+      static_cast<const uint32_t*>(w.down), static_cast<const uint16_t*>(w.down_scale),
+      static_cast<const uint16_t*>(w.down_bias), nullptr, nullptr, nullptr, Y);
 }
 
 }  // namespace moe
