@@ -256,6 +256,52 @@ moe_status moe_layer_forward(const moe_spec* spec, int64_t T, const void* x,
                              const moe_layer_stats* stats, void* workspace,
                              size_t ws_bytes, moe_stream_t stream);
 
+/* Routing health of one layer call, from its dispatch counts (device
+ * struct, filled by moe_routing_health).  Definitions follow the "Mixture
+ * of Experts" blog page (second program's RoutingHealth, third program's
+ * routing_health and load_balancing_loss) with kept_e = offsets[e+1] -
+ * offsets[e], shares s_e = kept_e / T and P_e = prob_sum[e] / T:
+ *   aux        E * sum_e (kept_e / (T*k)) * P_e   (1 under uniform routing;
+ *              0 when prob_sum is NULL, e.g. SIGMOID_GROUP)
+ *   aux3       E * sum_e (kept_e / T) * P_e = k * aux (the pages' code)
+ *   entropy    -sum_e q_e log q_e over q_e = s_e / sum s (q_e > 0)
+ *   max_entropy log E;  entropy_ratio = entropy / max_entropy
+ *   max_share  max_e q_e;  collapsed = entropy_ratio < 0.5
+ *   dropped_fraction  dropped / (T*k)
+ *   load_peak_over_mean  max_e count_pre_e / mean_e count_pre_e (pre-drop)
+ * All zero-share cases give 0 (no division by zero). */
+typedef struct moe_health {
+  float aux;
+  float aux3;
+  float entropy;
+  float max_entropy;
+  float entropy_ratio;
+  float max_share;
+  float dropped_fraction;
+  float load_peak_over_mean;
+  int32_t collapsed;
+  int32_t kept_total;
+} moe_health;
+
+/* Routing health and the aux-loss-free bias update (dockyard
+ * "Mixture-of-Experts" page, "Aux-loss-free load balancing"; the blog page's
+ * routing health), one small kernel on the stream.
+ *   counts_pre [E], offsets [E+1], dropped [1]: int32, as written by
+ *     moe_dispatch / moe_layer_forward for the same spec and T;
+ *   prob_sum [E] fp32 or NULL (SOFTMAX_TOPK's sum of probabilities);
+ *   health: device moe_health (written);
+ *   bias [E] fp32 or NULL: when given, every expert's selection bias moves
+ *     by bias_step -- up when its pre-drop load is below the mean load,
+ *     down when above, unchanged when equal (the comparison is exact, in
+ *     integers); bias_step = 0 leaves it unchanged.
+ * Errors: the spec's; MOE_ERR_SHAPE for a missing counts_pre, offsets,
+ * dropped or health pointer.  T = 0 is a no-op. */
+moe_status moe_routing_health(const moe_spec* spec, int64_t T,
+                              const int32_t* counts_pre, const int32_t* offsets,
+                              const int32_t* dropped, const float* prob_sum,
+                              float* bias, float bias_step,
+                              moe_health* health, moe_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* moe_status_string(moe_status status);
 

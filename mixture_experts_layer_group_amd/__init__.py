@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_INVALID_TOPK"
                 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP", 7: "MOE_ERR_UNSUPPORTED"}
 EXPORTS = ("moe_spec_validate", "moe_capacity", "moe_workspace_size", "moe_route",
            "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-           "moe_status_string")
+           "moe_routing_health", "moe_status_string")
 
 
 class MoESpec(ctypes.Structure):
@@ -49,6 +49,17 @@ class MoEExpertWeights(ctypes.Structure):
 
 _S_FIELDS = ["topk_ids", "topk_w", "logits", "counts_pre", "offsets", "dropped",
              "prob_sum", "slot_row", "sorted_token"]
+
+
+class MoEHealth(ctypes.Structure):
+    """Device struct filled by moe_routing_health (allocate it as a 40-byte
+    tensor and read it back with ``health_from_bytes``)."""
+    _fields_ = [("aux", ctypes.c_float), ("aux3", ctypes.c_float),
+                ("entropy", ctypes.c_float), ("max_entropy", ctypes.c_float),
+                ("entropy_ratio", ctypes.c_float), ("max_share", ctypes.c_float),
+                ("dropped_fraction", ctypes.c_float),
+                ("load_peak_over_mean", ctypes.c_float),
+                ("collapsed", ctypes.c_int32), ("kept_total", ctypes.c_int32)]
 
 
 class MoELayerStats(ctypes.Structure):
@@ -90,6 +101,8 @@ def library() -> ctypes.CDLL:
         lib.moe_layer_forward.argtypes = [sp, i64, vp, vp, vp,
                                           ctypes.POINTER(MoEExpertWeights), vp,
                                           ctypes.POINTER(MoELayerStats), vp, sz, vp]
+        lib.moe_routing_health.argtypes = [sp, i64, vp, vp, vp, vp, vp, ctypes.c_float,
+                                           vp, vp]
         for n in EXPORTS[:-1]:
             getattr(lib, n).restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -240,6 +253,28 @@ def moe_layer_forward(spec, T, x, w_router, expert_bias, weights, out, stats=Non
                                        ctypes.byref(st) if st is not None else None,
                                        _ptr(workspace), ws_bytes, _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_routing_health(spec, T, counts_pre, offsets, dropped, prob_sum, health,
+                       bias=None, bias_step: float = 0.0, stream=None) -> None:
+    _check(library().moe_routing_health(ctypes.byref(spec), T, _ptr(counts_pre),
+                                        _ptr(offsets), _ptr(dropped), _ptr(prob_sum),
+                                        _ptr(bias), ctypes.c_float(bias_step),
+                                        _ptr(health), _stream(stream)),
+           "moe_routing_health")
+
+
+def health_buffer(device="cuda"):
+    """Device bytes for one moe_health struct."""
+    import torch
+    return torch.zeros(ctypes.sizeof(MoEHealth), dtype=torch.uint8, device=device)
+
+
+def health_from_bytes(buf) -> dict:
+    """The moe_health fields of a device buffer, as a dict (copies to host)."""
+    raw = bytes(buf.detach().to("cpu").numpy().tobytes())
+    h = MoEHealth.from_buffer_copy(raw[:ctypes.sizeof(MoEHealth)])
+    return {name: getattr(h, name) for name, _ in MoEHealth._fields_}
 
 
 def workspace(spec: MoESpec, T: int, device="cuda"):

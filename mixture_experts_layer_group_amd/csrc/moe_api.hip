@@ -406,6 +406,21 @@ moe_status moe_layer_forward(const moe_spec* spec, int64_t T, const void* x,
                                    out, s));
 }
 
+moe_status moe_routing_health(const moe_spec* spec, int64_t T,
+                              const int32_t* counts_pre, const int32_t* offsets,
+                              const int32_t* dropped, const float* prob_sum,
+                              float* bias, float bias_step,
+                              moe_health* health, moe_stream_t stream) {
+  moe_status st = validate(spec, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!counts_pre || !offsets || !dropped || !health) return MOE_ERR_SHAPE;
+  const Dims D = dims_of(*spec, T);
+  return hip_status(launch_routing_health(D, counts_pre, offsets, dropped, prob_sum,
+                                          bias, bias_step, health,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 const char* moe_status_string(moe_status status) {
   switch (status) {
     case MOE_OK: return "ok";

@@ -143,6 +143,12 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
                               const moe_expert_weights& w, void* Hs, void* Ys,
                               hipStream_t s);
 
+// stats.hip: routing health and the aux-loss-free bias update
+hipError_t launch_routing_health(const Dims& D, const int32_t* counts,
+                                 const int32_t* offsets, const int32_t* dropped,
+                                 const float* prob_sum, float* bias, float step,
+                                 moe_health* h, hipStream_t s);
+
 // combine.hip (expert outputs are fp32)
 // y_part (may be null): second K split of the expert rows, added to y_rows
 hipError_t launch_combine(const Dims& D, const void* y_rows, const float* y_part,

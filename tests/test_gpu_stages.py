@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from tests import gpu_util as gu
 
@@ -167,3 +168,62 @@ def test_determinism_bitwise():
     b = gu.run_layer(cfg, inp)
     for key in ("out", "topk_ids", "topk_w", "slot_row", "prob_sum"):
         assert torch.equal(a[key], b[key]), key
+
+
+def _health_case(cfg, inp, step):
+    import mixture_experts_layer_group_amd as moe
+    r = gu.run_layer(cfg, inp)
+    spec = moe.spec_from_config(cfg)
+    T, k, E = cfg.T, cfg.top_k, cfg.E
+    h = moe.health_buffer()
+    bias0 = torch.linspace(-0.1, 0.1, E, dtype=torch.float32, device="cuda")
+    bias = bias0.clone()
+    moe.moe_routing_health(spec, T, r["counts_pre"], r["offsets"], r["dropped"],
+                           r["prob_sum"], h, bias, step)
+    torch.cuda.synchronize()
+    got = moe.health_from_bytes(h)
+    counts = r["counts_pre"].cpu().numpy().astype(np.int64)
+    off = r["offsets"].cpu().numpy().astype(np.int64)
+    kept = np.diff(off)
+    dropped = int(r["dropped"].item())
+    P = (r["prob_sum"].cpu().numpy().astype(np.float64) / T
+         if r["prob_sum"] is not None else None)
+    ref = oracle.layer_stats(counts, kept, dropped, P, T, k, E)
+    gu.log(f"  health: {got}")
+    assert got["kept_total"] == int(kept.sum())
+    for key in ("entropy", "max_entropy", "entropy_ratio", "max_share",
+                "dropped_fraction", "load_peak_over_mean"):
+        assert abs(got[key] - ref[key]) <= 2e-6 * max(1.0, abs(ref[key])), key
+    if P is not None:
+        for key in ("aux", "aux3"):
+            assert abs(got[key] - ref[key]) <= 2e-6 * max(1.0, abs(ref[key])), key
+    else:
+        assert got["aux"] == 0.0 and got["aux3"] == 0.0
+    if abs(ref["entropy_ratio"] - 0.5) > 1e-5:
+        assert got["collapsed"] == int(ref["collapsed"])
+    ref_b = oracle.bias_update(bias0.cpu().numpy(), counts, step)
+    got_b = bias.cpu().numpy().astype(np.float64)
+    # one fp32 addition of +-step or 0
+    assert np.all(np.abs(got_b - ref_b) <= 1e-7 + 2.0 ** -24 * np.abs(ref_b))
+    return got, ref
+
+
+@pytest.mark.parametrize("name", ["swiglu-bf16-zipf-capacity", "sigmoid-group-shared",
+                                  "relu-bf16-capacity"])
+def test_routing_health_and_bias_update(name):
+    """moe_routing_health on a layer's own dispatch counts equals the
+    oracle's health fields (fp32 against fp64) and its bias update."""
+    cfg = MEDIUM[name]
+    _health_case(cfg, gu.make_inputs(cfg), 1e-3)
+
+
+def test_routing_health_collapsed_and_equal_loads():
+    """Zero router: every token picks experts 0 and 1, so the kept shares
+    are two equal halves (entropy log 2, ratio 1/3, collapsed); the other
+    six experts are below the mean load and move up, the two busy ones down."""
+    cfg = C("zero-router-health", 122, T=256, d=128, E=8, top_k=2, F=128)
+    inp = gu.make_inputs(cfg)
+    inp["w_router"].zero_()
+    got, ref = _health_case(cfg, inp, 0.25)
+    assert got["collapsed"] == 1 and abs(got["max_share"] - 0.5) < 1e-7
+    assert abs(got["entropy_ratio"] - 1.0 / 3.0) < 1e-6

@@ -24,7 +24,7 @@ def header_symbols():
 def test_library_exports_every_declared_symbol():
     lib = moe.library()
     syms = header_symbols()
-    assert len(syms) == 9
+    assert len(syms) == len(moe.EXPORTS) == 10
     for s in syms:
         assert hasattr(lib, s), s
     assert sorted(moe.EXPORTS) == syms
@@ -112,3 +112,18 @@ def test_errors_raise_before_any_launch():
         moe.moe_route(base(), 4, 16, 16, 32, 16, 16, workspace=16, ws_bytes=1 << 40,
                       stream=0)
     assert e.value.status == 1  # a selection bias with softmax routing
+
+
+def test_routing_health_errors_before_any_launch():
+    """moe_routing_health validates the spec and its required pointers on
+    the host; T = 0 is a no-op that touches nothing."""
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_routing_health(base(top_k=0), 4, 16, 16, 16, None, 16, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_routing_health(base(), 4, 0, 16, 16, None, 16, stream=0)
+    assert e.value.status == 4  # counts_pre missing
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_routing_health(base(), 4, 16, 16, 16, None, 0, stream=0)
+    assert e.value.status == 4  # health missing
+    moe.moe_routing_health(base(), 0, 0, 0, 0, None, 0, stream=0)
