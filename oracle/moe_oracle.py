@@ -215,6 +215,46 @@ def route_from_logits(L: np.ndarray, spec: Dict, expert_bias=None):
     return ids, w, None
 
 
+def route_forced(L: np.ndarray, forced_ids: np.ndarray, spec: Dict):
+    """Router replay, [dockyard] "Router replay (R3)": the expert ids of
+    every token are given (recorded at generation), and the gating weights
+    still come from the model's own gate on these logits:
+
+      * SOFTMAX_TOPK: p = softmax(L); w_i = p[id_i], divided by the given
+        ids' total probability when ``norm_topk_prob``;
+      * SIGMOID_GROUP: w_i = sigmoid(L)[id_i] (fp32 scores, no bias: the
+        bias only steers selection), divided by (their sum + 1e-20) when
+        ``norm_topk_prob``, then times ``routed_scaling``.
+
+    A row whose ids are not k distinct experts in [0, E) -- e.g. the
+    sentinel of a missing route -- is rejected instead of replayed: it gets
+    the identity route 0..k-1 with zero weights and is reported.
+
+    Returns (ids [T,k] int32, weights [T,k] fp64, rejected [T] bool).
+    """
+    T, E = L.shape
+    k = spec["top_k"]
+    f = np.asarray(forced_ids, dtype=np.int64).reshape(T, k)
+    in_range = np.all((f >= 0) & (f < E), axis=1)
+    distinct = np.array([len(set(row.tolist())) == k for row in f])
+    rejected = ~(in_range & distinct)
+    ids = np.where(rejected[:, None], np.arange(k)[None, :], f)
+    if spec["router"] == SOFTMAX_TOPK:
+        score = softmax(L)
+    else:
+        score = sigmoid_f32(L).astype(np.float64)
+    w = np.take_along_axis(score, ids, axis=-1)
+    if spec["router"] == SOFTMAX_TOPK:
+        if spec.get("norm_topk_prob", True):
+            w = w / w.sum(axis=-1, keepdims=True)
+    else:
+        if spec.get("norm_topk_prob", True):
+            w = w / (w.sum(axis=-1, keepdims=True) + 1e-20)
+        w = w * spec.get("routed_scaling", 1.0)
+    w[rejected] = 0.0
+    return ids.astype(np.int32), w, rejected
+
+
 def route(x, w_router, spec: Dict, expert_bias=None):
     """Router: fp64 logits, then ``route_from_logits``.  Returns (L, ids,
     weights, probabilities or None)."""

@@ -515,3 +515,57 @@ def test_zipf_skew_makes_hot_experts():
     counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
     assert counts[0] > 5 * counts.mean()
     assert counts[:8].mean() > counts[-32:].mean() * 4
+
+
+# ---------------------------------------------------------------- P15 replay
+@pytest.mark.parametrize("router", ["softmax", "sigmoid"])
+@pytest.mark.parametrize("norm", [True, False])
+def test_route_forced_replays_the_routers_own_choice(router, norm):
+    """Replaying the ids the router itself chose gives back its weights:
+    the forced path and the selection path share only the softmax/sigmoid,
+    not the ranking or the renormalisation code."""
+    rng = np.random.default_rng(17)
+    T, E, k = 40, 16, 4
+    L = rng.normal(size=(T, E)).astype(np.float32).astype(np.float64)
+    if router == "softmax":
+        spec = {"router": oracle.SOFTMAX_TOPK, "top_k": k, "norm_topk_prob": norm}
+        ids, w, _ = oracle.route_from_logits(L, spec)
+    else:
+        spec = {"router": oracle.SIGMOID_GROUP, "top_k": k, "norm_topk_prob": norm,
+                "n_group": 4, "topk_group": 2, "routed_scaling": 2.5}
+        bias = rng.uniform(-0.05, 0.05, size=E)
+        ids, w, _ = oracle.route_from_logits(L, spec, bias)
+    ids_f, w_f, rej = oracle.route_forced(L, ids, spec)
+    assert not rej.any()
+    assert np.array_equal(ids_f, ids)
+    np.testing.assert_allclose(w_f, w, rtol=1e-12, atol=0)
+
+
+def test_route_forced_weights_are_the_gate_at_the_given_ids():
+    """Any distinct ids, in any order: weights are p[id] renormalised over
+    the given set (softmax), or sigmoid(L)[id] (sigmoid, norm off) -- order
+    preserved, worked by hand on one row."""
+    L = np.array([[0.0, np.log(2.0), np.log(3.0), np.log(4.0)]])
+    spec = {"router": oracle.SOFTMAX_TOPK, "top_k": 2, "norm_topk_prob": True}
+    ids, w, rej = oracle.route_forced(L, np.array([[3, 0]]), spec)
+    assert ids.tolist() == [[3, 0]] and not rej[0]
+    np.testing.assert_allclose(w, [[4.0 / 5.0, 1.0 / 5.0]], rtol=1e-15)
+    spec["norm_topk_prob"] = False
+    _, w, _ = oracle.route_forced(L, np.array([[1, 2]]), spec)
+    np.testing.assert_allclose(w, [[2.0 / 10.0, 3.0 / 10.0]], rtol=1e-15)
+    sspec = {"router": oracle.SIGMOID_GROUP, "top_k": 2, "norm_topk_prob": False,
+             "n_group": 2, "topk_group": 1, "routed_scaling": 3.0}
+    _, w, _ = oracle.route_forced(np.zeros((1, 4)), np.array([[2, 1]]), sspec)
+    np.testing.assert_allclose(w, [[1.5, 1.5]], rtol=1e-15)  # 3 * sigmoid(0)
+
+
+@pytest.mark.parametrize("row", [[-1, 2], [2, 2], [0, 4], [7, -7]])
+def test_route_forced_rejects_sentinels_and_duplicates(row):
+    """A missing-route sentinel, a repeated id or an id outside [0, E) is
+    rejected: identity route, zero weights, reported."""
+    L = np.zeros((2, 4))
+    spec = {"router": oracle.SOFTMAX_TOPK, "top_k": 2, "norm_topk_prob": True}
+    ids, w, rej = oracle.route_forced(L, np.array([[1, 3], row]), spec)
+    assert rej.tolist() == [False, True]
+    assert ids[1].tolist() == [0, 1] and np.all(w[1] == 0.0)
+    np.testing.assert_allclose(w[0], [0.5, 0.5])
