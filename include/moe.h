@@ -179,6 +179,36 @@ moe_status moe_route(const moe_spec* spec, int64_t T, const void* x,
                      float* prob_sum, void* workspace, size_t ws_bytes,
                      moe_stream_t stream);
 
+/* Router replay (dockyard "Mixture-of-Experts" page, "Router replay (R3)"):
+ * the expert ids of each token are given -- recorded when the tokens were
+ * generated -- and only the gating weights come from the model's own gate
+ * on the same logits L = x @ Wr^T as moe_route:
+ *  SOFTMAX_TOPK: w_i = p[id_i] with p = softmax(L), divided by the given
+ *    ids' total probability when norm_topk_prob;
+ *  SIGMOID_GROUP: w_i = sigmoid(L)[id_i] (no bias, no group restriction:
+ *    both only steer a selection), divided by (their sum + 1e-20) when
+ *    norm_topk_prob, times routed_scaling.
+ * Forcing the ids moe_route chose for the same x reproduces its weights
+ * exactly.  A row that is not k distinct ids in [0,E) (a sentinel such as
+ * -1 for a route that was never recorded, a repeat, an out-of-range id) is
+ * rejected, not replayed: it gets the ids 0..k-1 with zero weights, so it
+ * passes through dispatch and combine and contributes nothing, and it is
+ * counted in *rejected.
+ *  forced_ids device [T,k] int32, any values
+ *  rejected   device out [1] int32, number of rejected rows
+ *  other arguments as moe_route (prob_sum: softmax p over every token,
+ *  rejected rows included)
+ * Errors: the spec's; MOE_ERR_SHAPE for a missing x, w_router, forced_ids,
+ * topk_ids, topk_w or rejected, or unaligned x / w_router;
+ * MOE_ERR_WORKSPACE for a missing or short workspace.  T = 0 is a no-op
+ * that writes nothing. */
+moe_status moe_route_forced(const moe_spec* spec, int64_t T, const void* x,
+                            const void* w_router, const int32_t* forced_ids,
+                            int32_t* topk_ids, float* topk_w, float* logits,
+                            float* prob_sum, int32_t* rejected,
+                            void* workspace, size_t ws_bytes,
+                            moe_stream_t stream);
+
 /* Dispatch with capacity, blog page first program's moe_layer (arrival
  * order) and third program's route_and_sort (stable sort by expert):
  * slots (t,i) are visited in token order; expert e keeps its first

@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_INVALID_TOPK"
                 3: "MOE_ERR_CAPACITY_TOO_TIGHT", 4: "MOE_ERR_SHAPE",
                 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP", 7: "MOE_ERR_UNSUPPORTED"}
 EXPORTS = ("moe_spec_validate", "moe_capacity", "moe_workspace_size", "moe_route",
-           "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
+           "moe_route_forced", "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
            "moe_routing_health", "moe_status_string")
 
 
@@ -92,6 +92,8 @@ def library() -> ctypes.CDLL:
         lib.moe_capacity.argtypes = [sp, i64, ctypes.POINTER(ctypes.c_int64)]
         lib.moe_workspace_size.argtypes = [sp, i64, ctypes.POINTER(ctypes.c_size_t)]
         lib.moe_route.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.moe_route_forced.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         sz, vp]
         lib.moe_dispatch.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, sz, vp]
         lib.moe_grouped_ffn.argtypes = [sp, i64, vp, vp, vp,
@@ -214,6 +216,17 @@ def moe_route(spec, T, x, w_router, expert_bias, topk_ids, topk_w, logits=None,
                                _ptr(expert_bias), _ptr(topk_ids), _ptr(topk_w),
                                _ptr(logits), _ptr(prob_sum), _ptr(workspace),
                                ws_bytes, _stream(stream)), "moe_route")
+
+
+def moe_route_forced(spec, T, x, w_router, forced_ids, topk_ids, topk_w, rejected,
+                     logits=None, prob_sum=None, workspace=None, ws_bytes=None,
+                     stream=None) -> None:
+    ws_bytes = ws_bytes if ws_bytes is not None else (workspace.numel() if workspace is not None else 0)
+    _check(library().moe_route_forced(ctypes.byref(spec), T, _ptr(x), _ptr(w_router),
+                                      _ptr(forced_ids), _ptr(topk_ids), _ptr(topk_w),
+                                      _ptr(logits), _ptr(prob_sum), _ptr(rejected),
+                                      _ptr(workspace), ws_bytes, _stream(stream)),
+           "moe_route_forced")
 
 
 def moe_dispatch(spec, T, topk_ids, topk_w, counts_pre, offsets, sorted_token,

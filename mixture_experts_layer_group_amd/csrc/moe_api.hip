@@ -185,6 +185,7 @@ moe_status check_weights(const moe_spec& sp, const moe_expert_weights* w) {
 // ------------------------------------------------------------ stage bodies
 moe_status do_route(const moe_spec& sp, const Dims& D, const WsLayout& L,
                     const void* x, const void* wr, const float* bias,
+                    const int32_t* forced, int32_t* rejected,
                     int32_t* ids, float* w, float* logits, float* prob_sum,
                     void* ws, hipStream_t s) {
   const RouterPlan rp = router_plan(D, sp.router_dtype);
@@ -204,8 +205,12 @@ moe_status do_route(const moe_spec& sp, const Dims& D, const WsLayout& L,
   if (e != hipSuccess) return MOE_ERR_HIP;
   const bool want_p = prob_sum != nullptr && sp.router == MOE_ROUTER_SOFTMAX_TOPK;
   float* part = want_p ? at<float>(ws, L.probpart) : nullptr;
-  e = launch_router_select(D, sp, Lg, rp.mfma ? rp.S : 1, Lout, bias, ids, w, part,
-                           L.route_blocks, s);
+  if (forced != nullptr) {
+    e = launch_zero_i32(rejected, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  e = launch_router_select(D, sp, Lg, rp.mfma ? rp.S : 1, Lout, bias, forced,
+                           rejected, ids, w, part, L.route_blocks, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (want_p) return hip_status(launch_prob_finalize(D, part, L.route_blocks, prob_sum, s));
   return MOE_OK;
@@ -287,8 +292,29 @@ moe_status moe_route(const moe_spec* spec, int64_t T, const void* x,
   const Dims D = dims_of(*spec, T);
   const WsLayout L = layout_of(D);
   if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  return do_route(*spec, D, L, x, w_router, expert_bias, topk_ids, topk_w,
+  return do_route(*spec, D, L, x, w_router, expert_bias, nullptr, nullptr,
+                  topk_ids, topk_w,
                   logits, prob_sum, workspace, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_route_forced(const moe_spec* spec, int64_t T, const void* x,
+                            const void* w_router, const int32_t* forced_ids,
+                            int32_t* topk_ids, float* topk_w, float* logits,
+                            float* prob_sum, int32_t* rejected,
+                            void* workspace, size_t ws_bytes,
+                            moe_stream_t stream) {
+  moe_status st = validate(spec, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !forced_ids || !topk_ids || !topk_w || !rejected ||
+      !aligned16(x) || !aligned16(w_router))
+    return MOE_ERR_SHAPE;
+  const Dims D = dims_of(*spec, T);
+  const WsLayout L = layout_of(D);
+  if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return do_route(*spec, D, L, x, w_router, nullptr, forced_ids, rejected,
+                  topk_ids, topk_w, logits, prob_sum, workspace,
+                  static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_dispatch(const moe_spec* spec, int64_t T,
@@ -386,7 +412,8 @@ moe_status moe_layer_forward(const moe_spec* spec, int64_t T, const void* x,
   int32_t* sorted_token = o.sorted_token ? o.sorted_token : at<int32_t>(ws, L.sorted_token);
   float* sorted_w = at<float>(ws, L.sorted_w);
 
-  st = do_route(*spec, D, L, x, w_router, expert_bias, ids, tw, o.logits,
+  st = do_route(*spec, D, L, x, w_router, expert_bias, nullptr, nullptr, ids,
+                tw, o.logits,
                 o.prob_sum, ws, s);
   if (st != MOE_OK) return st;
   const bool mfma_path = D.bf16 && !D.u4;

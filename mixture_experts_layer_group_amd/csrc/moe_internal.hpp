@@ -96,8 +96,11 @@ hipError_t launch_router_logits(const Dims& D, int act_dtype, int router_dtype,
 // logits_out (may be null) receives the summed logits
 hipError_t launch_router_select(const Dims& D, const moe_spec& sp,
                                 const float* logits, int S, float* logits_out,
-                                const float* bias, int32_t* ids, float* w,
+                                const float* bias, const int32_t* forced,
+                                int32_t* rejected, int32_t* ids, float* w,
                                 float* probpart, int nblocks, hipStream_t s);
+// *p = 0 by a one-thread kernel
+hipError_t launch_zero_i32(int32_t* p, hipStream_t s);
 // router_mfma.hip: partial logits of plan p into part ([p.S][T][E]); w3
 // holds 3*E*d bf16 when p.npass == 3
 hipError_t launch_router_mfma(const Dims& D, const RouterPlan& p, const void* x,

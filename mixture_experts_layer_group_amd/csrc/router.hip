@@ -243,7 +243,8 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
 template <int EPL>
 __global__ void __launch_bounds__(256)
 select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
-              const float* __restrict__ bias,
+              const float* __restrict__ bias, const int32_t* __restrict__ forced,
+              int32_t* __restrict__ rejected,
               int32_t* __restrict__ ids, float* __restrict__ wout,
               float* __restrict__ probpart, int64_t T, int E, int k,
               int router, int norm, float scaling, int n_group,
@@ -294,7 +295,7 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
         v[j] = sc[j] + ((bias != nullptr && e < E) ? bias[e] : 0.f);
         if (e < E) sel_lds[wv][e] = v[j];
       }
-      if (topk_group < n_group) {
+      if (topk_group < n_group && forced == nullptr) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -334,7 +335,28 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
     // top-k by repeated wave argmax; lane r keeps the r-th winner
     int my_id = 0;
     float my_val = 0.f;
-    for (int r = 0; r < k; ++r) {
+    bool reject = false;
+    if (forced != nullptr) {
+      // router replay: lane r takes the r-th given id; a row that is not k
+      // distinct experts in [0, E) is rejected (identity route, weight 0)
+      const int fid = lane < k ? forced[t * k + lane] : 0;
+      bool bad = lane < k && (fid < 0 || fid >= E);
+      for (int j = 0; j < k; ++j) {
+        const int o = __shfl(fid, j, kWave);
+        if (lane < k && j < lane && o == fid) bad = true;
+      }
+      reject = __ballot(bad) != 0;
+      my_id = reject ? lane : fid;
+      if (lane >= k) my_id = 0;
+      // the given expert's logit, fetched from the lane that holds it
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) {
+        const float y = __shfl(v[j], my_id % kWave, kWave);
+        if (my_id / kWave == j) my_val = y;
+      }
+      if (reject && lane == 0) atomicAdd(rejected, 1);
+    }
+    for (int r = 0; r < k && forced == nullptr; ++r) {
       float bv = 0.f;
       int bi = INT_MAX;
 #pragma unroll
@@ -354,7 +376,18 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
     }
     float wk;
     if (router == MOE_ROUTER_SOFTMAX_TOPK) {
-      const float m = __shfl(my_val, 0, kWave);  // the largest logit
+      // the largest logit: the first choice, or for given ids the maximum
+      // over all experts (the same value whenever the first choice is given)
+      float m = __shfl(my_val, 0, kWave);
+      if (forced != nullptr) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < EPL; ++j)
+          if (lane + kWave * j < E) mx = fmaxf(mx, v[j]);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+        m = mx;
+      }
       float S = 0.f;
       if (want_p || !norm) {
         float part = 0.f;
@@ -387,7 +420,7 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
     }
     if (lane < k) {
       ids[t * k + lane] = my_id;
-      wout[t * k + lane] = wk;
+      wout[t * k + lane] = reject ? 0.f : wk;
     }
   }
   if (want_p) {
@@ -410,6 +443,9 @@ __global__ void prob_finalize_kernel(const float* __restrict__ part, int nb,
   for (int b = 0; b < nb; ++b) s += part[static_cast<int64_t>(b) * E + e];
   out[e] = s;
 }
+
+// one counter cleared by a kernel (safe inside a captured graph)
+__global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
 
 template <typename XT, typename WT>
 hipError_t logits_dispatch(const Dims& D, const void* x, const void* wr,
@@ -449,16 +485,23 @@ hipError_t launch_router_logits(const Dims& D, int act_dtype, int router_dtype,
   return logits_dispatch<float, float>(D, x, wr, logits, s);
 }
 
+hipError_t launch_zero_i32(int32_t* p, hipStream_t s) {
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(1), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_router_select(const Dims& D, const moe_spec& sp,
                                 const float* logits, int S, float* logits_out,
-                                const float* bias, int32_t* ids, float* w,
+                                const float* bias, const int32_t* forced,
+                                int32_t* rejected, int32_t* ids, float* w,
                                 float* probpart, int nblocks, hipStream_t s) {
   const int epl = (D.E + kWave - 1) / kWave;
   const float scaling =
       sp.router == MOE_ROUTER_SIGMOID_GROUP ? sp.routed_scaling : 1.0f;
 #define MOE_SELECT(N)                                                        \
   hipLaunchKernelGGL((select_kernel<N>), dim3(nblocks), dim3(256), 0, s,     \
-                     logits, S, logits_out, bias, ids, w, probpart, D.T, D.E,  \
+                     logits, S, logits_out, bias, forced, rejected, ids, w,     \
+                     probpart, D.T, D.E,                                        \
                      D.k, sp.router,                                            \
                      sp.norm_topk_prob, scaling, sp.n_group, sp.topk_group)
   if (epl <= 1) MOE_SELECT(1);

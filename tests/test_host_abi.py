@@ -24,7 +24,7 @@ def header_symbols():
 def test_library_exports_every_declared_symbol():
     lib = moe.library()
     syms = header_symbols()
-    assert len(syms) == len(moe.EXPORTS) == 10
+    assert len(syms) == len(moe.EXPORTS) == 11
     for s in syms:
         assert hasattr(lib, s), s
     assert sorted(moe.EXPORTS) == syms
@@ -127,3 +127,21 @@ def test_routing_health_errors_before_any_launch():
         moe.moe_routing_health(base(), 4, 16, 16, 16, None, 0, stream=0)
     assert e.value.status == 4  # health missing
     moe.moe_routing_health(base(), 0, 0, 0, 0, None, 0, stream=0)
+
+
+def test_route_forced_errors_before_any_launch():
+    """moe_route_forced validates the spec and its required pointers on the
+    host; T = 0 is a no-op."""
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_route_forced(base(top_k=0), 4, 16, 16, 16, 16, 16, 16, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_route_forced(base(), 4, 16, 16, 0, 16, 16, 16, stream=0)
+    assert e.value.status == 4  # forced ids missing
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_route_forced(base(), 4, 16, 16, 16, 16, 16, 0, stream=0)
+    assert e.value.status == 4  # rejected counter missing
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_route_forced(base(), 4, 16, 16, 16, 16, 16, 16, stream=0)
+    assert e.value.status == 5  # no workspace
+    moe.moe_route_forced(base(), 0, 0, 0, 0, 0, 0, 0, stream=0)
