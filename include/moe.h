@@ -50,6 +50,11 @@ enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU = 1 };
 /* Storage types.  U4_AFFINE: Edge0 page, QuantSpec (bits 4, group 64,
  * mode affine). */
 enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_U4_AFFINE = 2 };
+/* Expert weight layouts, Edge0 page, WeightLayout: SEPARATE stacks gate,
+ * up and down one tensor each; FUSED_GATE_UP stacks each expert's gate
+ * rows directly above its up rows in one tensor (twice the out rows, the
+ * two slices interleaved expert by expert), down separate. */
+enum { MOE_LAYOUT_SEPARATE = 0, MOE_LAYOUT_FUSED_GATE_UP = 1 };
 
 /* Everything the math depends on; the subset of the Edge0 page's MoESpec
  * (and the blog page's MoEConfig) that changes results. */
@@ -74,11 +79,12 @@ typedef struct moe_spec {
   int32_t quant_group;     /* U4_AFFINE group size along K (64) */
   int32_t out_dtype;       /* F32 or BF16: the layer output (the combine
                               accumulates in fp32 either way) */
+  int32_t layout;          /* MOE_LAYOUT_*: how gate and up are stored */
 } moe_spec;
 
-/* Expert weights, device pointers, the Edge0 page's SEPARATE layout: one
- * stacked tensor per projection with the expert on axis 0, each matrix
- * [out, in] row-major (K contiguous), applied as x @ W^T.
+/* Expert weights, device pointers.  SEPARATE layout (Edge0 page,
+ * WeightLayout): one stacked tensor per projection with the expert on axis
+ * 0, each matrix [out, in] row-major (K contiguous), applied as x @ W^T.
  *   gate : [E, F, d]  (SwiGLU gate; the ReLU expert's input matrix)
  *   up   : [E, F, d]  (SwiGLU only; NULL for ReLU)
  *   down : [E, d, F]  (the output matrix for both activations)
@@ -87,7 +93,13 @@ typedef struct moe_spec {
  * first) and *_scale / *_bias hold bf16 [E, N, K/quant_group]; the weight
  * is scale*q + bias.
  * Shared experts (act dtype, never quantised): shared_gate [S, Fs, d],
- * shared_up [S, Fs, d] (SwiGLU), shared_down [S, d, Fs]. */
+ * shared_up [S, Fs, d] (SwiGLU), shared_down [S, d, Fs].
+ * FUSED_GATE_UP layout (SwiGLU only): gate points to the fused tensor
+ * [E, 2F, d] whose expert e holds its F gate rows followed by its F up rows
+ * (for U4_AFFINE: codes [E, 2F, d/8], gate_scale / gate_bias
+ * [E, 2F, d/quant_group]), shared_gate to [S, 2Fs, d] likewise; up,
+ * up_scale, up_bias and shared_up must be NULL (MOE_ERR_INVALID_ARG
+ * otherwise).  The kernels read the fused tensor in place. */
 typedef struct moe_expert_weights {
   const void* gate;
   const void* up;
@@ -135,7 +147,8 @@ typedef void* moe_stream_t;
  *     E/n_group < 2 (a group's top-two is undefined), topk_group outside
  *     [1, n_group], or k > topk_group*E/n_group; shared experts with
  *     shared_ffn < 1; U4_AFFINE with quant_group != 64 or d, F not
- *     multiples of it; BF16 activations with F32 routed weights
+ *     multiples of it; BF16 activations with F32 routed weights;
+ *     layout not a MOE_LAYOUT_* value; FUSED_GATE_UP with ReLU
  *   MOE_ERR_SHAPE               T < 0 or T*max(k,1) above 2^31 - 1
  *   MOE_ERR_UNSUPPORTED         F32 activations with non-F32 weights;
  *     d not a multiple of 8; BF16 activations whose d, F or shared_ffn is

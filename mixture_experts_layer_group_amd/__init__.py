@@ -19,6 +19,7 @@ MOE_OK = 0
 ROUTER = {"softmax_topk": 0, "sigmoid_group": 1}
 ACT = {"swiglu": 0, "relu": 1}
 DTYPE = {"f32": 0, "bf16": 1, "u4": 2}
+LAYOUT = {"separate": 0, "fused_gate_up": 1}
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_INVALID_TOPK",
                 3: "MOE_ERR_CAPACITY_TOO_TIGHT", 4: "MOE_ERR_SHAPE",
                 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP", 7: "MOE_ERR_UNSUPPORTED"}
@@ -36,7 +37,8 @@ class MoESpec(ctypes.Structure):
                 ("shared_experts", ctypes.c_int32), ("shared_ffn", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("router_dtype", ctypes.c_int32),
-                ("quant_group", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("quant_group", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 _W_FIELDS = ["gate", "up", "down", "gate_scale", "gate_bias", "up_scale", "up_bias",
@@ -124,12 +126,12 @@ def make_spec(E: int, top_k: int, d: int, F: int, router: str = "softmax_topk",
               shared_experts: int = 0, shared_F: int = 0, act: str = "swiglu",
               act_dtype: str = "bf16", weight_dtype: str = "bf16",
               router_dtype: str = "f32", quant_group: int = 64,
-              out_dtype: str = "f32") -> MoESpec:
+              out_dtype: str = "f32", layout: str = "separate") -> MoESpec:
     return MoESpec(E, top_k, d, F, ROUTER[router], int(bool(norm_topk_prob)),
                    float(routed_scaling), n_group, topk_group, float(capacity_factor),
                    shared_experts, shared_F, ACT[act], DTYPE[act_dtype],
                    DTYPE[weight_dtype], DTYPE[router_dtype], quant_group,
-                   DTYPE[out_dtype])
+                   DTYPE[out_dtype], LAYOUT[layout])
 
 
 def spec_from_config(cfg) -> MoESpec:
@@ -139,7 +141,8 @@ def spec_from_config(cfg) -> MoESpec:
                      cfg.routed_scaling, cfg.n_group, cfg.topk_group,
                      cfg.capacity_factor, cfg.shared_experts, cfg.shared_F, cfg.act,
                      cfg.act_dtype, cfg.weight_dtype, cfg.router_dtype,
-                     cfg.quant_group, getattr(cfg, "out_dtype", "f32"))
+                     cfg.quant_group, getattr(cfg, "out_dtype", "f32"),
+                     getattr(cfg, "layout", "separate"))
 
 
 # ---------------------------------------------------------------- helpers
@@ -166,8 +169,12 @@ def _check(status: int, where: str) -> None:
 def expert_weights(w: Dict) -> MoEExpertWeights:
     """``moe_expert_weights`` from a dict of tensors keyed like the C struct
     (gate/up/down, *_scale/*_bias for 4-bit, shared_*).  Also accepts the
-    keys w_gate/w_up/w_down, q_*/s_*/b_* and sh_*."""
-    alias = {"w_gate": "gate", "w_up": "up", "w_down": "down", "q_gate": "gate",
+    keys w_gate/w_up/w_down, q_*/s_*/b_* and sh_*, and for the fused
+    gate/up layout w_gate_up, q_gate_up/s_gate_up/b_gate_up and sh_gate_up
+    (passed in the gate fields)."""
+    alias = {"w_gate_up": "gate", "q_gate_up": "gate", "s_gate_up": "gate_scale",
+             "b_gate_up": "gate_bias", "sh_gate_up": "shared_gate",
+             "w_gate": "gate", "w_up": "up", "w_down": "down", "q_gate": "gate",
              "q_up": "up", "q_down": "down", "s_gate": "gate_scale",
              "b_gate": "gate_bias", "s_up": "up_scale", "b_up": "up_bias",
              "s_down": "down_scale", "b_down": "down_bias", "sh_gate": "shared_gate",

@@ -86,8 +86,10 @@ struct GemmArgs {
   const int32_t* tiles;         // [E+1] group M-tile prefix (nullptr: one group)
   int E;
   int32_t single_rows;          // rows of the single group
-  const uint16_t* w0;           // gate / in / down  [E][N][K]
-  const uint16_t* w1;           // up (SwiGLU)
+  const uint16_t* w0;           // gate / in / down of expert 0, [N][K]
+  const uint16_t* w1;           // up (SwiGLU) of expert 0
+  int64_t wstride;              // elements from one expert's matrix to the
+                                // next (N*K; 2*N*K for fused gate/up)
   int N;                        // weight rows per expert
   int K;                        // reduction length (row length of a and w)
   void* out;                    // [rows][ldo]: bf16 H (up), fp32 Y (down)
@@ -210,8 +212,8 @@ grouped_gemm_kernel(GemmArgs g) {
   // output rows that are never stored).
   const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(g.a), (short)0, static_cast<int>(g.a_bytes), 0x00020000);
-  const uint16_t* wbase0 = g.w0 + static_cast<int64_t>(e) * g.N * K;
-  const uint16_t* wbase1 = (MODE == kSwiGLU ? g.w1 : g.w0) + static_cast<int64_t>(e) * g.N * K;
+  const uint16_t* wbase0 = g.w0 + static_cast<int64_t>(e) * g.wstride;
+  const uint16_t* wbase1 = (MODE == kSwiGLU ? g.w1 : g.w0) + static_cast<int64_t>(e) * g.wstride;
   const __amdgpu_buffer_rsrc_t rsW0 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(wbase0), (short)0, -1, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsW1 = __builtin_amdgcn_make_buffer_rsrc(
@@ -510,15 +512,22 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
                               hipStream_t s) {
   const int up_mode = D.swiglu ? kSwiGLU : kReLU;
   const int64_t mt = (D.T + BM - 1) / BM;
+  const int64_t mat = static_cast<int64_t>(D.Fs) * D.d;  // one [Fs][d] matrix
   for (int sh = 0; sh < D.S; ++sh) {
-    const int64_t wo = static_cast<int64_t>(sh) * D.Fs * D.d;
+    const int64_t wo = static_cast<int64_t>(sh) * mat;
     GemmArgs g{};
     g.a = static_cast<const uint16_t*>(x);
     g.a_bytes = static_cast<uint32_t>(D.T * D.d * 2);
     g.E = 1;
     g.single_rows = static_cast<int32_t>(D.T);
-    g.w0 = static_cast<const uint16_t*>(w.shared_gate) + wo;
-    g.w1 = D.swiglu ? static_cast<const uint16_t*>(w.shared_up) + wo : nullptr;
+    if (D.fused) {  // [S][2Fs][d]: gate rows, then up rows
+      g.w0 = static_cast<const uint16_t*>(w.shared_gate) + 2 * wo;
+      g.w1 = g.w0 + mat;
+    } else {
+      g.w0 = static_cast<const uint16_t*>(w.shared_gate) + wo;
+      g.w1 = D.swiglu ? static_cast<const uint16_t*>(w.shared_up) + wo : nullptr;
+    }
+    g.wstride = 0;  // a single expert
     g.N = D.Fs;
     g.K = D.d;
     g.out = Hs;
@@ -533,6 +542,7 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
     h.E = 1;
     h.single_rows = static_cast<int32_t>(D.T);
     h.w0 = static_cast<const uint16_t*>(w.shared_down) + wo;
+    h.wstride = 0;
     h.N = D.d;
     h.K = D.Fs;
     h.out = static_cast<float*>(Ys) + static_cast<int64_t>(sh) * D.T * D.d;
@@ -561,8 +571,15 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
     g.offsets = offsets;
     g.tiles = tiles1;
     g.E = D.E;
+    const int64_t mat = static_cast<int64_t>(D.F) * D.d;  // one [F][d] matrix
     g.w0 = static_cast<const uint16_t*>(w.gate);
-    g.w1 = D.swiglu ? static_cast<const uint16_t*>(w.up) : nullptr;
+    if (D.fused) {  // [E][2F][d]: each expert's gate rows, then its up rows
+      g.w1 = g.w0 + mat;
+      g.wstride = 2 * mat;
+    } else {
+      g.w1 = D.swiglu ? static_cast<const uint16_t*>(w.up) : nullptr;
+      g.wstride = mat;
+    }
     g.N = D.F;
     g.K = D.d;
     g.out = H;
@@ -580,6 +597,7 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
     g.tiles = tiles2;
     g.E = D.E;
     g.w0 = static_cast<const uint16_t*>(w.down);
+    g.wstride = static_cast<int64_t>(D.d) * D.F;
     g.N = D.d;
     g.K = D.F;
     g.out = Y;

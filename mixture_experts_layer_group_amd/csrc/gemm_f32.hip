@@ -33,8 +33,9 @@ __global__ void __launch_bounds__(256)
 f32_up_kernel(const int32_t* __restrict__ offsets, int E,
               const int32_t* __restrict__ sorted_token,
               const float* __restrict__ x, const float* __restrict__ wa,
-              const float* __restrict__ wb, float* __restrict__ H,
-              int64_t rows_max, int d, int F, int swiglu, int identity) {
+              const float* __restrict__ wb, int64_t wstride,
+              float* __restrict__ H, int64_t rows_max, int d, int F, int swiglu,
+              int identity) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = identity ? rows_max : offsets[E];
   if (idx >= total * F) return;
@@ -43,7 +44,8 @@ f32_up_kernel(const int32_t* __restrict__ offsets, int E,
   const int e = identity ? 0 : find_group(offsets, E, static_cast<int32_t>(r));
   const int64_t tok = identity ? r : sorted_token[r];
   const float* xr = x + tok * d;
-  const int64_t wrow = (static_cast<int64_t>(e) * F + n) * d;
+  // wstride: elements from one expert's matrix to the next
+  const int64_t wrow = static_cast<int64_t>(e) * wstride + static_cast<int64_t>(n) * d;
   const float a = dot(xr, wa + wrow, d);
   float h;
   if (swiglu) {
@@ -77,12 +79,15 @@ hipError_t launch_ffn_f32(const Dims& D, const int32_t* offsets,
                           const moe_expert_weights& w, void* H, void* Hs,
                           void* Y, void* Ys, hipStream_t s) {
   const float* xf = static_cast<const float*>(x);
+  // FUSED_GATE_UP: each expert's [F][d] gate rows, then its up rows
+  const int64_t mat = static_cast<int64_t>(D.F) * D.d;
+  const float* wg = static_cast<const float*>(w.gate);
+  const float* wu = D.fused ? wg + mat : static_cast<const float*>(w.up);
   {
     const int64_t n = D.slots * D.F;
     hipLaunchKernelGGL(f32_up_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
-                       dim3(256), 0, s, offsets, D.E, sorted_token, xf,
-                       static_cast<const float*>(w.gate),
-                       static_cast<const float*>(w.up), static_cast<float*>(H),
+                       dim3(256), 0, s, offsets, D.E, sorted_token, xf, wg, wu,
+                       D.fused ? 2 * mat : mat, static_cast<float*>(H),
                        D.slots, D.d, D.F, D.swiglu ? 1 : 0, 0);
     const int64_t m = D.slots * D.d;
     hipLaunchKernelGGL(f32_down_kernel, dim3(static_cast<unsigned>((m + 255) / 256)),
@@ -92,12 +97,16 @@ hipError_t launch_ffn_f32(const Dims& D, const int32_t* offsets,
   }
   for (int sh = 0; sh < D.S; ++sh) {
     const int64_t n = D.T * D.Fs;
-    const int64_t so = static_cast<int64_t>(sh) * D.Fs * D.d;
+    const int64_t smat = static_cast<int64_t>(D.Fs) * D.d;
+    const int64_t so = static_cast<int64_t>(sh) * smat;
+    const float* sg = static_cast<const float*>(w.shared_gate) + (D.fused ? 2 * so : so);
+    const float* su = D.fused ? sg + smat
+                              : (D.swiglu ? static_cast<const float*>(w.shared_up) + so
+                                          : nullptr);
     hipLaunchKernelGGL(f32_up_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
-                       dim3(256), 0, s, offsets, 1, sorted_token, xf,
-                       static_cast<const float*>(w.shared_gate) + so,
-                       D.swiglu ? static_cast<const float*>(w.shared_up) + so : nullptr,
-                       static_cast<float*>(Hs), D.T, D.d, D.Fs, D.swiglu ? 1 : 0, 1);
+                       dim3(256), 0, s, offsets, 1, sorted_token, xf, sg, su,
+                       int64_t{0}, static_cast<float*>(Hs), D.T, D.d, D.Fs,
+                       D.swiglu ? 1 : 0, 1);
     const int64_t m = D.T * D.d;
     hipLaunchKernelGGL(f32_down_kernel, dim3(static_cast<unsigned>((m + 255) / 256)),
                        dim3(256), 0, s, offsets, 1, static_cast<const float*>(Hs),

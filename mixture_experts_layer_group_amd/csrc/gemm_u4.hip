@@ -182,7 +182,7 @@ u4_kernel(const int32_t* __restrict__ offsets,
           const uint32_t* __restrict__ q1,            // up (PAIR)
           const uint16_t* __restrict__ s1,
           const uint16_t* __restrict__ b1,
-          void* __restrict__ out, int N) {
+          void* __restrict__ out, int N, int rstride) {
   constexpr int K = 32 * LPR;
   constexpr int UPW = 64 / LPR;     // units per wave-wide load
   constexpr int UPWB = UB * UPW;    // units per wave
@@ -208,7 +208,9 @@ u4_kernel(const int32_t* __restrict__ offsets,
 #pragma unroll
   for (int i = 0; i < UB; ++i) {
     const int u = min(ubase + i * UPW + sg, N - 1);
-    const int64_t wrow = static_cast<int64_t>(e) * N + u;
+    // rstride: rows from one expert's matrix to the next (N; 2N when gate
+    // and up are fused)
+    const int64_t wrow = static_cast<int64_t>(e) * rstride + u;
     w0[i] = *reinterpret_cast<const uint4*>(q0 + wrow * words + 4 * kl);
     sc0[i] = bf16_to_f32(s0[wrow * groups + gi]);
     bi0[i] = bf16_to_f32(b0[wrow * groups + gi]);
@@ -303,7 +305,8 @@ template <bool PAIR, int LPR>
 int units_per_block() { return 4 * kUB * (64 / LPR); }
 
 template <bool PAIR>
-hipError_t launch_u4(int K, int E, int N, hipStream_t s, const int32_t* offsets,
+hipError_t launch_u4(int K, int E, int N, int rstride, hipStream_t s,
+                     const int32_t* offsets,
                      const int32_t* st, const uint16_t* a, const uint32_t* q0,
                      const uint16_t* s0, const uint16_t* b0, const uint32_t* q1,
                      const uint16_t* s1, const uint16_t* b1, void* out) {
@@ -312,7 +315,7 @@ hipError_t launch_u4(int K, int E, int N, hipStream_t s, const int32_t* offsets,
     const int upb = 4 * kUB * (64 / L);                                            \
     const dim3 grid(E, (N + upb - 1) / upb);                                       \
     hipLaunchKernelGGL((u4_kernel<PAIR, L, kUB>), grid, dim3(256), 0, s, offsets,  \
-                       st, a, q0, s0, b0, q1, s1, b1, out, N);                     \
+                       st, a, q0, s0, b0, q1, s1, b1, out, N, rstride);            \
     break;                                                                         \
   }
   switch (pick_lpr(K)) {
@@ -336,14 +339,23 @@ hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
   if (D.d > kMaxK || D.F > kMaxK || !D.swiglu || group != 64 ||
       D.d != 32 * pick_lpr(D.d) || D.F != 32 * pick_lpr(D.F))
     return hipErrorInvalidValue;
-  hipError_t err = launch_u4<true>(
-      D.d, D.E, D.F, s, offsets, sorted_token, static_cast<const uint16_t*>(x),
-      static_cast<const uint32_t*>(w.gate), static_cast<const uint16_t*>(w.gate_scale),
-      static_cast<const uint16_t*>(w.gate_bias), static_cast<const uint32_t*>(w.up),
-      static_cast<const uint16_t*>(w.up_scale), static_cast<const uint16_t*>(w.up_bias), H);
+  const uint32_t* qg = static_cast<const uint32_t*>(w.gate);
+  const uint16_t* sg = static_cast<const uint16_t*>(w.gate_scale);
+  const uint16_t* bg = static_cast<const uint16_t*>(w.gate_bias);
+  const uint32_t* qu = static_cast<const uint32_t*>(w.up);
+  const uint16_t* su = static_cast<const uint16_t*>(w.up_scale);
+  const uint16_t* bu = static_cast<const uint16_t*>(w.up_bias);
+  if (D.fused) {  // each expert's F gate rows, then its F up rows
+    qu = qg + static_cast<int64_t>(D.F) * (D.d / 8);
+    su = sg + static_cast<int64_t>(D.F) * (D.d / group);
+    bu = bg + static_cast<int64_t>(D.F) * (D.d / group);
+  }
+  hipError_t err = launch_u4<true>(D.d, D.E, D.F, D.fused ? 2 * D.F : D.F, s, offsets,
+                                   sorted_token, static_cast<const uint16_t*>(x), qg,
+                                   sg, bg, qu, su, bu, H);
   if (err != hipSuccess) return err;
   return launch_u4<false>(
-      D.F, D.E, D.d, s, offsets, nullptr, static_cast<const uint16_t*>(H),
+      D.F, D.E, D.d, D.d, s, offsets, nullptr, static_cast<const uint16_t*>(H),
       static_cast<const uint32_t*>(w.down), static_cast<const uint16_t*>(w.down_scale),
       static_cast<const uint16_t*>(w.down_bias), nullptr, nullptr, nullptr, Y);
 }

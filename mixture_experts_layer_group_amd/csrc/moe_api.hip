@@ -42,6 +42,12 @@ moe_status validate(const moe_spec* sp, int64_t T) {
     return MOE_ERR_INVALID_ARG;
   if (s.out_dtype != MOE_DTYPE_F32 && s.out_dtype != MOE_DTYPE_BF16)
     return MOE_ERR_INVALID_ARG;
+  // Edge0 "MoE Spec and Routing" page, WeightLayout: the fused layout
+  // stacks gate above up, so it needs the gated activation
+  if (s.layout != MOE_LAYOUT_SEPARATE && s.layout != MOE_LAYOUT_FUSED_GATE_UP)
+    return MOE_ERR_INVALID_ARG;
+  if (s.layout == MOE_LAYOUT_FUSED_GATE_UP && s.act != MOE_ACT_SWIGLU)
+    return MOE_ERR_INVALID_ARG;
   // Edge0 "MoE Spec and Routing" page: group-limited routing needs groups
   // of at least two experts (each group scores its top two)
   if (s.router == MOE_ROUTER_SIGMOID_GROUP) {
@@ -113,6 +119,7 @@ Dims dims_of(const moe_spec& s, int64_t T) {
   D.bf16 = s.act_dtype == MOE_DTYPE_BF16;
   D.u4 = s.weight_dtype == MOE_DTYPE_U4_AFFINE;
   D.swiglu = s.act == MOE_ACT_SWIGLU;
+  D.fused = s.layout == MOE_LAYOUT_FUSED_GATE_UP;
   D.out_bf16 = s.out_dtype == MOE_DTYPE_BF16;
   D.router_dtype = s.router_dtype;
   return D;
@@ -165,6 +172,19 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 moe_status check_weights(const moe_spec& sp, const moe_expert_weights* w) {
   if (w == nullptr || !w->gate || !w->down) return MOE_ERR_SHAPE;
+  const bool fused = sp.layout == MOE_LAYOUT_FUSED_GATE_UP;
+  if (fused) {
+    // the up rows live inside the fused gate tensor
+    if (w->up || w->up_scale || w->up_bias || w->shared_up) return MOE_ERR_INVALID_ARG;
+    if (sp.weight_dtype == MOE_DTYPE_U4_AFFINE &&
+        (!w->gate_scale || !w->gate_bias || !w->down_scale || !w->down_bias))
+      return MOE_ERR_SHAPE;
+    if (sp.shared_experts > 0 &&
+        (!w->shared_gate || !w->shared_down || !aligned16(w->shared_gate) ||
+         !aligned16(w->shared_down)))
+      return MOE_ERR_SHAPE;
+    return aligned16(w->gate) && aligned16(w->down) ? MOE_OK : MOE_ERR_SHAPE;
+  }
   if (sp.act == MOE_ACT_SWIGLU && !w->up) return MOE_ERR_SHAPE;
   if (!aligned16(w->gate) || !aligned16(w->down) || (w->up && !aligned16(w->up)))
     return MOE_ERR_SHAPE;

@@ -44,6 +44,7 @@ struct Dims {
   bool bf16;          // bf16 activations
   bool u4;            // 4-bit routed weights
   bool swiglu;
+  bool fused;         // FUSED_GATE_UP: gate holds [E][2F][d], gate rows first
   bool out_bf16;      // layer output in bf16 (else fp32)
   int router_dtype;   // MOE_DTYPE_* of the router weights
 };

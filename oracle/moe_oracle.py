@@ -380,19 +380,34 @@ class ExpertBank:
     w_gate/w_up/w_down/sh_gate/sh_up/sh_down a [N, K] array (float32, or
     uint16 bf16 bits), and for 4-bit weights q_* (uint32 packed), s_*, b_*
     (uint16 bf16 bits).
+
+    ``fused``: the gate and up projections are stored together, [dockyard
+    MoE Spec and Routing] "Weight layout" (FUSED_GATE_UP) and "Bundle layout
+    and the up-first order": one [2F, K] slice per expert under w_gate_up
+    (q_/s_/b_gate_up for 4-bit, sh_gate_up for shared experts) whose first F
+    rows are the gate and the last F the up projection, so that splitting
+    x @ W^T in two halves gives (gate, up).
     """
 
     def __init__(self, fetch: Callable[[str, int], np.ndarray], act: str,
-                 u4: bool = False, group: int = 64):
+                 u4: bool = False, group: int = 64, fused: bool = False):
         self.fetch = fetch
         self.act = act
         self.u4 = u4
         self.group = group
+        self.fused = fused
 
     @classmethod
     def from_arrays(cls, arrays: Dict[str, np.ndarray], act: str,
-                    u4: bool = False, group: int = 64) -> "ExpertBank":
-        return cls(lambda name, e: arrays[name][e], act, u4, group)
+                    u4: bool = False, group: int = 64,
+                    fused: bool = False) -> "ExpertBank":
+        return cls(lambda name, e: arrays[name][e], act, u4, group, fused)
+
+    @staticmethod
+    def split_gate_up(w: np.ndarray):
+        """(gate, up) of one fused [2F, K] slice: gate rows on top."""
+        F = w.shape[0] // 2
+        return w[:F], w[F:]
 
     def _mat(self, name: str, e: int) -> np.ndarray:
         if self.u4 and not name.startswith("sh_"):
@@ -403,13 +418,19 @@ class ExpertBank:
         return as_f64(self.fetch(name, e))
 
     def routed(self, e: int):
-        a = self._mat("w_gate", e)
-        b = self._mat("w_up", e) if self.act == SWIGLU else None
+        if self.fused:
+            a, b = self.split_gate_up(self._mat("w_gate_up", e))
+        else:
+            a = self._mat("w_gate", e)
+            b = self._mat("w_up", e) if self.act == SWIGLU else None
         return a, b, self._mat("w_down", e)
 
     def shared(self, s: int):
-        a = as_f64(self.fetch("sh_gate", s))
-        b = as_f64(self.fetch("sh_up", s)) if self.act == SWIGLU else None
+        if self.fused:
+            a, b = self.split_gate_up(as_f64(self.fetch("sh_gate_up", s)))
+        else:
+            a = as_f64(self.fetch("sh_gate", s))
+            b = as_f64(self.fetch("sh_up", s)) if self.act == SWIGLU else None
         return a, b, as_f64(self.fetch("sh_down", s))
 
 

@@ -40,6 +40,8 @@ RELU = "relu"
 F32 = "f32"
 BF16 = "bf16"
 U4 = "u4"
+SEPARATE = "separate"
+FUSED_GATE_UP = "fused_gate_up"
 
 # tensor ids used in the seed sequence
 TID_X, TID_WR, TID_BIAS, TID_GATE, TID_UP, TID_DOWN = 0, 1, 2, 3, 4, 5
@@ -72,6 +74,7 @@ class LayerConfig:
     router_dtype: str = F32
     quant_group: int = 64
     out_dtype: str = F32  # layer output (fp32 accumulation result by default)
+    layout: str = "separate"  # or FUSED_GATE_UP: gate rows above up rows
     # generation recipe only
     bias_range: float = 0.0  # U(-r, r) selection bias (sigmoid-group)
     zipf_s: float = 0.0  # > 0: fold a Zipf popularity prior into router rows
@@ -230,6 +233,24 @@ def make_layer_inputs(cfg: LayerConfig, device="cpu", base: int = SEED_BASE,
         out["sh_up"] = (_stacked(c, TID_SH_UP, S, Fs, c.d, sdt, device, base)
                         if c.act == SWIGLU else None)
         out["sh_down"] = _stacked(c, TID_SH_DOWN, S, c.d, Fs, sdt, device, base)
+    if c.layout == FUSED_GATE_UP:
+        out = fuse_gate_up(out)
+    return out
+
+
+def fuse_gate_up(inp: Dict[str, Optional[torch.Tensor]]) -> Dict[str, Optional[torch.Tensor]]:
+    """The same weights in the fused gate/up storage: for every pair
+    (w_gate, w_up), (q_gate, q_up), (s_gate, s_up), (b_gate, b_up) and
+    (sh_gate, sh_up) of [E, F, K] stacks, one [E, 2F, K] stack under
+    <prefix>_gate_up holding each expert's gate rows followed by its up
+    rows; the separate keys are dropped."""
+    out = dict(inp)
+    for pre in ("w", "q", "s", "b", "sh"):
+        g, u = out.pop(pre + "_gate", None), out.pop(pre + "_up", None)
+        if g is None:
+            continue
+        assert u is not None and u.shape == g.shape
+        out[pre + "_gate_up"] = torch.cat([g, u], dim=1)
     return out
 
 

@@ -90,7 +90,8 @@ def bank_for(cfg, inp) -> oracle.ExpertBank:
         return cache[key]
 
     return oracle.ExpertBank(fetch, cfg.act, u4=cfg.weight_dtype == synth.U4,
-                             group=cfg.quant_group)
+                             group=cfg.quant_group,
+                             fused=cfg.layout == synth.FUSED_GATE_UP)
 
 
 def logits_bound(x_h, wr_h, d):

@@ -145,3 +145,30 @@ def test_route_forced_errors_before_any_launch():
         moe.moe_route_forced(base(), 4, 16, 16, 16, 16, 16, 16, stream=0)
     assert e.value.status == 5  # no workspace
     moe.moe_route_forced(base(), 0, 0, 0, 0, 0, 0, 0, stream=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"layout": "fused_gate_up"}, 0),
+    ({"layout": "fused_gate_up", "act": "relu"}, 1),
+    ({"layout": "fused_gate_up", "weight_dtype": "u4", "d": 256, "F": 128}, 0),
+])
+def test_layout_validation(kw, status):
+    assert moe.moe_spec_validate(base(**kw), 16) == status
+    bad = base(**kw)
+    bad.layout = 2
+    assert moe.moe_spec_validate(bad, 16) == 1
+
+
+def test_fused_layout_rejects_separate_up_pointers():
+    """FUSED_GATE_UP carries the up rows inside the gate tensor: a non-NULL
+    up pointer is an error, found before any launch."""
+    spec = base(layout="fused_gate_up")
+    args = (spec, 4, 16, 16, 16)
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_grouped_ffn(*args, {"gate": 16, "up": 16, "down": 16}, 16, None,
+                            workspace=16, ws_bytes=1 << 40, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_grouped_ffn(*args, {"gate": 16, "down": 16}, 16, None,
+                            workspace=16, ws_bytes=16, stream=0)
+    assert e.value.status == 5  # weights accepted; the workspace is short

@@ -569,3 +569,72 @@ def test_route_forced_rejects_sentinels_and_duplicates(row):
     assert rej.tolist() == [False, True]
     assert ids[1].tolist() == [0, 1] and np.all(w[1] == 0.0)
     np.testing.assert_allclose(w[0], [0.5, 0.5])
+
+
+# ---------------------------------------------------------------- P16 fused gate/up
+def test_fused_gate_up_split_gives_gate_then_up():
+    """[edge0] "Weight layout" and "Bundle layout": in the fused tensor each
+    expert's gate rows sit above its up rows, so one product with the fused
+    matrix, split in two halves along the output, is (gate, up); the slices
+    are interleaved expert by expert, and a wholesale concatenation of the
+    two stacks would pair the wrong rows."""
+    r = rng(71)
+    E, F, d = 3, 5, 4
+    g = r.normal(size=(E, F, d))
+    u = r.normal(size=(E, F, d))
+    fused = np.concatenate([g, u], axis=1)          # [E, 2F, d], per expert
+    x = r.normal(size=(6, d))
+    for e in range(E):
+        xg, xu = np.split(x @ fused[e].T, 2, axis=-1)
+        assert np.allclose(xg, x @ g[e].T, rtol=1e-13, atol=1e-13)
+        assert np.allclose(xu, x @ u[e].T, rtol=1e-13, atol=1e-13)
+        a, b = oracle.ExpertBank.split_gate_up(fused[e])
+        assert np.array_equal(a, g[e]) and np.array_equal(b, u[e])
+    wholesale = np.concatenate([g.reshape(E * F, d), u.reshape(E * F, d)]).reshape(E, 2 * F, d)
+    a, b = oracle.ExpertBank.split_gate_up(wholesale[1])
+    assert not np.array_equal(a, g[1]) and not np.array_equal(b, u[1])
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_fused_bank_layer_equals_separate(seed):
+    """The layer over a fused gate/up bank (routed and shared experts) is the
+    layer over the separate bank, bit for bit; a wholesale-concatenated
+    tensor changes the output."""
+    x, wr, arrays, spec, bank = _tiny_layer(seed, act="swiglu", shared=1)
+    fused = {"w_gate_up": np.concatenate([arrays["w_gate"], arrays["w_up"]], axis=1),
+             "w_down": arrays["w_down"],
+             "sh_gate_up": np.concatenate([arrays["sh_gate"], arrays["sh_up"]], axis=1),
+             "sh_down": arrays["sh_down"]}
+    a = oracle.layer(x, wr, bank, spec)
+    b = oracle.layer(x, wr, oracle.ExpertBank.from_arrays(fused, "swiglu", fused=True), spec)
+    assert np.array_equal(a["out"], b["out"])
+    E, F, d = arrays["w_gate"].shape
+    bad = dict(fused)
+    bad["w_gate_up"] = np.concatenate([arrays["w_gate"].reshape(E * F, d),
+                                       arrays["w_up"].reshape(E * F, d)]).reshape(E, 2 * F, d)
+    c = oracle.layer(x, wr, oracle.ExpertBank.from_arrays(bad, "swiglu", fused=True), spec)
+    assert not np.allclose(a["out"], c["out"])
+
+
+def test_fused_u4_inputs_decode_to_the_separate_experts():
+    """4-bit codes, scales and biases in the fused storage (synth's fusing of
+    the seeded separate tensors) decode, through the fused bank, to exactly
+    the separate bank's gate and up matrices."""
+    base = synth.LayerConfig("u4-fused-pin", 77, T=4, d=128, E=3, top_k=2, F=64,
+                             weight_dtype=synth.U4, shared_experts=1, shared_F=64)
+    sep = synth.make_layer_inputs(base)
+    fus = synth.make_layer_inputs(base.replace(layout=synth.FUSED_GATE_UP))
+    assert fus["q_gate_up"].shape == (3, 128, 16) and fus["s_gate_up"].shape == (3, 128, 2)
+    assert "q_up" not in fus and "sh_up" not in fus
+
+    def bank(inp, fused):
+        arrays = {k: synth.host_array(v) for k, v in inp.items()
+                  if v is not None and k not in ("x", "w_router", "expert_bias")}
+        return oracle.ExpertBank.from_arrays(arrays, "swiglu", u4=True, fused=fused)
+
+    bs, bf = bank(sep, False), bank(fus, True)
+    for e in range(3):
+        for m1, m2 in zip(bs.routed(e), bf.routed(e)):
+            assert np.array_equal(m1, m2)
+    for m1, m2 in zip(bs.shared(0), bf.shared(0)):
+        assert np.array_equal(m1, m2)
