@@ -183,38 +183,50 @@ logits_small_e_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
     }
 }
 
-// Few tokens (decode): one wave per (expert row, 8 tokens), lanes split K,
-// 4 tokens at a time; the expert's router row is read once per 4 tokens
-// (then cached).
+// Few tokens (decode): one wave per (expert row, 4 tokens), lanes split K.
+// The loads of up to 4 K steps of 512 (the expert's router row and the 4
+// token rows) are all issued before any product, so a row of up to 2048
+// elements costs one memory round trip.
 template <typename XT, typename WT>
 __global__ void __launch_bounds__(256)
 logits_rowdot_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
                      float* __restrict__ L, int64_t T, int E, int d) {
+  constexpr int KC = 4;
   const int lane = threadIdx.x % kWave;
   const int e = blockIdx.x * 4 + threadIdx.x / kWave;
   if (e >= E) return;
   const WT* wrow = wr + static_cast<int64_t>(e) * d;
-  const int64_t tb = static_cast<int64_t>(blockIdx.y) * 8;
-  for (int64_t t0 = tb; t0 < T && t0 < tb + 8; t0 += 4) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int k = lane * 8; k < d; k += kWave * 8) {
-      float wv[8];
-      ld8(wrow, k, wv);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * 4;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = lane * 8; k0 < d; k0 += kWave * 8 * KC) {
+    float wv[KC][8];
+    float xv[KC][4][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (t0 + i < T) {
-          float xv[8];
-          ld8(x, (t0 + i) * d + k, xv);
+    for (int c = 0; c < KC; ++c) {
+      const int k = k0 + c * kWave * 8;
+      if (k < d) {
+        ld8(wrow, k, wv[c]);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i] = fmaf(xv[j], wv[j], acc[i]);
-        }
+        for (int i = 0; i < 4; ++i)
+          if (t0 + i < T) ld8(x, (t0 + i) * d + k, xv[c][i]);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s = wave_sum(acc[i]);
-      if (lane == 0 && t0 + i < T) L[(t0 + i) * E + e] = s;
+    for (int c = 0; c < KC; ++c) {
+      if (k0 + c * kWave * 8 < d) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + i < T) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i] = fmaf(xv[c][i][j], wv[c][j], acc[i]);
+          }
+      }
     }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float s = wave_sum(acc[i]);
+    if (lane == 0 && t0 + i < T) L[(t0 + i) * E + e] = s;
   }
 }
 
@@ -225,18 +237,34 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-// Wave-wide best (value, index) among candidates; lanes without one pass
-// index INT_MAX.
-__device__ __forceinline__ void wave_best(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float v2 = __shfl_xor(v, o, kWave);
-    const int i2 = __shfl_xor(i, o, kWave);
-    if (i2 != INT_MAX && (i == INT_MAX || better(v2, i2, v, i))) {
-      v = v2;
-      i = i2;
-    }
+// the better of two candidates; index INT_MAX marks no candidate
+__device__ __forceinline__ void take_better(float& v, int& i, float v2, int i2) {
+  if (i2 != INT_MAX && (i == INT_MAX || better(v2, i2, v, i))) {
+    v = v2;
+    i = i2;
   }
+}
+
+template <int CTRL>
+__device__ __forceinline__ void best_step(float& v, int& i) {
+  take_better(v, i, dpp_f<CTRL>(v), dpp_i<CTRL>(i));
+}
+
+// Wave-wide best (value, index) among candidates, the same in every lane;
+// lanes without one pass index INT_MAX.  Rows of 16 lanes first (DPP), then
+// the four row winners.
+__device__ __forceinline__ void wave_best(float& v, int& i) {
+  best_step<kDppXor1>(v, i);
+  best_step<kDppXor2>(v, i);
+  best_step<kDppHalfMirror>(v, i);
+  best_step<kDppMirror>(v, i);
+  float bv = lane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r)
+    take_better(bv, bi, lane_f(v, 16 * r), __builtin_amdgcn_readlane(i, 16 * r));
+  v = bv;
+  i = bi;
 }
 
 // One wave per token; EPL = experts per lane (expert lane + 64*j).
@@ -342,7 +370,7 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
       const int fid = lane < k ? forced[t * k + lane] : 0;
       bool bad = lane < k && (fid < 0 || fid >= E);
       for (int j = 0; j < k; ++j) {
-        const int o = __shfl(fid, j, kWave);
+        const int o = __builtin_amdgcn_readlane(fid, j);
         if (lane < k && j < lane && o == fid) bad = true;
       }
       reject = __ballot(bad) != 0;
@@ -378,15 +406,13 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
     if (router == MOE_ROUTER_SOFTMAX_TOPK) {
       // the largest logit: the first choice, or for given ids the maximum
       // over all experts (the same value whenever the first choice is given)
-      float m = __shfl(my_val, 0, kWave);
+      float m = lane_f(my_val, 0);
       if (forced != nullptr) {
         float mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < EPL; ++j)
           if (lane + kWave * j < E) mx = fmaxf(mx, v[j]);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-        m = mx;
+        m = wave_max(mx);
       }
       float S = 0.f;
       if (want_p || !norm) {
@@ -453,7 +479,7 @@ hipError_t logits_dispatch(const Dims& D, const void* x, const void* wr,
   const XT* xp = static_cast<const XT*>(x);
   const WT* wp = static_cast<const WT*>(wr);
   if (D.T <= 64 && (D.d % 8) == 0) {
-    dim3 grid((D.E + 3) / 4, static_cast<unsigned>((D.T + 7) / 8));
+    dim3 grid((D.E + 3) / 4, static_cast<unsigned>((D.T + 3) / 4));
     hipLaunchKernelGGL((logits_rowdot_kernel<XT, WT>), grid, dim3(256), 0, s,
                        xp, wp, L, D.T, D.E, D.d);
   } else if (D.E <= 16 && (D.d % 8) == 0) {

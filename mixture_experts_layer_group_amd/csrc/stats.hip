@@ -29,8 +29,7 @@ __device__ float block_sum(float v, float* red) {
   return s;
 }
 __device__ float block_max(float v, float* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  v = wave_max(v);
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   __syncthreads();
   if (lane == 0) red[w] = v;
