@@ -31,11 +31,41 @@ constexpr int kMaxK = 2048;  // one pass of 64 lanes x 32 elements per row
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
+// The value of this lane's partner at distance D (a power of two up to 32):
+// partners differ in bit D of the lane index and possibly in lower bits.
+// D <= 8 are DPP moves inside rows of 16 lanes (the two xor pairings of a
+// quad, then the mirrors of 8 and 16 lanes), 16 and 32 the gfx950 row
+// swaps; none goes through LDS.
+template <int D>
+__device__ __forceinline__ float pair_move(float v, int lane) {
+  if constexpr (D == 1) {
+    return dpp_f<kDppXor1>(v);
+  } else if constexpr (D == 2) {
+    return dpp_f<kDppXor2>(v);
+  } else if constexpr (D == 4) {
+    return dpp_f<kDppHalfMirror>(v);
+  } else if constexpr (D == 8) {
+    return dpp_f<kDppMirror>(v);
+  } else if constexpr (D == 16) {
+    // odd rows of the first result hold the even rows, and the other way
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(D == 32, "distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
 // In-place reduction of V per-lane values over each group of LPR lanes
 // (LPR and V powers of two).  Butterfly with halving: at distance D the
 // lane with bit D set keeps the upper half of its values and sends the
 // lower half, so each exchange carries half of the values and V values cost
-// about V shuffles in all instead of V*log2(LPR).  On return a lane holds
+// about V moves in all instead of V*log2(LPR).  Any partner that differs in
+// bit D (and possibly lower bits) holds the same index subset at that step,
+// so the pair_move pairings serve as well as xor.  On return a lane holds
 // C = max(1, V/LPR) totals in v[0..C): those of indices
 // reduce_index(lane, j), identical on lanes that differ only below the
 // last halving distance.
@@ -49,11 +79,11 @@ __device__ __forceinline__ void reduce_step(float (&v)[V], int lane) {
       for (int i = 0; i < kHalf; ++i) {
         const float send = upper ? v[i] : v[i + kHalf];
         const float keep = upper ? v[i + kHalf] : v[i];
-        v[i] = keep + __shfl_xor(send, D, 64);
+        v[i] = keep + pair_move<D>(send, lane);
       }
       reduce_step<D / 2, kHalf, V>(v, lane);
     } else {
-      v[0] += __shfl_xor(v[0], D, 64);
+      v[0] += pair_move<D>(v[0], lane);
       reduce_step<D / 2, 1, V>(v, lane);
     }
   }
@@ -526,7 +556,7 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
           if (j % 2 == 1) continue;
           upv = v[j + 1];
         } else {
-          upv = __shfl_xor(v[0], kPartner, 64);
+          upv = pair_move<kPartner>(v[0], lane);
           if (idx % 2 == 1) continue;
         }
       }
