@@ -33,6 +33,14 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
 
 
+def u4_expert_bytes(cfg) -> int:
+    """Bytes of one routed expert's 4-bit weights: packed codes (half a byte
+    per weight) plus a bf16 scale and bias per 64 weights of a row, for the
+    gate, up and down matrices (1,769,472 B at d=2048, F=512)."""
+    per_matrix = cfg.d * cfg.F // 2 + 2 * 2 * cfg.d * cfg.F // cfg.quant_group
+    return 3 * per_matrix
+
+
 def expert_flops(cfg, n_kept: int) -> float:
     """Algorithmic FLOPs of the expert FFN: 2*d*F per matrix per row (3
     matrices for SwiGLU, 2 for ReLU), routed kept rows plus shared experts
@@ -45,15 +53,18 @@ def expert_flops(cfg, n_kept: int) -> float:
 
 
 # sources of the kernels one grouped-FFN call runs (tile prefix, both expert
-# GEMMs, the fold of a split down projection): a traffic summary measured on
-# other sources is stale
-TRAFFIC_SOURCES = ("csrc/gemm_bf16.hip", "csrc/dispatch.hip", "csrc/combine.hip")
+# GEMMs, the fold of a split down projection; the two 4-bit kernels): a
+# traffic summary measured on other sources is stale
+TRAFFIC_SOURCES = {"bf16": ("csrc/gemm_bf16.hip", "csrc/dispatch.hip", "csrc/combine.hip"),
+                   "u4": ("csrc/gemm_u4.hip",)}
 COPY_BYTES = 1 << 30  # calibration kernel: reads and writes 1 GiB
+# counters are collected for the calibration copy and the FFN kernels only
+TRAFFIC_REGEX = "neg_kernel|grouped_gemm|tile_prefix|fold_split|u4s_kernel"
 
 
-def sources_digest() -> str:
+def sources_digest(weight_dtype: str = "bf16") -> str:
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in TRAFFIC_SOURCES["u4" if weight_dtype == "u4" else "bf16"]:
         with open(os.path.join(ROOT, "mixture_experts_layer_group_amd", rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -63,7 +74,7 @@ def traffic_summary_path(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"grouped_ffn_{workload}_hbm_traffic.md")
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, weight_dtype: str = "bf16"):
     """HBM bytes per grouped-FFN call from the committed counter summary, or
     None when there is none or it was taken on other kernel sources."""
     path = traffic_summary_path(workload)
@@ -75,7 +86,7 @@ def measured_traffic(workload: str):
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].strip().split(": ", 1)
                 vals[k.strip("`")] = v.strip().strip("`")
-    if vals.get("sources_sha256") != sources_digest():
+    if vals.get("sources_sha256") != sources_digest(weight_dtype):
         return None
     try:
         return float(vals["bytes_per_call"])
@@ -159,33 +170,45 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     cfg = synth.CONFIGS[args.config]
-    inp = synth.make_layer_inputs(cfg, "cuda")
+    u4 = cfg.weight_dtype == "u4"
+    # the 4-bit decode layer touches ~290 MB of weights, about the size of
+    # the 256 MB last-level cache: its timed steps rotate through three
+    # independently drawn copies of the inputs (1.4 GB) so no step finds the
+    # previous step's weights cached; larger layers exceed the cache anyway
+    n_rep = 3 if u4 else 1
+    reps = [synth.make_layer_inputs(cfg, "cuda", base=synth.SEED_BASE + r)
+            for r in range(n_rep)]
+    inp = reps[0]
     spec = moe.spec_from_config(cfg)
     T = cfg.T
     odt = torch.bfloat16 if cfg.out_dtype == "bf16" else torch.float32
     out = torch.empty((T, cfg.d), dtype=odt, device="cuda")
     ws = moe.workspace(spec, T)
-    w = moe.expert_weights(inp)
+    ws_all = [moe.expert_weights(r) for r in reps]
+    w = ws_all[0]
     dev = "cuda"
-    offsets = torch.empty(cfg.E + 1, dtype=torch.int32, device=dev)
-    sorted_token = torch.empty(T * cfg.top_k, dtype=torch.int32, device=dev)
-    stats = moe.layer_stats(offsets=offsets, sorted_token=sorted_token)
+    offs_all = [torch.empty(cfg.E + 1, dtype=torch.int32, device=dev) for _ in reps]
+    st_all = [torch.empty(T * cfg.top_k, dtype=torch.int32, device=dev) for _ in reps]
+    stats_all = [moe.layer_stats(offsets=o, sorted_token=t) for o, t in zip(offs_all, st_all)]
+    offsets, sorted_token = offs_all[0], st_all[0]
 
-    def step():
-        moe.moe_layer_forward(spec, T, inp["x"], inp["w_router"], inp["expert_bias"],
-                              w, out, stats=stats, workspace=ws)
+    def step(i=0):
+        r = i % n_rep
+        moe.moe_layer_forward(spec, T, reps[r]["x"], reps[r]["w_router"],
+                              reps[r]["expert_bias"], ws_all[r], out, stats=stats_all[r],
+                              workspace=ws)
 
     if args.traffic_probe:
         return traffic_probe(torch, moe, spec, cfg, inp, w, offsets, sorted_token, ws, step)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(max(args.warmup, n_rep)):
+        step(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -193,23 +216,32 @@ def main() -> int:
     tokens_per_s = T / (ms_step / 1e3)
 
     # the grouped expert FFN alone (both GEMMs), each call timed with HIP
-    # events on the stream the kernels run on
-    n_kept = int(offsets[-1].item())
+    # events on the stream the kernels run on (rotating copies as above)
+    kept = [int(o[-1].item()) for o in offs_all]
+    touched = [int((o[1:] - o[:-1] > 0).sum().item()) for o in offs_all]
+    n_kept = kept[0]
     y = torch.empty((T * cfg.top_k, cfg.d), dtype=torch.float32, device=dev)
     ysh = (torch.empty((cfg.shared_experts * T, cfg.d), dtype=torch.float32, device=dev)
            if cfg.shared_experts else None)
-    for _ in range(2):
-        moe.moe_grouped_ffn(spec, T, offsets, sorted_token, inp["x"], w, y, ysh, ws)
+
+    def ffn(i):
+        r = i % n_rep
+        moe.moe_grouped_ffn(spec, T, offs_all[r], st_all[r], reps[r]["x"], ws_all[r], y, ysh,
+                            ws)
+
+    for i in range(max(2, n_rep)):
+        ffn(i)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    for a, b in evs:
+    for i, (a, b) in enumerate(evs):
         a.record()
-        moe.moe_grouped_ffn(spec, T, offsets, sorted_token, inp["x"], w, y, ysh, ws)
+        ffn(i)
         b.record()
     torch.cuda.synchronize()
-    ffn_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-    flops = expert_flops(cfg, n_kept)
+    ffn_times = [a.elapsed_time(b) for a, b in evs]
+    ffn_ms = sum(ffn_times) / len(ffn_times)
+    flops = sum(expert_flops(cfg, kept[i % n_rep]) for i in range(args.steps)) / args.steps
     tflops = flops / (ffn_ms / 1e3) / 1e12
 
     res = {
@@ -240,6 +272,26 @@ def main() -> int:
                      "frac": tflops / PEAK_BF16_TFLOPS, "flops_per_launch": flops,
                      "avg_launch_ms": ffn_ms, "traffic": measured_traffic(cfg.name)},
     }
+    if u4:
+        # bound by HBM: the touched experts' packed weights, the token rows
+        # read and the fp32 expert rows written, per call (touched experts
+        # counted on each copy's own routing)
+        def ffn_bytes(r):
+            return (touched[r] * u4_expert_bytes(cfg) + T * cfg.d * 2 + kept[r] * cfg.d * 4)
+        byts = sum(ffn_bytes(i % n_rep) for i in range(args.steps)) / args.steps
+        gbs = byts / (ffn_ms / 1e3) / 1e9
+        res["roofline"] = {"bound": "hbm", "kernel": "grouped expert FFN call (both "
+                           "4-bit expert kernels)", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                           "bytes_per_launch": byts, "avg_launch_ms": ffn_ms,
+                           "traffic": measured_traffic(cfg.name, "u4")}
+        # the whole layer against HBM: the FFN's bytes plus the router
+        # weights and the layer output
+        layer_bytes = byts + cfg.E * cfg.d * (4 if cfg.router_dtype == "f32" else 2) \
+            + T * cfg.d * (4 if cfg.out_dtype == "f32" else 2)
+        res["layer_hbm_gbs"] = layer_bytes / (ms_step / 1e3) / 1e9
+        res["touched_experts"] = touched
+        res["input_copies_rotated"] = n_rep
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
     print(json.dumps(res), flush=True)
@@ -266,7 +318,7 @@ def traffic_probe(torch, moe, spec, cfg, inp, w, offsets, sorted_token, ws, step
     return 0
 
 
-FFN_KERNELS = ("grouped_gemm_kernel", "tile_prefix_kernel", "fold_split_kernel")
+FFN_KERNELS = ("grouped_gemm_kernel", "tile_prefix_kernel", "fold_split_kernel", "u4s_kernel")
 
 
 def _counter_rows(d):
@@ -325,7 +377,8 @@ def summarize_traffic(args) -> int:
                 "negation for calibration, then three grouped-FFN calls):\n\n```\n")
         f.write("cd /tmp && export TMPDIR=/tmp\n")
         for c, dd in (("FETCH_SIZE", "pmc_fetch"), ("WRITE_SIZE", "pmc_write")):
-            f.write(f"timeout -s KILL 120 rocprofv3 --pmc {c} --output-format csv -d $REPO/gpurun_out/{dd} "
+            f.write(f"timeout -s KILL 120 rocprofv3 --kernel-include-regex '{TRAFFIC_REGEX}' "
+                    f"--pmc {c} --output-format csv -d $REPO/gpurun_out/{dd} "
                     f"-o p -- python3 $REPO/bench.py --config {cfg.cfg_id} --traffic-probe\n")
         f.write(f"python3 $REPO/bench.py --config {cfg.cfg_id} --summarize-traffic "
                 "$REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write\n```\n\n")
@@ -340,7 +393,7 @@ def summarize_traffic(args) -> int:
         f.write(f"- fetch_bytes_per_call: {res['FETCH_SIZE']['per_call']:.6g}\n")
         f.write(f"- write_bytes_per_call: {res['WRITE_SIZE']['per_call']:.6g}\n")
         f.write(f"- bytes_per_call: {total:.6g}\n")
-        f.write(f"- sources_sha256: {sources_digest()}\n")
+        f.write(f"- sources_sha256: {sources_digest(cfg.weight_dtype)}\n")
     print(f"wrote {rel}: {total / 1e9:.3f} GB per call", flush=True)
     return 0
 
