@@ -237,12 +237,12 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
   return v1 > v2 || (v1 == v2 && i1 < i2);
 }
 
-// the better of two candidates; index INT_MAX marks no candidate
+// the better of two candidates, without branches; a lane with no candidate
+// holds (-inf, INT_MAX), which every candidate beats (scores are finite)
 __device__ __forceinline__ void take_better(float& v, int& i, float v2, int i2) {
-  if (i2 != INT_MAX && (i == INT_MAX || better(v2, i2, v, i))) {
-    v = v2;
-    i = i2;
-  }
+  const bool take = (v2 > v) | ((v2 == v) & (i2 < i));
+  v = take ? v2 : v;
+  i = take ? i2 : i;
 }
 
 template <int CTRL>
@@ -251,7 +251,7 @@ __device__ __forceinline__ void best_step(float& v, int& i) {
 }
 
 // Wave-wide best (value, index) among candidates, the same in every lane;
-// lanes without one pass index INT_MAX.  Rows of 16 lanes first (DPP), then
+// lanes without one pass (-inf, INT_MAX).  Rows of 16 lanes first (DPP), then
 // the four row winners.
 __device__ __forceinline__ void wave_best(float& v, int& i) {
   best_step<kDppXor1>(v, i);
@@ -268,17 +268,21 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
 }
 
 // One wave per token; EPL = experts per lane (expert lane + 64*j).
-template <int EPL>
-__global__ void __launch_bounds__(256)
-select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
-              const float* __restrict__ bias, const int32_t* __restrict__ forced,
-              int32_t* __restrict__ rejected,
-              int32_t* __restrict__ ids, float* __restrict__ wout,
-              float* __restrict__ probpart, int64_t T, int E, int k,
-              int router, int norm, float scaling, int n_group,
-              int topk_group) {
-  __shared__ float sel_lds[kSelectWaves][EPL * kWave];
-  __shared__ float pacc[kSelectWaves][EPL * kWave];
+// The selection of every token t = blockIdx.x * NW + wave, + gridDim.x * NW
+// ...: one wave per token.  The routing kind and
+// the forced-id replay are template parameters, so each kernel carries only
+// its own path.
+template <int EPL, int NW, int ROUTER, bool FORCED>
+__device__ __forceinline__ void
+select_body(const float* __restrict__ L, int S, float* __restrict__ Lout,
+            const float* __restrict__ bias, const int32_t* __restrict__ forced,
+            int32_t* __restrict__ rejected,
+            int32_t* __restrict__ ids, float* __restrict__ wout,
+            float* __restrict__ probpart, int64_t T, int E, int k,
+            int norm, float scaling, int n_group, int topk_group) {
+  constexpr int router = ROUTER;
+  __shared__ float sel_lds[NW][EPL * kWave];
+  __shared__ float pacc[NW][EPL * kWave];
   const int lane = threadIdx.x % kWave;
   const int wv = threadIdx.x / kWave;
   float pa[EPL];
@@ -287,8 +291,8 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
   const bool want_p = probpart != nullptr;
   const int G = router == MOE_ROUTER_SIGMOID_GROUP ? E / n_group : 0;
 
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kSelectWaves + wv; t < T;
-       t += static_cast<int64_t>(gridDim.x) * kSelectWaves) {
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * NW + wv; t < T;
+       t += static_cast<int64_t>(gridDim.x) * NW) {
     float v[EPL];
     float sc[EPL];  // sigmoid scores (SIGMOID_GROUP)
     uint32_t cand = 0;  // bit j: expert lane+64j may still be chosen
@@ -299,21 +303,25 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
       if (e < E) {
         // partial logit planes added in plane order
         // all planes are loaded before the (in-order) additions
-        float pv[kMaxLogitPlanes];
+        if (S == 1) {
+          lv = L[t * E + e];
+        } else {
+          float pv[kMaxLogitPlanes];
 #pragma unroll
-        for (int q = 0; q < kMaxLogitPlanes; ++q)
-          pv[q] = q < S ? L[(q * T + t) * E + e] : 0.f;
-        lv = pv[0];
+          for (int q = 0; q < kMaxLogitPlanes; ++q)
+            pv[q] = q < S ? L[(q * T + t) * E + e] : 0.f;
+          lv = pv[0];
 #pragma unroll
-        for (int q = 1; q < kMaxLogitPlanes; ++q)
-          if (q < S) lv += pv[q];
+          for (int q = 1; q < kMaxLogitPlanes; ++q)
+            if (q < S) lv += pv[q];
+        }
         if (Lout) Lout[t * E + e] = lv;
       }
       v[j] = lv;
       sc[j] = 0.f;
       if (e < E) cand |= 1u << j;
     }
-    if (router == MOE_ROUTER_SIGMOID_GROUP) {
+    if constexpr (ROUTER == MOE_ROUTER_SIGMOID_GROUP) {
       // s = sigmoid(L) held in fp32 (evaluated in fp64, rounded once);
       // selection score s + bias, also fp32
 #pragma unroll
@@ -323,12 +331,12 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
         v[j] = sc[j] + ((bias != nullptr && e < E) ? bias[e] : 0.f);
         if (e < E) sel_lds[wv][e] = v[j];
       }
-      if (topk_group < n_group && forced == nullptr) {
+      if (topk_group < n_group && !FORCED) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         // group score: sum of the two largest selection scores
-        float gs = 0.f;
+        float gs = -INFINITY;
         int gi = INT_MAX;
         if (lane < n_group) {
           float a = -INFINITY, b = -INFINITY;
@@ -347,8 +355,9 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
         // keep the best topk_group groups (ties to the lower group)
         uint64_t kept = 0;
         for (int r = 0; r < topk_group; ++r) {
-          float bv = gs;
-          int bi = ((kept >> lane) & 1ull) ? INT_MAX : gi;
+          const bool out = (kept >> lane) & 1ull;
+          float bv = out ? -INFINITY : gs;
+          int bi = out ? INT_MAX : gi;
           wave_best(bv, bi);
           kept |= 1ull << bi;
         }
@@ -364,7 +373,7 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
     int my_id = 0;
     float my_val = 0.f;
     bool reject = false;
-    if (forced != nullptr) {
+    if constexpr (FORCED) {
       // router replay: lane r takes the r-th given id; a row that is not k
       // distinct experts in [0, E) is rejected (identity route, weight 0)
       const int fid = lane < k ? forced[t * k + lane] : 0;
@@ -384,16 +393,13 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
       }
       if (reject && lane == 0) atomicAdd(rejected, 1);
     }
-    for (int r = 0; r < k && forced == nullptr; ++r) {
-      float bv = 0.f;
+    for (int r = 0; r < k && !FORCED; ++r) {
+      float bv = -INFINITY;
       int bi = INT_MAX;
 #pragma unroll
       for (int j = 0; j < EPL; ++j) {
-        const int e = lane + kWave * j;
-        if (((cand >> j) & 1u) && (bi == INT_MAX || better(v[j], e, bv, bi))) {
-          bv = v[j];
-          bi = e;
-        }
+        const bool c = (cand >> j) & 1u;
+        take_better(bv, bi, c ? v[j] : -INFINITY, c ? lane + kWave * j : INT_MAX);
       }
       wave_best(bv, bi);
       if (lane == r) {
@@ -403,11 +409,11 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
       if ((bi % kWave) == lane) cand &= ~(1u << (bi / kWave));
     }
     float wk;
-    if (router == MOE_ROUTER_SOFTMAX_TOPK) {
+    if constexpr (ROUTER == MOE_ROUTER_SOFTMAX_TOPK) {
       // the largest logit: the first choice, or for given ids the maximum
       // over all experts (the same value whenever the first choice is given)
       float m = lane_f(my_val, 0);
-      if (forced != nullptr) {
+      if constexpr (FORCED) {
         float mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < EPL; ++j)
@@ -455,11 +461,25 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += blockDim.x) {
       float s = 0.f;
-      for (int q = 0; q < kSelectWaves; ++q) s += pacc[q][e];
+      for (int q = 0; q < NW; ++q) s += pacc[q][e];
       probpart[static_cast<int64_t>(blockIdx.x) * E + e] = s;
     }
   }
 }
+
+template <int EPL, int ROUTER, bool FORCED>
+__global__ void __launch_bounds__(256)
+select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
+              const float* __restrict__ bias, const int32_t* __restrict__ forced,
+              int32_t* __restrict__ rejected,
+              int32_t* __restrict__ ids, float* __restrict__ wout,
+              float* __restrict__ probpart, int64_t T, int E, int k,
+              int norm, float scaling, int n_group, int topk_group) {
+  select_body<EPL, kSelectWaves, ROUTER, FORCED>(L, S, Lout, bias, forced, rejected, ids,
+                                                 wout, probpart, T, E, k, norm, scaling,
+                                                 n_group, topk_group);
+}
+
 
 __global__ void prob_finalize_kernel(const float* __restrict__ part, int nb,
                                      int E, float* __restrict__ out) {
@@ -524,18 +544,29 @@ hipError_t launch_router_select(const Dims& D, const moe_spec& sp,
   const int epl = (D.E + kWave - 1) / kWave;
   const float scaling =
       sp.router == MOE_ROUTER_SIGMOID_GROUP ? sp.routed_scaling : 1.0f;
-#define MOE_SELECT(N)                                                        \
-  hipLaunchKernelGGL((select_kernel<N>), dim3(nblocks), dim3(256), 0, s,     \
+#define MOE_SELECT3(N, R, F)                                                   \
+  hipLaunchKernelGGL((select_kernel<N, R, F>), dim3(nblocks), dim3(256), 0, s,  \
                      logits, S, logits_out, bias, forced, rejected, ids, w,     \
-                     probpart, D.T, D.E,                                        \
-                     D.k, sp.router,                                            \
-                     sp.norm_topk_prob, scaling, sp.n_group, sp.topk_group)
-  if (epl <= 1) MOE_SELECT(1);
-  else if (epl <= 2) MOE_SELECT(2);
-  else if (epl <= 4) MOE_SELECT(4);
-  else if (epl <= 8) MOE_SELECT(8);
-  else MOE_SELECT(16);
+                     probpart, D.T, D.E, D.k, sp.norm_topk_prob, scaling,       \
+                     sp.n_group, sp.topk_group)
+#define MOE_SELECT(N)                                                           \
+  {                                                                             \
+    const bool f = forced != nullptr;                                           \
+    if (sp.router == MOE_ROUTER_SOFTMAX_TOPK) {                                 \
+      if (f) MOE_SELECT3(N, MOE_ROUTER_SOFTMAX_TOPK, true);                     \
+      else MOE_SELECT3(N, MOE_ROUTER_SOFTMAX_TOPK, false);                      \
+    } else {                                                                    \
+      if (f) MOE_SELECT3(N, MOE_ROUTER_SIGMOID_GROUP, true);                    \
+      else MOE_SELECT3(N, MOE_ROUTER_SIGMOID_GROUP, false);                     \
+    }                                                                           \
+  }
+  if (epl <= 1) MOE_SELECT(1)
+  else if (epl <= 2) MOE_SELECT(2)
+  else if (epl <= 4) MOE_SELECT(4)
+  else if (epl <= 8) MOE_SELECT(8)
+  else MOE_SELECT(16)
 #undef MOE_SELECT
+#undef MOE_SELECT3
   return hipGetLastError();
 }
 
