@@ -217,7 +217,7 @@ dispatch_small_kernel(const int32_t* __restrict__ ids, const float* __restrict__
   __shared__ int32_t h[1024];
   __shared__ int32_t run[1024];
   __shared__ int32_t offs[1024];
-  __shared__ int32_t wcnt[16][64];  // per-wave counts of a 64-expert window
+  __shared__ int32_t wcnt[16][1024];  // per-wave counts of one round
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += blockDim.x) h[e] = 0;
   __syncthreads();
@@ -233,7 +233,7 @@ dispatch_small_kernel(const int32_t* __restrict__ ids, const float* __restrict__
   __syncthreads();
   // ranks: slots in flat order; inside a wave, lanes with the same expert
   // are matched on the expert-id bits; across waves, earlier waves' counts
-  // are added through LDS (experts are visited in windows of 64)
+  // are added through a per-wave table of all experts in LDS
   const int lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   for (int e = tid; e < E; e += blockDim.x) run[e] = 0;
@@ -255,27 +255,22 @@ dispatch_small_kernel(const int32_t* __restrict__ ids, const float* __restrict__
     const int within = __popcll(mask & lt_mask);
     const int mine = __popcll(mask);
     int32_t rank = 0;
-    // process experts in windows of 64 so the per-wave table stays small
-    for (int e0 = 0; e0 < E; e0 += 64) {
-      for (int i = tid; i < nw * 64; i += blockDim.x) wcnt[i / 64][i % 64] = 0;
-      __syncthreads();
-      const bool here = valid && e >= e0 && e < e0 + 64;
-      if (here && within == 0) wcnt[wv][e - e0] = mine;
-      __syncthreads();
-      if (here) {
-        rank = run[e] + within;
-        for (int q = 0; q < wv; ++q) rank += wcnt[q][e - e0];
-      }
-      __syncthreads();
-      for (int i = tid; i < 64; i += blockDim.x) {
-        if (e0 + i < E) {
-          int32_t add = 0;
-          for (int q = 0; q < nw; ++q) add += wcnt[q][i];
-          run[e0 + i] += add;
-        }
-      }
-      __syncthreads();
+    for (int q = 0; q < nw; ++q)
+      for (int x = tid; x < E; x += blockDim.x) wcnt[q][x] = 0;
+    __syncthreads();
+    if (valid && within == 0) wcnt[wv][e] = mine;
+    __syncthreads();
+    if (valid) {
+      rank = run[e] + within;
+      for (int q = 0; q < wv; ++q) rank += wcnt[q][e];
     }
+    __syncthreads();
+    for (int x = tid; x < E; x += blockDim.x) {
+      int32_t add = 0;
+      for (int q = 0; q < nw; ++q) add += wcnt[q][x];
+      run[x] += add;
+    }
+    __syncthreads();
     if (s < S) {
       int32_t row = -1;
       if (valid && static_cast<int64_t>(rank) < cap) {
