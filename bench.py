@@ -33,6 +33,12 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
 
 
+def _median(v):
+    s = sorted(v)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
 def u4_expert_bytes(cfg) -> int:
     """Bytes of one routed expert's 4-bit weights: packed codes (half a byte
     per weight) plus a bf16 scale and bias per 64 weights of a row, for the
@@ -94,6 +100,17 @@ def measured_traffic(workload: str, weight_dtype: str = "bf16"):
         return None
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, inp, sample: int):
     """The oracle as it stands, on the host cores: routing and dispatch of
     the whole batch plus the expert FFN of `sample` seeded tokens."""
@@ -140,14 +157,15 @@ def cpu_baseline(cfg, inp, sample: int):
             "sample": f"{reps} oracle layer calls, each routing+dispatch of all {cfg.T} tokens "
                       f"and expert FFN+combine of {len(toks)} seeded tokens (fp64 NumPy), "
                       f"{dt:.1f} s in total",
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
+            "cpu_model": _cpu_model()}
 
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, help="workload id (1-5)")
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens whose expert FFN the CPU oracle evaluates")
@@ -270,7 +288,8 @@ def main() -> int:
                      "GEMM1 gate/up + SwiGLU, GEMM2 down, split fold)", "achieved": tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS, "flops_per_launch": flops,
-                     "avg_launch_ms": ffn_ms, "traffic": measured_traffic(cfg.name)},
+                     "avg_launch_ms": ffn_ms, "median_launch_ms": _median(ffn_times),
+                     "min_launch_ms": min(ffn_times), "traffic": measured_traffic(cfg.name)},
     }
     if u4:
         # bound by HBM: the touched experts' packed weights, the token rows
@@ -284,6 +303,8 @@ def main() -> int:
                            "4-bit expert kernels)", "achieved": gbs, "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                            "bytes_per_launch": byts, "avg_launch_ms": ffn_ms,
+                           "median_launch_ms": _median(ffn_times),
+                           "min_launch_ms": min(ffn_times),
                            "traffic": measured_traffic(cfg.name, "u4")}
         # the whole layer against HBM: the FFN's bytes plus the router
         # weights and the layer output
