@@ -4,22 +4,23 @@
 //
 // Built for decode-shaped batches, where each touched expert sees a handful
 // of rows and the layer is bound by streaming the packed weights from HBM:
-// every weight byte is read once and used for all of the expert's rows.
+// every weight byte is read once and serves up to 4 of the expert's rows.
 // The affine dequantisation is factored per group so no dequantised weight
 // is formed:
 //   sum_j x_j (s q_j + b) = s * sum_j x_j q_j + b * sum_j x_j
-// over the 32-element run a lane owns (always inside one group of 64), and
-// the codes enter v_dot2_f32_f16 as exact fp16 values (1024 + q or
-// 1024 + 16q), two per instruction, against the lane's activations
-// pre-packed as fp16 pairs.
+// The codes enter the matrix cores as exact fp16 values (1024 + q for the
+// even nibbles, 1024 + 16q for the odd ones, one AND-OR per pair of codes)
+// and sum_j x_j q_j is formed by v_mfma_f32_4x4x4_16b_f16: 16 independent
+// 4x4x4 products per instruction, each block taking 4 units of the weight
+// matrix against up to 4 activation rows over its own slice of K.  The
+// blocks of one unit group split K between them; their partial sums, scaled
+// per group, are added across lanes once per item.
 //
 // One kernel serves both products:
 //   up   : unit = hidden column f; the gate row f and the up row f, the
 //          epilogue writes H = silu(gate) * up (fp16, as on the
 //          matrix-core path)
 //   down : unit = output column n of W_down, writes Y (fp32)
-// LPR = K/32 lanes share one unit; a wave-wide 16-byte load covers 64/LPR
-// units, and the lane groups reduce their partial sums together.
 #include <type_traits>
 
 #include "moe_internal.hpp"
@@ -27,25 +28,24 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxK = 2048;  // one pass of 64 lanes x 32 elements per row
+constexpr int kMaxK = 2048;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 
-// The value of this lane's partner at distance D (a power of two up to 32):
-// partners differ in bit D of the lane index and possibly in lower bits.
-// D <= 8 are DPP moves inside rows of 16 lanes (the two xor pairings of a
-// quad, then the mirrors of 8 and 16 lanes), 16 and 32 the gfx950 row
-// swaps; none goes through LDS.
+// The value held by lane (this lane xor D), D in {4, 8, 16, 32}: the row
+// shifts by 4 (each direction serves the lanes whose partner stays inside
+// their row of 16), the row rotation by 8, and the gfx950 row swaps for 16
+// and 32.  None goes through LDS.
 template <int D>
-__device__ __forceinline__ float pair_move(float v, int lane) {
-  if constexpr (D == 1) {
-    return dpp_f<kDppXor1>(v);
-  } else if constexpr (D == 2) {
-    return dpp_f<kDppXor2>(v);
-  } else if constexpr (D == 4) {
-    return dpp_f<kDppHalfMirror>(v);
+__device__ __forceinline__ float xor_move(float v, int lane) {
+  if constexpr (D == 4) {
+    const float dn = dpp_f<0x114>(v);  // row_shr:4, from lane l-4
+    const float up = dpp_f<0x104>(v);  // row_shl:4, from lane l+4
+    return (lane & 4) ? dn : up;
   } else if constexpr (D == 8) {
-    return dpp_f<kDppMirror>(v);
+    return dpp_f<0x128>(v);  // row_ror:8, xor 8 inside a row of 16
   } else if constexpr (D == 16) {
     // odd rows of the first result hold the even rows, and the other way
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
@@ -59,19 +59,15 @@ __device__ __forceinline__ float pair_move(float v, int lane) {
   }
 }
 
-// In-place reduction of V per-lane values over each group of LPR lanes
-// (LPR and V powers of two).  Butterfly with halving: at distance D the
-// lane with bit D set keeps the upper half of its values and sends the
-// lower half, so each exchange carries half of the values and V values cost
-// about V moves in all instead of V*log2(LPR).  Any partner that differs in
-// bit D (and possibly lower bits) holds the same index subset at that step,
-// so the pair_move pairings serve as well as xor.  On return a lane holds
-// C = max(1, V/LPR) totals in v[0..C): those of indices
-// reduce_index(lane, j), identical on lanes that differ only below the
-// last halving distance.
+// In-place sum of V per-lane values over the lanes that differ only in the
+// bits D, D/2, ..., 4 (the K slices of a unit group).  Butterfly with
+// halving: at distance D the lane with bit D set keeps the upper half of its
+// values and sends the lower half; once one value is left the remaining
+// distances add it whole.  On return a lane holds max(1, V >> halvings)
+// totals, those of indices kred_index(lane, j).
 template <int D, int CNT, int V>
-__device__ __forceinline__ void reduce_step(float (&v)[V], int lane) {
-  if constexpr (D >= 1) {
+__device__ __forceinline__ void kred(float (&v)[V], int lane) {
+  if constexpr (D >= 4) {
     if constexpr (CNT > 1) {
       constexpr int kHalf = CNT / 2;
       const bool upper = (lane & D) != 0;
@@ -79,97 +75,104 @@ __device__ __forceinline__ void reduce_step(float (&v)[V], int lane) {
       for (int i = 0; i < kHalf; ++i) {
         const float send = upper ? v[i] : v[i + kHalf];
         const float keep = upper ? v[i + kHalf] : v[i];
-        v[i] = keep + pair_move<D>(send, lane);
+        v[i] = keep + xor_move<D>(send, lane);
       }
-      reduce_step<D / 2, kHalf, V>(v, lane);
+      kred<D / 2, kHalf, V>(v, lane);
     } else {
-      v[0] += pair_move<D>(v[0], lane);
-      reduce_step<D / 2, 1, V>(v, lane);
+      v[0] += xor_move<D>(v[0], lane);
+      kred<D / 2, 1, V>(v, lane);
     }
   }
 }
 
-template <int V, int LPR>
-__device__ __forceinline__ void multi_reduce(float (&v)[V], int lane) {
-  reduce_step<LPR / 2, V, V>(v, lane);
-}
-
-// index of v[j] after multi_reduce<V, LPR> on this lane
-template <int V, int LPR>
-__device__ __forceinline__ int reduce_index(int lane, int j) {
+// index of v[j] after kred<DTOP, V, V> on this lane
+template <int V, int DTOP>
+__device__ __forceinline__ int kred_index(int lane, int j) {
   int idx = j, c = V;
 #pragma unroll
-  for (int d = LPR / 2; d >= 1 && c > 1; d >>= 1) {
+  for (int d = DTOP; d >= 4 && c > 1; d >>= 1) {
     c /= 2;
     if (lane & d) idx += c;
   }
   return idx;
 }
 
-// lowest lane distance at which multi_reduce<V, LPR> still halves
-template <int V, int LPR>
-constexpr int last_halving_distance() {
-  int c = V, last = LPR;
-  for (int d = LPR / 2; d >= 1 && c > 1; d >>= 1) {
+// lowest distance at which kred<DTOP, V, V> still halves (2 * DTOP when it
+// never does); lanes that differ only in the bits from 4 up to below it
+// hold the same totals
+template <int V, int DTOP>
+constexpr int kred_last() {
+  int c = V, last = 2 * DTOP;
+  for (int d = DTOP; d >= 4 && c > 1; d >>= 1) {
     c /= 2;
     last = d;
   }
-  return last;
+  return last < 4 ? 4 : last;
 }
 
-// lanes per unit: each lane owns 32 elements of K, so LPR = K/32 (K is a
-// power of two from 64 to 2048)
-int pick_lpr(int K) {
-  int l = 64;
-  while (l > 1 && K % (32 * l) != 0) l >>= 1;
-  return l;
-}
+// Work layout for a reduction length K (a power of two from 64 to 2048).
+// Lane 4b+i of a wave is row i of MFMA block b (unit i of the block's group
+// in the A operand, activation row i in the B operand); block
+// b = ug * NKS + ks takes the 4 units of unit group ug over K slice ks (KB
+// elements).  An item is UPI = 4 * NUG consecutive units of one expert:
+// 32 * KB bytes of codes per matrix (4 KiB; 2 KiB for K = 64) and
+// 2 * KB bytes each of scales and biases.
+template <int K>
+struct KCfg {
+  static constexpr int KB = K < 128 ? K : 128;
+  static constexpr int NKS = K / KB;         // K slices per unit group
+  static constexpr int NUG = 16 / NKS;       // unit groups per item
+  static constexpr int UPI = 4 * NUG;        // units per item
+  static constexpr int WPL = KB / 8;         // packed words per lane and matrix
+  static constexpr int GPL = KB / 64;        // quantisation groups per K slice
+  static constexpr int G = K / 64;           // groups per unit row
+  static constexpr int kCode = UPI * K / 2;  // code bytes per matrix
+  static constexpr int kDma = kCode / 1024;  // wave-wide 16-byte loads per matrix
+  static constexpr int kSB = UPI * G * 2;    // scale (or bias) bytes per matrix
+  static constexpr int kSBLanes = kSB / 4;   // lanes of its 4-byte load
+  // In LDS, 16-byte piece p of a kSeg-byte segment of unit u sits at slot
+  // p ^ (u % kPieces): the 16 lanes that one LDS read serves together (4 K
+  // slices x 4 units) then hit distinct banks for K >= 512.
+  static constexpr int kSeg = K / 2 < 64 ? K / 2 : 64;
+  static constexpr int kPieces = kSeg / 16;
+  static_assert(NKS * NUG == 16 && GPL >= 1 && WPL % 4 == 0, "blocks");
+  static_assert(kCode == 32 * KB && kCode % 1024 == 0 && kSB == 2 * KB, "item layout");
+};
 
 // ---------------------------------------------------------------- streaming
-// The packed weights stream through LDS.  Work is cut into items: one row
-// chunk (up to kRows of the expert's rows) against kSub wave-wide 16-byte
-// loads per matrix, i.e. kSub * (64/LPR) consecutive units of one expert
-// (kSub KiB of codes per matrix) plus their scales and biases (64 kSub
-// bytes each).  The active
-// experts are listed on the device and their items numbered (expert, row
-// chunk, unit block) with the unit block fastest; every wave of a persistent
-// grid takes one contiguous range of items of equal cost, an item of r rows
-// costing kItemCost + r (its loads and unpacking, then r rows of dot
-// products), so a wave on a busy expert takes fewer items.  An expert with
-// more than kRows rows streams its weights once per chunk.  A wave is an independent pipeline over a private ring of NS
-// stages in LDS: the direct-to-LDS loads of the item NS-1 ahead are issued
-// before the current item is computed, so NS-1 items per wave are always in
-// flight, and the only wait is the wave's own vmcnt.  The buffer descriptors
-// carry each expert matrix's size, so a load past the last unit fetches
-// nothing.
-constexpr int kItemCost = 2;     // cost of an item beyond its rows, in rows
+// The packed weights stream through LDS.  The active experts are listed on
+// the device and their items numbered (expert, row chunk, unit block) with
+// the unit block fastest; every wave of a persistent grid takes one
+// contiguous range of items of equal cost, an item of r rows costing
+// kItemCost + r, so a wave on a busy expert takes fewer items.  A chunk is up
+// to 4 of the expert's rows (the 4 columns of every MFMA block), so an
+// expert with more than 4 rows streams its weights once per chunk.  A wave
+// is an independent pipeline over a private ring of NS stages in LDS: the
+// direct-to-LDS loads of the item NS-1 ahead are issued before the current
+// item is computed, so NS-1 items per wave are always in flight, and the
+// only wait is the wave's own vmcnt.  The buffer descriptors carry each
+// expert matrix's size, so a load past the last unit fetches nothing.
+constexpr int kItemCost = 12;    // cost of an item beyond its rows, in rows
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxChunkRows = 4;
 
-// Per product: waves per workgroup (one workgroup per CU), wave-wide 16-byte
-// loads per matrix and item, rows per chunk (held in registers) and stages
-// per wave.  Both keep 144 KiB of LDS in the ring.  Measured on the decode
-// layer (256 experts, top-8, 32 tokens): 16 waves with 2-row chunks keep the
-// registers under 128 (4 waves per SIMD) and beat 8 waves with 4-row
-// chunks by a third; 1-row chunks lose what they save in registers to
-// unpacking the codes once per row.
-template <bool PAIR>
+// Per product: 8 waves per workgroup (one workgroup per CU, two waves per
+// SIMD) and 2 (gate/up) or 4 (down) stages per wave: 144 KiB of ring for the
+// decode shapes (K = 2048 and 512).
+template <bool PAIR, int K>
 struct SCfg {
-  static constexpr int kWaves = 16;
-  static constexpr int kSub = 2;
-  static constexpr int kRows = 2;
+  using KC = KCfg<K>;
+  static constexpr int kWaves = 8;
+  static constexpr int kRows = kMaxChunkRows;
   static constexpr int kStages = PAIR ? 2 : 4;
   static constexpr int M = PAIR ? 2 : 1;
-  static constexpr int kCode = kSub * 1024;  // codes of one matrix
-  static constexpr int kSB = kSub * 64;      // scales (or biases) of one matrix
-  static constexpr int kSBLanes = kSB / 4;   // lanes of its 4-byte load
-  static constexpr int kBytes = M * kCode + 2 * M * kSB;  // one stage
-  static constexpr int kLoads = M * kSub + 2 * M;  // load instructions per item
+  static constexpr int kBytes = M * KC::kCode + 2 * M * KC::kSB;  // one stage
+  static constexpr int kLoads = M * KC::kDma + 2 * M;  // load instructions per item
   static constexpr int kThreads = kWaves * 64;
   static constexpr int kPasses = (kMaxExperts + kThreads - 1) / kThreads;
   static constexpr int kLds =
       kWaves * kStages * kBytes + (3 * kMaxExperts + 2) * 4 + 3 * kPasses * kWaves * 4;
-  static_assert(kRows <= kMaxChunkRows && kLds <= 160 * 1024, "stream layout");
+  static_assert(kLds <= 160 * 1024, "stream layout");
 };
 
 // The direct-to-LDS loads are written out here rather than through the
@@ -234,11 +237,14 @@ __device__ __forceinline__ void wait_later(int later) {
   wait_vm<0>();
 }
 
-// (a & m) | c in one instruction (the masks would otherwise cost an AND and
-// an OR each: a VOP3 instruction takes no literal here)
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+// A VGPR holding c that the optimiser cannot fold back into a literal, so
+// that (a & m) | c with m in it is one v_and_or_b32 (a VOP3 instruction
+// takes no literal here).  The AND-OR itself stays ordinary code: the
+// matrix cores read its results, and the compiler must see it as the VALU
+// write it is to keep the required wait states in front of them.
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t c) {
   uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "s"(c));
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
   return r;
 }
 
@@ -250,46 +256,38 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
 __device__ __forceinline__ void unpack8(uint32_t w, uint32_t m_lo, uint32_t m_hi,
                                         half2_t* c) {
   const uint32_t h = w >> 8;
-  c[0] = __builtin_bit_cast(half2_t, and_or(w, m_lo, 0x64006400u));
-  c[1] = __builtin_bit_cast(half2_t, and_or(w, m_hi, 0x64006400u));
-  c[2] = __builtin_bit_cast(half2_t, and_or(h, m_lo, 0x64006400u));
-  c[3] = __builtin_bit_cast(half2_t, and_or(h, m_hi, 0x64006400u));
+  c[0] = __builtin_bit_cast(half2_t, (w & m_lo) | 0x64006400u);
+  c[1] = __builtin_bit_cast(half2_t, (w & m_hi) | 0x64006400u);
+  c[2] = __builtin_bit_cast(half2_t, (h & m_lo) | 0x64006400u);
+  c[3] = __builtin_bit_cast(half2_t, (h & m_hi) | 0x64006400u);
 }
 
-// One lane's 32 activations of a row as fp16 pairs xp[4m + j] = (x_{8m+j},
-// x_{8m+j+4}) matching unpack8, with the fp32 sums over all 32 (xs) and
-// over the pairs j = 1, 3 (s13).
+// Eight activations of a row (bf16, or fp16 when !BF16) as the two MFMA B
+// operands that match unpack8: xa = (x0, x4, x2, x6) against the codes
+// that carry 1024 + q, xb = (x1, x5, x3, x7) against 1024 + 16q, with the
+// fp32 sums of the fp16 values of each set.
 template <bool BF16>
-__device__ __forceinline__ void load_row(const uint16_t* p, half2_t* xp, float& xs,
-                                         float& s13) {
-  xs = 0.f;
-  s13 = 0.f;
+__device__ __forceinline__ void load_word(const uint16_t* p, half4_t& xa, half4_t& xb,
+                                          float& sa, float& sb) {
+  const uint4 t = *reinterpret_cast<const uint4*>(p);
+  const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
+  _Float16 h[8];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint4 t = *reinterpret_cast<const uint4*>(p + 8 * m);
-    const uint32_t tw[4] = {t.x, t.y, t.z, t.w};
-    _Float16 h[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (BF16) {
-        h[2 * i] = static_cast<_Float16>(__uint_as_float(tw[i] << 16));
-        h[2 * i + 1] = static_cast<_Float16>(__uint_as_float(tw[i] & 0xffff0000u));
-      } else {
-        h[2 * i] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(tw[i] & 0xffffu));
-        h[2 * i + 1] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(tw[i] >> 16));
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      half2_t v;
-      v[0] = h[j];
-      v[1] = h[j + 4];
-      xp[m * 4 + j] = v;
-      const float pair = static_cast<float>(h[j]) + static_cast<float>(h[j + 4]);
-      xs += pair;
-      if (j & 1) s13 += pair;
+  for (int i = 0; i < 4; ++i) {
+    if (BF16) {
+      h[2 * i] = static_cast<_Float16>(__uint_as_float(tw[i] << 16));
+      h[2 * i + 1] = static_cast<_Float16>(__uint_as_float(tw[i] & 0xffff0000u));
+    } else {
+      h[2 * i] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(tw[i] & 0xffffu));
+      h[2 * i + 1] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(tw[i] >> 16));
     }
   }
+  xa = half4_t{h[0], h[4], h[2], h[6]};
+  xb = half4_t{h[1], h[5], h[3], h[7]};
+  sa += (static_cast<float>(h[0]) + static_cast<float>(h[4])) +
+        (static_cast<float>(h[2]) + static_cast<float>(h[6]));
+  sb += (static_cast<float>(h[1]) + static_cast<float>(h[5])) +
+        (static_cast<float>(h[3]) + static_cast<float>(h[7]));
 }
 
 struct U4Args {
@@ -317,19 +315,19 @@ __device__ __forceinline__ int wave_prefix(int v, int lane, int& total) {
   return inc - v;
 }
 
-template <bool PAIR, int LPR>
+template <bool PAIR, int K>
 __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
-  using SL = SCfg<PAIR>;
+  using SL = SCfg<PAIR, K>;
+  using KC = KCfg<K>;
   constexpr int kRows = SL::kRows;
   constexpr int kSWaves = SL::kWaves;
-  constexpr int kSUB = SL::kSub;
-  constexpr int K = 32 * LPR;
-  constexpr int UPW = 64 / LPR;        // units per wave-wide load
-  constexpr int UPI = kSUB * UPW;      // units per item
-  constexpr int G = K / 64;            // quantisation groups per row
+  constexpr int UPI = KC::UPI;
+  constexpr int G = KC::G;
   constexpr int NS = SL::kStages;
   constexpr int M = SL::M;
   constexpr int L = SL::kLoads;
+  constexpr int V = 4 * M;             // an item's per-lane values: 4 units x M matrices
+  constexpr int DTOP = 2 * KC::NKS;    // largest lane distance between K slices
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -456,6 +454,34 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
     }
   };
 
+  // ---- per-lane layout
+  const int i4 = lane & 3;  // unit i4 of the block's group (A), activation row i4 (B)
+  const int blk = lane >> 2;
+  const int ug = blk / KC::NKS, ks = blk % KC::NKS;
+  // load c of a matrix fills LDS bytes [1024c, 1024c + 1024) of the item's
+  // code region; lane l writes bytes 1024c + 16l and fetches the piece that
+  // the slot rotation puts there
+  uint32_t dma_off[KC::kDma];
+#pragma unroll
+  for (int c = 0; c < KC::kDma; ++c) {
+    const int q = c * 1024 + 16 * lane;
+    const int u = q / (K / 2), o = q % (K / 2);
+    const int slot = (o % KC::kSeg) / 16;
+    dma_off[c] = static_cast<uint32_t>(u * (K / 2) + (o / KC::kSeg) * KC::kSeg +
+                                       ((slot ^ (u % KC::kPieces)) * 16));
+  }
+  // read c of a lane: 16 bytes (4 packed words) of unit 4*ug + i4 at code
+  // byte ks * KB/2 + 16c of its row
+  uint32_t rd_off[KC::WPL / 4];
+#pragma unroll
+  for (int c = 0; c < KC::WPL / 4; ++c) {
+    const int u = 4 * ug + i4;
+    const int o = ks * (KC::KB / 2) + 16 * c;
+    const int piece = (o % KC::kSeg) / 16;
+    rd_off[c] = static_cast<uint32_t>(u * (K / 2) + (o / KC::kSeg) * KC::kSeg +
+                                      ((piece ^ (u % KC::kPieces)) * 16));
+  }
+
   auto issue = [&](int t) {
     const int a = ia;
     const int u0 = ib * UPI;
@@ -467,9 +493,10 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const rsrc_t rq = make_rsrc(g.q[m] + erow * (K / 2), g.N * (K / 2));
-      const uint32_t vq = static_cast<uint32_t>(u0 * (K / 2) + lane * 16);
+      const uint32_t vq = static_cast<uint32_t>(u0 * (K / 2));
 #pragma unroll
-      for (int j = 0; j < kSUB; ++j) dma16(rq, st + m * SL::kCode + j * 1024, vq + j * 1024);
+      for (int c = 0; c < KC::kDma; ++c)
+        dma16(rq, st + m * KC::kCode + c * 1024, vq + dma_off[c]);
     }
 #pragma unroll
     for (int m = 0; m < M; ++m) {
@@ -477,94 +504,112 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
       const rsrc_t rs = make_rsrc(g.s[m] + erow * (G * 2), g.N * G * 2);
       const rsrc_t rb = make_rsrc(g.b[m] + erow * (G * 2), g.N * G * 2);
       // the item's scales (biases) are kSB contiguous bytes
-      if (SL::kSBLanes >= 64 || lane < SL::kSBLanes) {
-        dma4(rs, st + M * SL::kCode + (2 * m) * SL::kSB, vs);
-        dma4(rb, st + M * SL::kCode + (2 * m + 1) * SL::kSB, vs);
+      if (KC::kSBLanes >= 64 || lane < KC::kSBLanes) {
+        dma4(rs, st + M * KC::kCode + (2 * m) * KC::kSB, vs);
+        dma4(rb, st + M * KC::kCode + (2 * m + 1) * KC::kSB, vs);
       }
     }
   };
 
-  // the chunk's activation rows, held in registers
-  const int kl = lane % LPR;
-  const int sg = lane / LPR;
-  const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u;
-  half2_t xp[kRows][16];
-  float xs[kRows], xc[kRows];
+  // the chunk's activation row i4 over K slice ks, as MFMA B operands
+  const uint32_t m_lo = opaque_vgpr(0x000F000Fu), m_hi = opaque_vgpr(0x00F000F0u);
+  half4_t xa[KC::WPL], xb[KC::WPL];
+  float xs[KC::GPL], xc[KC::GPL];
   auto load_rows = [&](int row0, int rows) {
+    // a lane past the chunk's rows reads the chunk's first row and keeps
+    // zeros, so no branch divides the wave here
+    const bool live = i4 < rows;
+    const int32_t kr = row0 + (live ? i4 : 0);
+    const int64_t src = g.sorted_token ? static_cast<int64_t>(g.sorted_token[kr])
+                                       : static_cast<int64_t>(kr);
+    const uint16_t* p = g.a + src * K + ks * KC::KB;
+    const half4_t zero = half4_t{0, 0, 0, 0};
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      if (r < rows) {
-        const int32_t kr = row0 + r;
-        const int64_t src = g.sorted_token ? static_cast<int64_t>(g.sorted_token[kr])
-                                           : static_cast<int64_t>(kr);
-        float s13;
-        load_row<PAIR>(g.a + src * K + 32 * kl, xp[r], xs[r], s13);
-        // offsets carried by the codes: 1024 per element of the pairs
-        // j = 0, 2 and 64 (1024/16) per element of the pairs j = 1, 3
-        xc[r] = 1024.f * xs[r] - 960.f * s13;
+    for (int gg = 0; gg < KC::GPL; ++gg) {
+      float sa = 0.f, sb = 0.f;
+#pragma unroll
+      for (int w = gg * 8; w < gg * 8 + 8; ++w) {
+        load_word<PAIR>(p + 8 * w, xa[w], xb[w], sa, sb);
+        xa[w] = live ? xa[w] : zero;
+        xb[w] = live ? xb[w] : zero;
       }
+      xs[gg] = live ? sa + sb : 0.f;
+      // offsets carried by the codes: 1024 per element of xa, 64 (1024/16)
+      // per element of xb
+      xc[gg] = live ? fmaf(1024.f, sa, 64.f * sb) : 0.f;
     }
   };
 
-  // R rows (register slots 0..R-1, kept rows row0..) against the codes in
-  // stage st
-  auto rows_pass = [&](auto RC, const uint8_t* st, int row0, int u0) {
-    constexpr int R = decltype(RC)::value;
-    constexpr int V = kSUB * R * M;
-    float v[V];
+  // the item in stage st: units u0.. of the expert, chunk rows row0..
+  auto compute = [&](const uint8_t* st, int row0, int rows, int u0) {
+    float4_t acc[M][KC::GPL][2];
 #pragma unroll
-    for (int j = 0; j < kSUB; ++j) {
-      const int ul = j * UPW + sg;  // unit inside the item
+    for (int m = 0; m < M; ++m)
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const uint4 w = *reinterpret_cast<const uint4*>(st + m * SL::kCode + j * 1024 + lane * 16);
-        const uint16_t* sb = reinterpret_cast<const uint16_t*>(st + M * SL::kCode);
-        const float sc = bf16_to_f32(sb[(2 * m) * (SL::kSB / 2) + ul * G + kl / 2]);
-        const float bi = bf16_to_f32(sb[(2 * m + 1) * (SL::kSB / 2) + ul * G + kl / 2]);
-        half2_t c[4][4];
-        unpack8(w.x, m_lo, m_hi, c[0]);
-        unpack8(w.y, m_lo, m_hi, c[1]);
-        unpack8(w.z, m_lo, m_hi, c[2]);
-        unpack8(w.w, m_lo, m_hi, c[3]);
+      for (int gg = 0; gg < KC::GPL; ++gg)
+        acc[m][gg][0] = acc[m][gg][1] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          float a0 = 0.f, a1 = 0.f;
+    for (int m = 0; m < M; ++m) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            a0 = __builtin_amdgcn_fdot2(c[q][0], xp[r][4 * q + 0], a0, false);
-            a1 = __builtin_amdgcn_fdot2(c[q][1], xp[r][4 * q + 1], a1, false);
-            a0 = __builtin_amdgcn_fdot2(c[q][2], xp[r][4 * q + 2], a0, false);
-            a1 = __builtin_amdgcn_fdot2(c[q][3], xp[r][4 * q + 3], a1, false);
-          }
-          const float dm = fmaf(a1, 0.0625f, a0);  // sum x (offset + q)
-          v[(j * R + r) * M + m] = fmaf(sc, dm - xc[r], bi * xs[r]);
+      for (int c = 0; c < KC::WPL / 4; ++c) {
+        const uint4 q = *reinterpret_cast<const uint4*>(st + m * KC::kCode + rd_off[c]);
+        const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int w = 4 * c + t;
+          half2_t cc[4];
+          unpack8(qw[t], m_lo, m_hi, cc);
+          const half4_t aa = half4_t{cc[0][0], cc[0][1], cc[2][0], cc[2][1]};
+          const half4_t ab = half4_t{cc[1][0], cc[1][1], cc[3][0], cc[3][1]};
+          acc[m][w / 8][0] = __builtin_amdgcn_mfma_f32_4x4x4f16(aa, xa[w], acc[m][w / 8][0], 0, 0, 0);
+          acc[m][w / 8][1] = __builtin_amdgcn_mfma_f32_4x4x4f16(ab, xb[w], acc[m][w / 8][1], 0, 0, 0);
         }
       }
     }
-    multi_reduce<V, LPR>(v, lane);
-    constexpr int CT = V / LPR > 1 ? V / LPR : 1;
-    // gate and up of one (unit, row) sit side by side when a lane keeps
-    // several totals, else in the lanes one last-halving distance apart
-    constexpr int kPartner = last_halving_distance<V, LPR>();
-    const bool writer = (lane & (kPartner - 1)) == 0;
+    // result register v of a lane: unit 4*ug + v against activation row i4,
+    // over K slice ks; apply the slice's group scales and biases
+    const uint16_t* sb = reinterpret_cast<const uint16_t*>(st + M * KC::kCode);
+    float val[V];  // index v * M + m
 #pragma unroll
-    for (int j = 0; j < CT; ++j) {
-      float gv = v[j], upv = 0.f;
-      const int idx = reduce_index<V, LPR>(lane, j);
+    for (int m = 0; m < M; ++m) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int so = (4 * ug + v) * G + ks * KC::GPL;
+        float tot = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < KC::GPL; ++gg) {
+          const float sc = bf16_to_f32(sb[(2 * m) * (KC::kSB / 2) + so + gg]);
+          const float bi = bf16_to_f32(sb[(2 * m + 1) * (KC::kSB / 2) + so + gg]);
+          const float dm = fmaf(acc[m][gg][1][v], 0.0625f, acc[m][gg][0][v]) - xc[gg];
+          tot = fmaf(sc, dm, fmaf(bi, xs[gg], tot));
+        }
+        val[v * M + m] = tot;
+      }
+    }
+    kred<DTOP, V, V>(val, lane);
+    constexpr int C = KC::NKS >= V ? 1 : V / KC::NKS;
+    constexpr int kLast = kred_last<V, DTOP>();
+    // lanes that differ only in the bits from 4 to below kLast hold the
+    // same totals: the one with those bits clear writes
+    const bool writer = (lane & (kLast - 1) & ~3) == 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      float gv = val[j], upv = 0.f;
+      const int idx = kred_index<V, DTOP>(lane, j);
       if (PAIR) {
-        if (CT > 1) {
+        // gate and up of one (unit, row) sit side by side when a lane keeps
+        // several totals, else in the lanes kLast apart
+        if constexpr (C > 1) {
           if (j % 2 == 1) continue;
-          upv = v[j + 1];
+          upv = val[j + 1];
         } else {
-          upv = pair_move<kPartner>(v[0], lane);
+          upv = xor_move<kLast>(val[0], lane);
           if (idx % 2 == 1) continue;
         }
       }
-      const int jl = idx / (R * M);
-      const int r = (idx / M) % R;
-      const int u = u0 + jl * UPW + sg;
-      if (!writer || u >= g.N) continue;
-      const int64_t o = static_cast<int64_t>(row0 + r) * g.N + u;
+      const int u = u0 + 4 * ug + idx / M;
+      if (!writer || i4 >= rows || u >= g.N) continue;
+      const int64_t o = static_cast<int64_t>(row0 + i4) * g.N + u;
       if (PAIR) {  // hidden activation, fp16 (saturating)
         float h = gv / (1.f + __expf(-gv)) * upv;
         h = fminf(fmaxf(h, -65504.f), 65504.f);
@@ -591,44 +636,28 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
       cache_e = e;
       cache_k = k;
     }
-    const uint8_t* st = ring + (t % NS) * SL::kBytes;
-    if (kRows == 4 && rows == 4) {
-      rows_pass(std::integral_constant<int, kRows>(), st, row0, u0);
-    } else if (kRows == 4 && rows == 3) {
-      // rows 0-1 as a pair, then row 2 alone (moved to slot 0)
-      rows_pass(std::integral_constant<int, 2>(), st, row0, u0);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) xp[0][q] = xp[2][q];
-      xs[0] = xs[2];
-      xc[0] = xc[2];
-      rows_pass(std::integral_constant<int, 1>(), st, row0 + 2, u0);
-      cache_e = -1;  // slot 0 no longer holds the chunk's first row
-    } else if (rows == 2) {
-      rows_pass(std::integral_constant<int, 2>(), st, row0, u0);
-    } else {
-      rows_pass(std::integral_constant<int, 1>(), st, row0, u0);
-    }
+    compute(ring + (t % NS) * SL::kBytes, row0, rows, u0);
   }
 }
 
-#define MOE_U4S_KERNEL(P, LPR)                                                  \
-  __global__ void __launch_bounds__(SCfg<P>::kThreads)                       \
-      u4s_kernel_##P##_##LPR(U4Args g) {                                      \
-    __shared__ __attribute__((aligned(16))) uint8_t smem[SCfg<P>::kLds];      \
-    u4_stream<P, LPR>(g, smem);                                               \
+#define MOE_U4S_KERNEL(P, K)                                                    \
+  __global__ void __launch_bounds__((SCfg<P, K>::kThreads))                   \
+      u4s_kernel_##P##_##K(U4Args g) {                                        \
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SCfg<P, K>::kLds];   \
+    u4_stream<P, K>(g, smem);                                                 \
   }
+MOE_U4S_KERNEL(true, 2048)
+MOE_U4S_KERNEL(true, 1024)
+MOE_U4S_KERNEL(true, 512)
+MOE_U4S_KERNEL(true, 256)
+MOE_U4S_KERNEL(true, 128)
 MOE_U4S_KERNEL(true, 64)
-MOE_U4S_KERNEL(true, 32)
-MOE_U4S_KERNEL(true, 16)
-MOE_U4S_KERNEL(true, 8)
-MOE_U4S_KERNEL(true, 4)
-MOE_U4S_KERNEL(true, 2)
+MOE_U4S_KERNEL(false, 2048)
+MOE_U4S_KERNEL(false, 1024)
+MOE_U4S_KERNEL(false, 512)
+MOE_U4S_KERNEL(false, 256)
+MOE_U4S_KERNEL(false, 128)
 MOE_U4S_KERNEL(false, 64)
-MOE_U4S_KERNEL(false, 32)
-MOE_U4S_KERNEL(false, 16)
-MOE_U4S_KERNEL(false, 8)
-MOE_U4S_KERNEL(false, 4)
-MOE_U4S_KERNEL(false, 2)
 #undef MOE_U4S_KERNEL
 
 int stream_grid() {
@@ -640,21 +669,24 @@ int stream_grid() {
   return cus;
 }
 
+// K is a power of two from 64 to 2048
+bool supported_k(int K) { return K >= 64 && K <= kMaxK && (K & (K - 1)) == 0; }
+
 template <bool PAIR>
 hipError_t launch_stream(int K, const U4Args& g, hipStream_t s) {
-  const dim3 grid(stream_grid()), block(SCfg<PAIR>::kThreads);
-#define MOE_U4S(L)                                                                   \
-  case L:                                                                            \
-    hipLaunchKernelGGL(PAIR ? u4s_kernel_true_##L : u4s_kernel_false_##L, grid, block, \
-                       0, s, g);                                                     \
+  const dim3 grid(stream_grid()), block(SCfg<PAIR, 64>::kThreads);
+#define MOE_U4S(KK)                                                                    \
+  case KK:                                                                             \
+    hipLaunchKernelGGL(PAIR ? u4s_kernel_true_##KK : u4s_kernel_false_##KK, grid, block, \
+                       0, s, g);                                                       \
     break;
-  switch (pick_lpr(K)) {
+  switch (K) {
+    MOE_U4S(2048)
+    MOE_U4S(1024)
+    MOE_U4S(512)
+    MOE_U4S(256)
+    MOE_U4S(128)
     MOE_U4S(64)
-    MOE_U4S(32)
-    MOE_U4S(16)
-    MOE_U4S(8)
-    MOE_U4S(4)
-    MOE_U4S(2)
     default:
       return hipErrorInvalidValue;
   }
@@ -668,15 +700,14 @@ hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
                          const int32_t* sorted_token, const void* x,
                          const moe_expert_weights& w, void* H, void* Y,
                          hipStream_t s) {
-  if (D.d > kMaxK || D.F > kMaxK || !D.swiglu || group != 64 || D.E > kMaxExperts ||
-      D.d != 32 * pick_lpr(D.d) || D.F != 32 * pick_lpr(D.F))
+  if (!supported_k(D.d) || !supported_k(D.F) || !D.swiglu || group != 64 ||
+      D.E > kMaxExperts)
     return hipErrorInvalidValue;
   // item numbers and item costs are 32-bit: row chunks (at most T*k/4 + E)
-  // times unit blocks per expert, times the cost of an item
-  const int64_t chunks = D.slots / std::min(SCfg<true>::kRows, SCfg<false>::kRows) + D.E;
-  // unit blocks are >= kSub units
-  const int64_t blocks =
-      std::max(D.F, D.d) / std::min(SCfg<true>::kSub, SCfg<false>::kSub) + 1;
+  // times unit blocks per expert (at least 4 units each), times the cost of
+  // an item
+  const int64_t chunks = D.slots / kMaxChunkRows + D.E;
+  const int64_t blocks = std::max(D.F, D.d) / 4 + 1;
   if (chunks * blocks * (kItemCost + kMaxChunkRows) > INT32_MAX) return hipErrorInvalidValue;
   const int64_t words_d = D.d / 8, groups_d = D.d / 64;
   U4Args g{};
