@@ -410,22 +410,6 @@ grouped_gemm_kernel(GemmArgs g) {
   if (KT > 1) issue(1, 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (m0 + wm * (MB * 32) >= cnt) {
-    // every row of this wave's half of the tile lies past the group (the
-    // group's last tile holds at most BM/2 rows): no products, only this
-    // wave's share of the loads and the same barriers as the other waves,
-    // so the other wave on its SIMD has the matrix core to itself
-    for (int kt = 0; kt + 2 < KT; ++kt) {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-      __syncthreads();
-      issue(kt + 2, kt & 1);
-    }
-    if (KT > 1) {
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
-    return;  // its output rows are not stored
-  }
   read_frags(0, 0, 0);
   convert(0);
   for (int kt = 0; kt + 2 < KT; ++kt) tile(kt, std::integral_constant<int, 0>{});
