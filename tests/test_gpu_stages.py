@@ -42,13 +42,20 @@ MEDIUM = {
     # 4-bit affine weights, decode-shaped; K % 128 == 0 and == 64 variants
     "u4-decode": C("u4-decode", 109, T=20, d=512, E=64, top_k=4, F=256, weight_dtype=synth.U4),
     "u4-small-k": C("u4-small-k", 110, T=37, d=256, E=16, top_k=2, F=64, weight_dtype=synth.U4),
-    # 4-bit weights with 64 rows per expert (32 two-row chunks each, weights
+    # 4-bit weights with 64 rows per expert (16 four-row chunks each, weights
     # streamed once per chunk) and the largest expert count (1024 experts,
     # 64 of them touched at most)
     "u4-many-rows": C("u4-many-rows", 116, T=256, d=256, E=8, top_k=2, F=128,
                       weight_dtype=synth.U4),
     "u4-1024-experts": C("u4-1024-experts", 117, T=8, d=64, E=1024, top_k=8, F=64,
                          weight_dtype=synth.U4),
+    # the other reduction lengths of the 4-bit kernels: gate/up over
+    # K = 1024 and 128, down over K = 2048 and 1024 (1, 2, 8 and 16 K slices
+    # per unit group)
+    "u4-k1024-f2048": C("u4-k1024-f2048", 118, T=24, d=1024, E=8, top_k=2, F=2048,
+                        weight_dtype=synth.U4),
+    "u4-k128-f1024": C("u4-k128-f1024", 119, T=40, d=128, E=16, top_k=3, F=1024,
+                       weight_dtype=synth.U4),
     # fp32 path, SwiGLU and a shared expert
     "f32-swiglu-shared": C("f32-swiglu-shared", 111, T=150, d=48, E=5, top_k=2, F=40,
                            act_dtype=synth.F32, weight_dtype=synth.F32, shared_experts=2,
