@@ -305,15 +305,23 @@ struct U4Args {
   int rstride;                  // rows from one expert's matrix to the next
 };
 
-// exclusive prefix over the lanes of a wave, and the wave total
+// exclusive prefix over the lanes of a wave, and the wave total: an
+// inclusive scan inside each row of 16 lanes by DPP row shifts (a lane
+// without a source lane reads 0), then the totals of the rows before this
+// one from three lane reads
 __device__ __forceinline__ int wave_prefix(int v, int lane, int& total) {
   int inc = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(inc, d, 64);
-    if (lane >= d) inc += o;
-  }
-  total = __shfl(inc, 63, 64);
+  inc += dpp_i<0x111>(inc);  // row_shr:1
+  inc += dpp_i<0x112>(inc);  // row_shr:2
+  inc += dpp_i<0x114>(inc);  // row_shr:4
+  inc += dpp_i<0x118>(inc);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(inc, 15);
+  const int r1 = __builtin_amdgcn_readlane(inc, 31);
+  const int r2 = __builtin_amdgcn_readlane(inc, 47);
+  const int r3 = __builtin_amdgcn_readlane(inc, 63);
+  const int row = lane >> 4;
+  inc += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+  total = r0 + r1 + r2 + r3;
   return inc - v;
 }
 
