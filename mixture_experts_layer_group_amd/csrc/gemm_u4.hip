@@ -167,6 +167,9 @@ struct SCfg {
   static constexpr int kWaves = PAIR ? 8 : 16;
   static constexpr int kRows = kMaxChunkRows;
   static constexpr int kStages = 2;
+  // an item is read into registers as soon as it arrives (frees its stage
+  // one item earlier; needs about 50 VGPRs that the 16-wave down kernel lacks)
+  static constexpr bool kRegs = PAIR;
   static constexpr int M = PAIR ? 2 : 1;
   static constexpr int kBytes = M * KC::kCode + 2 * M * KC::kSB;  // one stage
   static constexpr int kLoads = M * KC::kDma + 2 * M;  // load instructions per item
@@ -550,7 +553,33 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
     }
   };
 
-  // the item in stage st: units u0.. of the expert, chunk rows row0..
+  // kRegs: an item's codes and its group scales and biases, read out of its
+  // stage into registers, so that the stage can take the next load before
+  // the item is computed (otherwise they are read from the stage as it goes)
+  uint4 rq[M][KC::WPL / 4];
+  uint32_t rsc[M][4][KC::GPL], rbi[M][4][KC::GPL];
+  auto fetch = [&](const uint8_t* st) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int c = 0; c < KC::WPL / 4; ++c)
+        rq[m][c] = *reinterpret_cast<const uint4*>(st + m * KC::kCode + rd_off[c]);
+    const uint16_t* sb = reinterpret_cast<const uint16_t*>(st + M * KC::kCode);
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int so = (4 * ug + v) * G + ks * KC::GPL;
+#pragma unroll
+        for (int gg = 0; gg < KC::GPL; ++gg) {
+          rsc[m][v][gg] = sb[(2 * m) * (KC::kSB / 2) + so + gg];
+          rbi[m][v][gg] = sb[(2 * m + 1) * (KC::kSB / 2) + so + gg];
+        }
+      }
+  };
+
+  // the item in stage st (fetched with kRegs): units u0.. of the expert,
+  // chunk rows row0..
   auto compute = [&](const uint8_t* st, int row0, int rows, int u0) {
     float4_t acc[M][KC::GPL][2];
 #pragma unroll
@@ -562,7 +591,11 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
     for (int m = 0; m < M; ++m) {
 #pragma unroll
       for (int c = 0; c < KC::WPL / 4; ++c) {
-        const uint4 q = *reinterpret_cast<const uint4*>(st + m * KC::kCode + rd_off[c]);
+        uint4 q;
+        if constexpr (SL::kRegs)
+          q = rq[m][c];
+        else
+          q = *reinterpret_cast<const uint4*>(st + m * KC::kCode + rd_off[c]);
         const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -588,8 +621,10 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
         float tot = 0.f;
 #pragma unroll
         for (int gg = 0; gg < KC::GPL; ++gg) {
-          const float sc = bf16_to_f32(sb[(2 * m) * (KC::kSB / 2) + so + gg]);
-          const float bi = bf16_to_f32(sb[(2 * m + 1) * (KC::kSB / 2) + so + gg]);
+          const uint32_t sw = SL::kRegs ? rsc[m][v][gg] : sb[(2 * m) * (KC::kSB / 2) + so + gg];
+          const uint32_t bw = SL::kRegs ? rbi[m][v][gg] : sb[(2 * m + 1) * (KC::kSB / 2) + so + gg];
+          const float sc = __uint_as_float(sw << 16);
+          const float bi = __uint_as_float(bw << 16);
           const float dm = fmaf(acc[m][gg][1][v], 0.0625f, acc[m][gg][0][v]) - xc[gg];
           tot = fmaf(sc, dm, fmaf(bi, xs[gg], tot));
         }
@@ -631,16 +666,35 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
   };
 
   int cache_e = -1, cache_k = -1;
-  for (int t = 0; t < NS - 1 && t < n; ++t) issue(t);
+  // With kRegs the item is read into registers as soon as it has arrived
+  // and its stage takes the load of the item NS ahead at once, so NS items
+  // are in flight while one is computed; without, the stage of item t-1
+  // takes the item NS-1 ahead.
+  constexpr int AHEAD = SL::kRegs ? NS : NS - 1;
+  for (int t = 0; t < AHEAD && t < n; ++t) issue(t);
   for (int t = 0; t < n; ++t) {
-    if (t + NS - 1 < n) issue(t + NS - 1);  // into the stage freed by item t-1
+    if constexpr (!SL::kRegs) {
+      if (t + NS - 1 < n) issue(t + NS - 1);  // into the stage freed by item t-1
+    }
     wait_later<L, NS>(min(NS - 1, n - 1 - t));
+    if constexpr (SL::kRegs) {
+      fetch(ring + (t % NS) * SL::kBytes);
+      if (t + NS < n) {
+        // the stage's reads must have returned before its next load lands
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(t + NS);
+      }
+    }
     const int a = ca, k = ck;
     const int u0 = cb * UPI;
     advance(ca, ck, cb);
     const int e = __builtin_amdgcn_readfirstlane(act_e[a]);
-    const int row0 = __builtin_amdgcn_readfirstlane(g.offsets[e]) + k * kRows;
-    const int rows = min(kRows, __builtin_amdgcn_readfirstlane(g.offsets[e + 1]) - row0);
+    // the offsets are read through the constant address space: a scalar
+    // load, which leaves the direct loads in flight alone (a vector load here
+    // would make the compiler wait for every pending load of the wave)
+    const auto* offs = (const __attribute__((address_space(4))) int32_t*)(g.offsets);
+    const int row0 = offs[e] + k * kRows;
+    const int rows = min(kRows, offs[e + 1] - row0);
     if (cache_e != e || cache_k != k) {
       load_rows(row0, rows);
       cache_e = e;
