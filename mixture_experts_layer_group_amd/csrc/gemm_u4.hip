@@ -148,10 +148,13 @@ struct KCfg {
 // to 4 of the expert's rows (the 4 columns of every MFMA block), so an
 // expert with more than 4 rows streams its weights once per chunk.  A wave
 // is an independent pipeline over a private ring of NS stages in LDS: the
-// direct-to-LDS loads of the item NS-1 ahead are issued before the current
-// item is computed, so NS-1 items per wave are always in flight, and the
-// only wait is the wave's own vmcnt.  The buffer descriptors carry each
-// expert matrix's size, so a load past the last unit fetches nothing.
+// direct-to-LDS loads of later items are issued before the current item is
+// computed (NS-1 of them; NS on the gate/up product, which copies an item
+// into registers as soon as it arrives and reloads its stage at once), and
+// the only wait is the wave's own vmcnt.  Inside the loop no other vector
+// load is waited for except when a new row chunk's activations are read.
+// The buffer descriptors carry each expert matrix's size, so a load past
+// the last unit fetches nothing.
 constexpr int kItemCost = 12;    // cost of an item beyond its rows, in rows
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxChunkRows = 4;
@@ -159,8 +162,9 @@ constexpr int kMaxChunkRows = 4;
 // Per product: one workgroup per CU of 8 (gate/up) or 16 (down) waves, two
 // stages per wave: 144 KiB of ring for the decode shapes (K = 2048 and 512).
 // Measured on the decode layer: the down kernel with 16 waves beats 8 waves
-// with 4 stages by 3%; fewer waves with deeper rings (4 x 4, 4 x 8) are
-// slower by a quarter or more.
+// with 3 or 4 stages (with or without the register copy) and 12 waves by
+// 1-4%; fewer waves with deeper rings (4 x 4, 4 x 8) are slower by a
+// quarter or more.
 template <bool PAIR, int K>
 struct SCfg {
   using KC = KCfg<K>;
