@@ -390,16 +390,22 @@ grouped_gemm_kernel(GemmArgs g) {
       // of this tile's last MFMAs, and start the loads of the tile after it
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __syncthreads();
+      // down projection: the waves that leave the barrier first issue the
+      // next loads and their last sub-step at raised priority (5% faster on
+      // the Mixtral-shaped layer; the gate/up product is 1% slower with it)
+      if constexpr (MODE == kDown) __builtin_amdgcn_s_setprio(1);
       read_frags(cur ^ 1, 0, 0);
       if constexpr (kind == 0) {
         issue(kt + 2, cur);
         mfmas(1);
         convert(0);
         pace_loads();
+        if constexpr (MODE == kDown) __builtin_amdgcn_s_setprio(0);
       } else {
         mfmas(1);
         convert(0);
         pace();
+        if constexpr (MODE == kDown) __builtin_amdgcn_s_setprio(0);
       }
     } else {
       mfmas(1);
