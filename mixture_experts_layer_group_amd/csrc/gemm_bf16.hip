@@ -117,7 +117,13 @@ __device__ __forceinline__ int largest_le(const int32_t* __restrict__ p, int E,
   return lo;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
+// silu with the hardware reciprocal (about 1 ulp of fp32) instead of an
+// IEEE division: H is rounded to fp16 right after, 2^-11 relative, far above
+// that error, and the epilogue of a tile runs 64 of these per lane.
+// Large negative z: exp overflows to inf, the reciprocal gives 0, silu -> -0.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
+}
 
 // hidden activation -> fp16, round to nearest even, saturating at +-65504
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
