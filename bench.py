@@ -7,11 +7,15 @@ in HBM.  The default workload is the Mixtral-shaped layer (T=4096 tokens,
 d=4096, 8 experts, top-2, SwiGLU FFN 14336, bf16 with fp32 accumulation,
 fp32 router, no capacity limit).
 
-Printed: ONE JSON line with tokens/s (value), the grouped expert GEMM
-TFLOP/s and its fraction of the bf16 matrix-core peak, a roofline object for
-the grouped FFN (both expert GEMMs, timed per call with HIP events on the
-stream they run on), and the CPU oracle timed on a bounded sample of the same
-workload (cpu_baseline).
+Printed: ONE JSON line with tokens/s (value); the grouped expert GEMM
+TFLOP/s (gate/up + down, both launches as the layer issues them) and its
+fraction of the bf16 matrix-core peak; a roofline object for the dominant
+kernel (the gate/up grouped GEMM; the 4-bit FFN against HBM on the decode
+workload); a `decode` object from the decode-shaped 4-bit layer timed in the
+same run (its HBM roofline); and the CPU oracle timed on a bounded sample of
+the same workload (cpu_baseline).  Every kernel time comes from HIP events
+that moe_layer_forward records on its own stream inside the timed steps
+(moe_layer_stats.ffn_events).
 """
 from __future__ import annotations
 
@@ -58,14 +62,13 @@ def expert_flops(cfg, n_kept: int) -> float:
     return f
 
 
-# sources of the kernels one grouped-FFN call runs (tile prefix, both expert
-# GEMMs, the fold of a split down projection; the two 4-bit kernels): a
-# traffic summary measured on other sources is stale
-TRAFFIC_SOURCES = {"bf16": ("csrc/gemm_bf16.hip", "csrc/dispatch.hip", "csrc/combine.hip"),
-                   "u4": ("csrc/gemm_u4.hip",)}
+# sources of the kernels whose HBM traffic the roofline quotes (the bf16
+# grouped GEMMs; the two 4-bit kernels): a traffic summary measured on other
+# sources is stale
+TRAFFIC_SOURCES = {"bf16": ("csrc/gemm_bf16.hip",), "u4": ("csrc/gemm_u4.hip",)}
 COPY_BYTES = 1 << 30  # calibration kernel: reads and writes 1 GiB
-# counters are collected for the calibration copy and the FFN kernels only
-TRAFFIC_REGEX = "neg_kernel|grouped_gemm|tile_prefix|fold_split|u4s_kernel"
+# counters are collected for the calibration copy and the expert kernels only
+TRAFFIC_REGEX = "neg_kernel|grouped_gemm|u4s_kernel"
 
 
 def sources_digest(weight_dtype: str = "bf16") -> str:
@@ -77,27 +80,149 @@ def sources_digest(weight_dtype: str = "bf16") -> str:
 
 
 def traffic_summary_path(workload: str) -> str:
-    return os.path.join(ROOT, "profiles", f"grouped_ffn_{workload}_hbm_traffic.md")
+    return os.path.join(ROOT, "profiles", f"expert_gemms_{workload}_hbm_traffic.md")
 
 
-def measured_traffic(workload: str, weight_dtype: str = "bf16"):
-    """HBM bytes per grouped-FFN call from the committed counter summary, or
-    None when there is none or it was taken on other kernel sources."""
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes (read + written) per layer call of the expert kernels whose
+    name contains `kernel`, from the committed counter summary; None when
+    there is none or it was taken on other kernel sources."""
     path = traffic_summary_path(workload)
     if not os.path.exists(path):
         return None
-    vals = {}
+    digest, total, found = None, 0.0, False
     with open(path) as f:
         for line in f:
-            if line.startswith("- ") and ": " in line:
-                k, v = line[2:].strip().split(": ", 1)
-                vals[k.strip("`")] = v.strip().strip("`")
-    if vals.get("sources_sha256") != sources_digest(weight_dtype):
+            if line.startswith("- sources_sha256: "):
+                digest = line.split(": ", 1)[1].strip()
+            elif line.startswith("- per_call[") and "]: " in line:
+                key, v = line[len("- per_call["):].rsplit("]: ", 1)
+                if kernel in key:
+                    total += float(v)
+                    found = True
+    wd = "u4" if "u4s" in kernel else "bf16"
+    if digest != sources_digest(wd) or not found:
         return None
-    try:
-        return float(vals["bytes_per_call"])
-    except (KeyError, ValueError):
-        return None
+    return total
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch already loaded (ctypes),
+    for the library to record on its stream."""
+
+    def __init__(self, n: int):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(h.value)
+
+    def ms(self, a: int, b: int) -> float:
+        t = self.ct.c_float()
+        self.hip.hipEventSynchronize(self.ev[b])
+        if self.hip.hipEventElapsedTime(self.ct.byref(t), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
+def time_layer(torch, moe, cfg, steps: int, warmup: int, n_rep: int):
+    """Warm-up, then two timed passes of `steps` moe_layer_forward calls of
+    workload `cfg`, rotating through `n_rep` independently drawn input
+    copies: the first, plain, gives the per-step layer time (torch events
+    around the loop, nothing else recorded); the second has the layer record
+    HIP events around its expert kernels (moe_layer_stats.ffn_events), which
+    give the gate/up and down (+ shared) kernel times of every step.
+    Also returns kept rows and touched experts of each copy."""
+    import synth
+    reps = [synth.make_layer_inputs(cfg, "cuda", base=synth.SEED_BASE + r)
+            for r in range(n_rep)]
+    spec = moe.spec_from_config(cfg)
+    T = cfg.T
+    odt = torch.bfloat16 if cfg.out_dtype == "bf16" else torch.float32
+    out = torch.empty((T, cfg.d), dtype=odt, device="cuda")
+    ws = moe.workspace(spec, T)
+    wts = [moe.expert_weights(r) for r in reps]
+    offs = [torch.empty(cfg.E + 1, dtype=torch.int32, device="cuda") for _ in reps]
+    ev = HipEvents(3 * steps)
+    plain = [moe.layer_stats(offsets=o) for o in offs]
+    timed = [moe.layer_stats(offsets=offs[i % n_rep],
+                             ffn_events=ev.ev[3 * i:3 * i + 3]) for i in range(steps)]
+
+    def step(i, st):
+        r = i % n_rep
+        moe.moe_layer_forward(spec, T, reps[r]["x"], reps[r]["w_router"],
+                              reps[r]["expert_bias"], wts[r], out, stats=st, workspace=ws)
+
+    def timed_pass(stats_of):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            step(i, stats_of(i))
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, time.perf_counter() - t0
+
+    for i in range(max(warmup, n_rep)):
+        step(i, plain[i % n_rep])
+    ms_step, wall = timed_pass(lambda i: plain[i % n_rep])
+    ms_step_ev, _ = timed_pass(lambda i: timed[i])
+    up = [ev.ms(3 * i, 3 * i + 1) for i in range(steps)]
+    down = [ev.ms(3 * i + 1, 3 * i + 2) for i in range(steps)]
+    ev.close()
+    kept = [int(o[-1].item()) for o in offs]
+    touched = [int((o[1:] - o[:-1] > 0).sum().item()) for o in offs]
+    return {"ms_step": ms_step, "ms_step_events": ms_step_ev, "wall": wall, "up": up,
+            "down": down, "kept": kept, "touched": touched, "inp": reps[0]}
+
+
+def decode_leg(torch, moe, steps: int, warmup: int):
+    """The decode-shaped 4-bit layer (T=32, d=2048, 256 experts, top-8,
+    SwiGLU 512), timed like the headline workload over three rotated input
+    copies (its ~290 MB of touched weights would otherwise sit in the
+    256 MB last-level cache between steps); HBM roofline of the layer and of
+    its two 4-bit expert kernels."""
+    import synth
+    cfg = synth.CONFIGS[5]
+    n_rep = 3
+    r = time_layer(torch, moe, cfg, steps, warmup, n_rep)
+    ffn = [a + b for a, b in zip(r["up"], r["down"])]
+
+    def ffn_bytes(j):
+        return (r["touched"][j] * u4_expert_bytes(cfg) + cfg.T * cfg.d * 2
+                + r["kept"][j] * cfg.d * 4)
+    byts = sum(ffn_bytes(i % n_rep) for i in range(steps)) / steps
+    ffn_ms = sum(ffn) / len(ffn)
+    layer_bytes = byts + cfg.E * cfg.d * 4 + cfg.T * cfg.d * 4
+    return {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.top_k,
+            "F": cfg.F, "weights": "u4-affine-g64", "steps": steps,
+            "input_copies_rotated": n_rep,
+            "layer_us": r["ms_step"] * 1e3, "tokens_per_s": cfg.T / (r["ms_step"] / 1e3),
+            "layer_us_with_events": r["ms_step_events"] * 1e3,
+            "ffn_us": ffn_ms * 1e3, "ffn_up_us": sum(r["up"]) / steps * 1e3,
+            "ffn_down_us": sum(r["down"]) / steps * 1e3,
+            "touched_experts": r["touched"],
+            "ffn_bytes_per_call": byts,
+            "ffn_hbm_gbs": byts / (ffn_ms / 1e3) / 1e9,
+            "ffn_frac_hbm": byts / (ffn_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "layer_bytes": layer_bytes,
+            "layer_hbm_gbs": layer_bytes / (r["ms_step"] / 1e3) / 1e9,
+            "layer_frac_hbm": layer_bytes / (r["ms_step"] / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "peak_hbm_gbs": PEAK_HBM_GBS}
 
 
 def _cpu_model() -> str:
@@ -170,8 +295,10 @@ def main() -> int:
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens whose expert FFN the CPU oracle evaluates")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the decode-shaped 4-bit layer's object")
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="run a 1 GiB copy and three grouped-FFN calls, for rocprofv3 --pmc")
+                    help="run a 1 GiB copy and three layer calls, for rocprofv3 --pmc")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two --pmc runs of --traffic-probe into the profiles/ summary")
     args = ap.parse_args()
@@ -189,92 +316,50 @@ def main() -> int:
     torch.cuda.set_device(0)
     cfg = synth.CONFIGS[args.config]
     u4 = cfg.weight_dtype == "u4"
+    if args.traffic_probe:
+        return traffic_probe(torch, moe, cfg)
     # the 4-bit decode layer touches ~290 MB of weights, about the size of
     # the 256 MB last-level cache: its timed steps rotate through three
     # independently drawn copies of the inputs (1.4 GB) so no step finds the
     # previous step's weights cached; larger layers exceed the cache anyway
     n_rep = 3 if u4 else 1
-    reps = [synth.make_layer_inputs(cfg, "cuda", base=synth.SEED_BASE + r)
-            for r in range(n_rep)]
-    inp = reps[0]
-    spec = moe.spec_from_config(cfg)
+    r = time_layer(torch, moe, cfg, args.steps, args.warmup, n_rep)
     T = cfg.T
-    odt = torch.bfloat16 if cfg.out_dtype == "bf16" else torch.float32
-    out = torch.empty((T, cfg.d), dtype=odt, device="cuda")
-    ws = moe.workspace(spec, T)
-    ws_all = [moe.expert_weights(r) for r in reps]
-    w = ws_all[0]
-    dev = "cuda"
-    offs_all = [torch.empty(cfg.E + 1, dtype=torch.int32, device=dev) for _ in reps]
-    st_all = [torch.empty(T * cfg.top_k, dtype=torch.int32, device=dev) for _ in reps]
-    stats_all = [moe.layer_stats(offsets=o, sorted_token=t) for o, t in zip(offs_all, st_all)]
-    offsets, sorted_token = offs_all[0], st_all[0]
-
-    def step(i=0):
-        r = i % n_rep
-        moe.moe_layer_forward(spec, T, reps[r]["x"], reps[r]["w_router"],
-                              reps[r]["expert_bias"], ws_all[r], out, stats=stats_all[r],
-                              workspace=ws)
-
-    if args.traffic_probe:
-        return traffic_probe(torch, moe, spec, cfg, inp, w, offsets, sorted_token, ws, step)
-
-    for i in range(max(args.warmup, n_rep)):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = r["ms_step"]
     tokens_per_s = T / (ms_step / 1e3)
-
-    # the grouped expert FFN alone (both GEMMs), each call timed with HIP
-    # events on the stream the kernels run on (rotating copies as above)
-    kept = [int(o[-1].item()) for o in offs_all]
-    touched = [int((o[1:] - o[:-1] > 0).sum().item()) for o in offs_all]
+    steps = args.steps
+    up_ms = sum(r["up"]) / steps
+    down_ms = sum(r["down"]) / steps
+    ffn_times = [a + b for a, b in zip(r["up"], r["down"])]
+    ffn_ms = sum(ffn_times) / steps
+    kept = r["kept"]
     n_kept = kept[0]
-    y = torch.empty((T * cfg.top_k, cfg.d), dtype=torch.float32, device=dev)
-    ysh = (torch.empty((cfg.shared_experts * T, cfg.d), dtype=torch.float32, device=dev)
-           if cfg.shared_experts else None)
-
-    def ffn(i):
-        r = i % n_rep
-        moe.moe_grouped_ffn(spec, T, offs_all[r], st_all[r], reps[r]["x"], ws_all[r], y, ysh,
-                            ws)
-
-    for i in range(max(2, n_rep)):
-        ffn(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i, (a, b) in enumerate(evs):
-        a.record()
-        ffn(i)
-        b.record()
-    torch.cuda.synchronize()
-    ffn_times = [a.elapsed_time(b) for a, b in evs]
-    ffn_ms = sum(ffn_times) / len(ffn_times)
-    flops = sum(expert_flops(cfg, kept[i % n_rep]) for i in range(args.steps)) / args.steps
+    flops = sum(expert_flops(cfg, kept[i % n_rep]) for i in range(steps)) / steps
     tflops = flops / (ffn_ms / 1e3) / 1e12
+    mats = 3 if cfg.act == "swiglu" else 2
+    up_flops = sum(2.0 * (mats - 1) * cfg.d * cfg.F * kept[i % n_rep]
+                   for i in range(steps)) / steps
+    up_tflops = up_flops / (up_ms / 1e3) / 1e12
+    if cfg.act_dtype == "f32":
+        dtype = "f32"
+    elif u4:
+        dtype = "bf16 x u4-affine (codes as exact fp16 on the matrix cores), fp32 accumulate"
+    else:
+        dtype = "bf16 (gate/up products), fp16 (down products: fp16 hidden x bf16 weights converted to fp16), fp32 accumulate"
 
     res = {
         "metric": METRIC,
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
-        "wall_s": wall,
+        "wall_s": r["wall"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.act_dtype if cfg.weight_dtype != "u4" else "bf16+u4",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "d": cfg.d, "E": cfg.E,
                    "top_k": cfg.top_k, "F": cfg.F, "router": cfg.router,
@@ -283,63 +368,71 @@ def main() -> int:
                    "weights": cfg.weight_dtype, "parallelism": "none (1 GPU)"},
         "grouped_gemm_tflops": tflops,
         "grouped_gemm_frac_peak": tflops / PEAK_BF16_TFLOPS,
+        "grouped_gemm": {"kernels": "routed gate/up GEMM + down GEMM (+ shared expert "
+                         "GEMMs), timed between HIP events the layer records around them "
+                         "in every step of a second timed pass", "flops_per_step": flops,
+                         "layer_ms_per_step_with_events": r["ms_step_events"],
+                         "avg_ms": ffn_ms, "median_ms": _median(ffn_times),
+                         "min_ms": min(ffn_times), "up_avg_ms": up_ms,
+                         "down_avg_ms": down_ms, "tflops": tflops,
+                         "frac_peak_bf16": tflops / PEAK_BF16_TFLOPS},
         "kept_rows": n_kept,
-        "roofline": {"bound": "mfma", "kernel": "grouped expert FFN call (tile prefix, "
-                     "GEMM1 gate/up + SwiGLU, GEMM2 down, split fold)", "achieved": tflops,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_BF16_TFLOPS, "flops_per_launch": flops,
-                     "avg_launch_ms": ffn_ms, "median_launch_ms": _median(ffn_times),
-                     "min_launch_ms": min(ffn_times), "traffic": measured_traffic(cfg.name)},
+        "roofline": {"bound": "mfma",
+                     "kernel": "grouped_gemm_kernel<SwiGLU> (routed gate/up GEMM + SwiGLU "
+                               "epilogue, the dominant kernel)",
+                     "achieved": up_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": up_tflops / PEAK_BF16_TFLOPS,
+                     "flops_per_launch": up_flops, "avg_launch_ms": up_ms,
+                     "median_launch_ms": _median(r["up"]), "min_launch_ms": min(r["up"]),
+                     "traffic": measured_traffic(cfg.name, "grouped_gemm_kernel<0, true>")},
     }
     if u4:
-        # bound by HBM: the touched experts' packed weights, the token rows
-        # read and the fp32 expert rows written, per call (touched experts
-        # counted on each copy's own routing)
-        def ffn_bytes(r):
-            return (touched[r] * u4_expert_bytes(cfg) + T * cfg.d * 2 + kept[r] * cfg.d * 4)
-        byts = sum(ffn_bytes(i % n_rep) for i in range(args.steps)) / args.steps
+        def ffn_bytes(j):
+            return (r["touched"][j] * u4_expert_bytes(cfg) + T * cfg.d * 2
+                    + kept[j] * cfg.d * 4)
+        byts = sum(ffn_bytes(i % n_rep) for i in range(steps)) / steps
         gbs = byts / (ffn_ms / 1e3) / 1e9
-        res["roofline"] = {"bound": "hbm", "kernel": "grouped expert FFN call (both "
-                           "4-bit expert kernels)", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                           "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
-                           "bytes_per_launch": byts, "avg_launch_ms": ffn_ms,
-                           "median_launch_ms": _median(ffn_times),
+        res["roofline"] = {"bound": "hbm", "kernel": "both 4-bit expert kernels "
+                           "(u4s_kernel gate/up, down) as the layer issues them",
+                           "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch": byts,
+                           "avg_launch_ms": ffn_ms, "median_launch_ms": _median(ffn_times),
                            "min_launch_ms": min(ffn_times),
-                           "traffic": measured_traffic(cfg.name, "u4")}
-        # the whole layer against HBM: the FFN's bytes plus the router
-        # weights and the layer output
-        layer_bytes = byts + cfg.E * cfg.d * (4 if cfg.router_dtype == "f32" else 2) \
-            + T * cfg.d * (4 if cfg.out_dtype == "f32" else 2)
-        res["layer_hbm_gbs"] = layer_bytes / (ms_step / 1e3) / 1e9
-        res["touched_experts"] = touched
+                           "traffic": measured_traffic(cfg.name, "u4s_kernel")}
+        res["touched_experts"] = r["touched"]
         res["input_copies_rotated"] = n_rep
+    elif not args.no_decode:
+        res["decode"] = decode_leg(torch, moe, args.steps, args.warmup)
+    inp = r["inp"]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
     print(json.dumps(res), flush=True)
     return 0
 
 
-def traffic_probe(torch, moe, spec, cfg, inp, w, offsets, sorted_token, ws, step) -> int:
+def traffic_probe(torch, moe, cfg) -> int:
     """Kernels for the HBM-traffic counters: an elementwise negation that
     reads and writes COPY_BYTES (the calibration of FETCH_SIZE and
-    WRITE_SIZE), then three grouped-FFN calls on the routed batch."""
+    WRITE_SIZE), then three layer calls of the workload."""
+    import synth
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    step()  # routing and dispatch for the FFN calls
+    inp = synth.make_layer_inputs(cfg, "cuda")
+    spec = moe.spec_from_config(cfg)
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    ws = moe.workspace(spec, cfg.T)
     torch.cuda.synchronize()
     for _ in range(3):
         torch.neg(src, out=dst)
-    y = torch.empty((cfg.T * cfg.top_k, cfg.d), dtype=torch.float32, device="cuda")
-    ysh = (torch.empty((cfg.shared_experts * cfg.T, cfg.d), dtype=torch.float32,
-                       device="cuda") if cfg.shared_experts else None)
     for _ in range(3):
-        moe.moe_grouped_ffn(spec, cfg.T, offsets, sorted_token, inp["x"], w, y, ysh, ws)
+        moe.moe_layer_forward(spec, cfg.T, inp["x"], inp["w_router"], inp["expert_bias"],
+                              inp, out, workspace=ws)
     torch.cuda.synchronize()
     print("traffic probe done", flush=True)
     return 0
 
 
-FFN_KERNELS = ("grouped_gemm_kernel", "tile_prefix_kernel", "fold_split_kernel", "u4s_kernel")
+FFN_KERNELS = ("grouped_gemm_kernel", "u4s_kernel")
 
 
 def _counter_rows(d):
@@ -351,10 +444,10 @@ def _counter_rows(d):
 
 
 def summarize_traffic(args) -> int:
-    """profiles/ summary of HBM traffic per grouped-FFN call: FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch) of the FFN kernels, each scaled by the
-    ratio of the calibration kernel's known bytes to what the same counter
-    read for it."""
+    """profiles/ summary of HBM traffic per layer call of each expert kernel:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the ratio of
+    the calibration kernel's known bytes to what the same counter read for
+    it."""
     import synth
     cfg = synth.CONFIGS[args.config]
     res = {}
@@ -363,7 +456,7 @@ def summarize_traffic(args) -> int:
         copy_kib, ffn = [], {}
         rows = [r for r in _counter_rows(d) if r["Counter_Name"] == counter]
         copies = [r for r in rows if "neg_kernel" in r["Kernel_Name"]]
-        # the FFN calls are the dispatches after the last calibration copy
+        # the layer calls are the dispatches after the last calibration copy
         last_copy = max((int(r["Dispatch_Id"]) for r in copies), default=None)
         for r in copies:
             copy_kib.append(float(r["Counter_Value"]))
@@ -376,26 +469,20 @@ def summarize_traffic(args) -> int:
                     key = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
                     ffn.setdefault(key, []).append(float(r["Counter_Value"]))
         if not copy_kib or not ffn:
-            print(f"no calibration or FFN dispatches for {counter} in {d}", file=sys.stderr)
+            print(f"no calibration or expert-kernel dispatches for {counter} in {d}",
+                  file=sys.stderr)
             return 1
         factor = COPY_BYTES / (sum(copy_kib) / len(copy_kib) * 1024.0)
-        # per call: every FFN kernel's mean per dispatch times its dispatches per call
-        per_call = 0.0
-        per_kernel = {}
-        for k, vs in ffn.items():
-            calls = 3
-            kib = sum(vs) / calls
-            per_kernel[k] = kib * 1024.0 * factor
-            per_call += per_kernel[k]
-        res[counter] = {"factor": factor, "copy_kib": copy_kib, "per_call": per_call,
-                        "per_kernel": per_kernel}
-    total = res["FETCH_SIZE"]["per_call"] + res["WRITE_SIZE"]["per_call"]
+        # per layer call: every kernel's dispatches over the 3 calls
+        per_kernel = {k: sum(vs) / 3 * 1024.0 * factor for k, vs in ffn.items()}
+        res[counter] = {"factor": factor, "copy_kib": copy_kib, "per_kernel": per_kernel}
     path = traffic_summary_path(cfg.name)
     rel = os.path.relpath(path, ROOT)
+    kernels = sorted(set(res["FETCH_SIZE"]["per_kernel"]) | set(res["WRITE_SIZE"]["per_kernel"]))
     with open(path, "w") as f:
-        f.write(f"# HBM traffic of one grouped-FFN call, {cfg.name}\n\n")
+        f.write(f"# HBM traffic of the expert kernels per layer call, {cfg.name}\n\n")
         f.write("Commands (repository root, one MI355X; the probe runs a 1 GiB elementwise "
-                "negation for calibration, then three grouped-FFN calls):\n\n```\n")
+                "negation for calibration, then three layer calls):\n\n```\n")
         f.write("cd /tmp && export TMPDIR=/tmp\n")
         for c, dd in (("FETCH_SIZE", "pmc_fetch"), ("WRITE_SIZE", "pmc_write")):
             f.write(f"timeout -s KILL 120 rocprofv3 --kernel-include-regex '{TRAFFIC_REGEX}' "
@@ -405,17 +492,21 @@ def summarize_traffic(args) -> int:
                 "$REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write\n```\n\n")
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             r = res[c]
-            f.write(f"{c}: calibration read {sum(r['copy_kib']) / len(r['copy_kib']):.0f} KiB for "
-                    f"{COPY_BYTES >> 10} KiB moved, factor {r['factor']:.4f}\n\n")
-            f.write("| kernel | bytes per call (scaled) |\n|---|---|\n")
-            for k, b in sorted(res[c]["per_kernel"].items()):
-                f.write(f"| `{k}` | {b:.4g} |\n")
-            f.write("\n")
-        f.write(f"- fetch_bytes_per_call: {res['FETCH_SIZE']['per_call']:.6g}\n")
-        f.write(f"- write_bytes_per_call: {res['WRITE_SIZE']['per_call']:.6g}\n")
-        f.write(f"- bytes_per_call: {total:.6g}\n")
+            f.write(f"{c}: calibration read {sum(r['copy_kib']) / len(r['copy_kib']):.0f} KiB "
+                    f"for {COPY_BYTES >> 10} KiB moved, factor {r['factor']:.4f}\n\n")
+        f.write("| kernel | fetched bytes per call | written bytes per call |\n|---|---|---|\n")
+        for k in kernels:
+            f.write(f"| `{k}` | {res['FETCH_SIZE']['per_kernel'].get(k, 0.0):.4g} | "
+                    f"{res['WRITE_SIZE']['per_kernel'].get(k, 0.0):.4g} |\n")
+        f.write("\n")
+        for k in kernels:
+            tot = res["FETCH_SIZE"]["per_kernel"].get(k, 0.0) + \
+                res["WRITE_SIZE"]["per_kernel"].get(k, 0.0)
+            f.write(f"- per_call[{k}]: {tot:.6g}\n")
         f.write(f"- sources_sha256: {sources_digest(cfg.weight_dtype)}\n")
-    print(f"wrote {rel}: {total / 1e9:.3f} GB per call", flush=True)
+    total = sum(res["FETCH_SIZE"]["per_kernel"].values()) + \
+        sum(res["WRITE_SIZE"]["per_kernel"].values())
+    print(f"wrote {rel}: {total / 1e9:.3f} GB per layer call", flush=True)
     return 0
 
 

@@ -56,6 +56,28 @@ enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_U4_AFFINE = 2 };
  * two slices interleaved expert by expert), down separate. */
 enum { MOE_LAYOUT_SEPARATE = 0, MOE_LAYOUT_FUSED_GATE_UP = 1 };
 
+/* Data-dependent conditions found on the device.  Calls that take an
+ * `errors` word (device int32, or NULL when not wanted) OR these bits into
+ * it and never clear it, so one word can collect a whole sequence of calls:
+ * zero it before the first call whose conditions you want to see.  None of
+ * them stops the computation.  The dockyard_rl "Mixture-of-Experts" page
+ * ("Router replay (R3)") asks that a bad route be reported rather than
+ * silently mis-handled; these bits are how the device reports one.
+ *   MOE_FLAG_BAD_EXPERT_ID   moe_dispatch met an expert id outside [0,E);
+ *                            that slot is treated as dropped (slot_row -1)
+ *   MOE_FLAG_H_SATURATED     a hidden activation (silu(gate)*up, or the
+ *                            ReLU output) of the bf16 / 4-bit path was
+ *                            outside the fp16 range (or NaN) and was stored
+ *                            as +-65504
+ *   MOE_FLAG_NONFINITE_LOGIT a router logit was NaN or infinite (an input
+ *                            outside the contract; the routing of that
+ *                            token is then undefined) */
+enum {
+  MOE_FLAG_BAD_EXPERT_ID = 1,
+  MOE_FLAG_H_SATURATED = 2,
+  MOE_FLAG_NONFINITE_LOGIT = 4
+};
+
 /* Everything the math depends on; the subset of the Edge0 page's MoESpec
  * (and the blog page's MoEConfig) that changes results. */
 typedef struct moe_spec {
@@ -121,7 +143,14 @@ typedef struct moe_expert_weights {
  *   offsets [E+1] int32 (kept rows per expert, exclusive prefix),
  *   dropped [1] int32, prob_sum [E] fp32 (sum over tokens of the softmax
  *   probabilities; SOFTMAX_TOPK only),
- *   slot_row [T,k] int32, sorted_token [T*k] int32. */
+ *   slot_row [T,k] int32, sorted_token [T*k] int32,
+ *   errors [1] int32: MOE_FLAG_* bits of this call are OR-ed in (the word
+ *     is not cleared by the call).
+ * ffn_events: host pointer to three hipEvent_t (or NULL), recorded on the
+ *   stream right before the first expert-FFN kernel, between the routed
+ *   gate/up kernel and the routed down kernel, and right after the last
+ *   expert-FFN kernel (shared experts included) -- the expert GEMMs exactly
+ *   as this call issues them, for profiling. */
 typedef struct moe_layer_stats {
   int32_t* topk_ids;
   float* topk_w;
@@ -132,6 +161,8 @@ typedef struct moe_layer_stats {
   float* prob_sum;
   int32_t* slot_row;
   int32_t* sorted_token;
+  int32_t* errors;
+  void* const* ffn_events;
 } moe_layer_stats;
 
 /* hipStream_t, passed as an opaque pointer. */
@@ -168,7 +199,9 @@ moe_status moe_capacity(const moe_spec* spec, int64_t T, int64_t* cap_out);
  * same size is enough for every stage call below.  bytes: host. */
 moe_status moe_workspace_size(const moe_spec* spec, int64_t T, size_t* bytes);
 
-/* Router: logits L = x @ Wr^T in fp32 (fp32 accumulation, VALU), then
+/* Router: logits L = x @ Wr^T accumulated in fp32 on the vector ALUs (one
+ * fp32 FMA per term, so within the d-term dot-product error bound; the
+ * matrix cores are left to the expert GEMMs), then
  *  SOFTMAX_TOPK (Edge0 page, select_from_logits; blog page, route): the k
  *    most probable experts, highest first, ties to the lower index; weight
  *    p_i / sum of the kept p when norm_topk_prob, else p_i;
@@ -185,12 +218,13 @@ moe_status moe_workspace_size(const moe_spec* spec, int64_t T, size_t* bytes);
  *  logits     device out [T,E] fp32 or NULL
  *  prob_sum   device out [E] fp32 (sum over tokens of softmax p) or NULL;
  *             SOFTMAX_TOPK only, summed in a fixed order (deterministic)
+ *  errors     device [1] int32 or NULL: MOE_FLAG_NONFINITE_LOGIT is OR-ed in
  *  workspace  device, at least moe_workspace_size bytes */
 moe_status moe_route(const moe_spec* spec, int64_t T, const void* x,
                      const void* w_router, const float* expert_bias,
                      int32_t* topk_ids, float* topk_w, float* logits,
-                     float* prob_sum, void* workspace, size_t ws_bytes,
-                     moe_stream_t stream);
+                     float* prob_sum, int32_t* errors, void* workspace,
+                     size_t ws_bytes, moe_stream_t stream);
 
 /* Router replay (dockyard "Mixture-of-Experts" page, "Router replay (R3)"):
  * the expert ids of each token are given -- recorded when the tokens were
@@ -238,14 +272,17 @@ moe_status moe_route_forced(const moe_spec* spec, int64_t T, const void* x,
  *  dropped      device out [1] int32 = T*k - offsets[E]
  *  x, x_perm    optional: when both non-NULL, x_perm[r] = x[sorted_token[r]]
  *               ([T*k, d] act dtype; the blog page's permuted copy)
+ *  errors       device [1] int32 or NULL: MOE_FLAG_BAD_EXPERT_ID is OR-ed
+ *               in when a topk_ids value lies outside [0,E) (that slot is
+ *               dropped: slot_row -1, not counted in counts_pre)
  *  workspace    device, at least moe_workspace_size bytes */
 moe_status moe_dispatch(const moe_spec* spec, int64_t T,
                         const int32_t* topk_ids, const float* topk_w,
                         int32_t* counts_pre, int32_t* offsets,
                         int32_t* sorted_token, float* sorted_w,
                         int32_t* slot_row, int32_t* dropped, const void* x,
-                        void* x_perm, void* workspace, size_t ws_bytes,
-                        moe_stream_t stream);
+                        void* x_perm, int32_t* errors, void* workspace,
+                        size_t ws_bytes, moe_stream_t stream);
 
 /* Grouped expert FFN over the ragged expert groups (dockyard page,
  * "The pipeline", grouped GEMM; blog page third program's moe_forward):
@@ -262,12 +299,14 @@ moe_status moe_dispatch(const moe_spec* spec, int64_t T,
  *  x         device [T,d] act dtype
  *  weights   host struct of device pointers
  *  y_rows    device out [T*k, d] fp32 (rows >= offsets[E] untouched)
- *  y_shared  device out [S*T, d] fp32, or NULL when S = 0 */
+ *  y_shared  device out [S*T, d] fp32, or NULL when S = 0
+ *  errors    device [1] int32 or NULL: MOE_FLAG_H_SATURATED is OR-ed in */
 moe_status moe_grouped_ffn(const moe_spec* spec, int64_t T,
                            const int32_t* offsets, const int32_t* sorted_token,
                            const void* x, const moe_expert_weights* weights,
-                           void* y_rows, void* y_shared, void* workspace,
-                           size_t ws_bytes, moe_stream_t stream);
+                           void* y_rows, void* y_shared, int32_t* errors,
+                           void* workspace, size_t ws_bytes,
+                           moe_stream_t stream);
 
 /* Combine, dockyard page "The pipeline" (weighted scatter back) and blog
  * page third program (scatter-add; a token routed to k experts sums k

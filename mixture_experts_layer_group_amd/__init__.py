@@ -20,6 +20,10 @@ ROUTER = {"softmax_topk": 0, "sigmoid_group": 1}
 ACT = {"swiglu": 0, "relu": 1}
 DTYPE = {"f32": 0, "bf16": 1, "u4": 2}
 LAYOUT = {"separate": 0, "fused_gate_up": 1}
+# MOE_FLAG_* bits of the device error word
+FLAG_BAD_EXPERT_ID = 1
+FLAG_H_SATURATED = 2
+FLAG_NONFINITE_LOGIT = 4
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_INVALID_TOPK",
                 3: "MOE_ERR_CAPACITY_TOO_TIGHT", 4: "MOE_ERR_SHAPE",
                 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP", 7: "MOE_ERR_UNSUPPORTED"}
@@ -50,7 +54,7 @@ class MoEExpertWeights(ctypes.Structure):
 
 
 _S_FIELDS = ["topk_ids", "topk_w", "logits", "counts_pre", "offsets", "dropped",
-             "prob_sum", "slot_row", "sorted_token"]
+             "prob_sum", "slot_row", "sorted_token", "errors"]
 
 
 class MoEHealth(ctypes.Structure):
@@ -65,7 +69,7 @@ class MoEHealth(ctypes.Structure):
 
 
 class MoELayerStats(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in _S_FIELDS]
+    _fields_ = [(n, ctypes.c_void_p) for n in _S_FIELDS] + [("ffn_events", ctypes.c_void_p)]
 
 
 class MoEError(RuntimeError):
@@ -93,13 +97,13 @@ def library() -> ctypes.CDLL:
         lib.moe_spec_validate.argtypes = [sp, i64]
         lib.moe_capacity.argtypes = [sp, i64, ctypes.POINTER(ctypes.c_int64)]
         lib.moe_workspace_size.argtypes = [sp, i64, ctypes.POINTER(ctypes.c_size_t)]
-        lib.moe_route.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.moe_route.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.moe_route_forced.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          sz, vp]
         lib.moe_dispatch.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                     vp, sz, vp]
+                                     vp, vp, sz, vp]
         lib.moe_grouped_ffn.argtypes = [sp, i64, vp, vp, vp,
-                                        ctypes.POINTER(MoEExpertWeights), vp, vp, vp,
+                                        ctypes.POINTER(MoEExpertWeights), vp, vp, vp, vp,
                                         sz, vp]
         lib.moe_combine.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp]
         lib.moe_layer_forward.argtypes = [sp, i64, vp, vp, vp,
@@ -189,12 +193,18 @@ def expert_weights(w: Dict) -> MoEExpertWeights:
     return out
 
 
-def layer_stats(**tensors) -> MoELayerStats:
+def layer_stats(ffn_events=None, **tensors) -> MoELayerStats:
+    """``moe_layer_stats`` from device tensors keyed like the C struct;
+    ``ffn_events``: three hipEvent_t handles (ints) or None."""
     s = MoELayerStats()
     for k, v in tensors.items():
         if k not in _S_FIELDS:
             raise KeyError(k)
         setattr(s, k, _ptr(v))
+    if ffn_events is not None:
+        arr = (ctypes.c_void_p * 3)(*[int(e) for e in ffn_events])
+        s._events_keepalive = arr
+        s.ffn_events = ctypes.cast(arr, ctypes.c_void_p)
     return s
 
 
@@ -217,12 +227,13 @@ def moe_workspace_size(spec: MoESpec, T: int) -> int:
 
 
 def moe_route(spec, T, x, w_router, expert_bias, topk_ids, topk_w, logits=None,
-              prob_sum=None, workspace=None, ws_bytes=None, stream=None) -> None:
+              prob_sum=None, workspace=None, ws_bytes=None, stream=None,
+              errors=None) -> None:
     ws_bytes = ws_bytes if ws_bytes is not None else (workspace.numel() if workspace is not None else 0)
     _check(library().moe_route(ctypes.byref(spec), T, _ptr(x), _ptr(w_router),
                                _ptr(expert_bias), _ptr(topk_ids), _ptr(topk_w),
-                               _ptr(logits), _ptr(prob_sum), _ptr(workspace),
-                               ws_bytes, _stream(stream)), "moe_route")
+                               _ptr(logits), _ptr(prob_sum), _ptr(errors),
+                               _ptr(workspace), ws_bytes, _stream(stream)), "moe_route")
 
 
 def moe_route_forced(spec, T, x, w_router, forced_ids, topk_ids, topk_w, rejected,
@@ -238,23 +249,25 @@ def moe_route_forced(spec, T, x, w_router, forced_ids, topk_ids, topk_w, rejecte
 
 def moe_dispatch(spec, T, topk_ids, topk_w, counts_pre, offsets, sorted_token,
                  sorted_w, slot_row, dropped, x=None, x_perm=None, workspace=None,
-                 ws_bytes=None, stream=None) -> None:
+                 ws_bytes=None, stream=None, errors=None) -> None:
     ws_bytes = ws_bytes if ws_bytes is not None else (workspace.numel() if workspace is not None else 0)
     _check(library().moe_dispatch(ctypes.byref(spec), T, _ptr(topk_ids), _ptr(topk_w),
                                   _ptr(counts_pre), _ptr(offsets), _ptr(sorted_token),
                                   _ptr(sorted_w), _ptr(slot_row), _ptr(dropped),
-                                  _ptr(x), _ptr(x_perm), _ptr(workspace), ws_bytes,
-                                  _stream(stream)), "moe_dispatch")
+                                  _ptr(x), _ptr(x_perm), _ptr(errors), _ptr(workspace),
+                                  ws_bytes, _stream(stream)), "moe_dispatch")
 
 
 def moe_grouped_ffn(spec, T, offsets, sorted_token, x, weights, y_rows,
-                    y_shared=None, workspace=None, ws_bytes=None, stream=None) -> None:
+                    y_shared=None, workspace=None, ws_bytes=None, stream=None,
+                    errors=None) -> None:
     w = weights if isinstance(weights, MoEExpertWeights) else expert_weights(weights)
     ws_bytes = ws_bytes if ws_bytes is not None else (workspace.numel() if workspace is not None else 0)
     _check(library().moe_grouped_ffn(ctypes.byref(spec), T, _ptr(offsets),
                                      _ptr(sorted_token), _ptr(x), ctypes.byref(w),
-                                     _ptr(y_rows), _ptr(y_shared), _ptr(workspace),
-                                     ws_bytes, _stream(stream)), "moe_grouped_ffn")
+                                     _ptr(y_rows), _ptr(y_shared), _ptr(errors),
+                                     _ptr(workspace), ws_bytes, _stream(stream)),
+           "moe_grouped_ffn")
 
 
 def moe_combine(spec, T, y_rows, slot_row, topk_w, y_shared, out, stream=None) -> None:

@@ -22,16 +22,20 @@ namespace {
 
 __global__ void __launch_bounds__(256)
 count_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
-             int32_t* __restrict__ hist) {
+             int32_t* __restrict__ hist, int32_t* __restrict__ err) {
   extern __shared__ int32_t h[];
   for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
   __syncthreads();
   const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
   const int64_t s1 = min(S, s0 + kDispatchChunk);
+  bool bad = false;  // an id outside [0,E): its slot is dropped
   for (int64_t s = s0 + threadIdx.x; s < s1; s += blockDim.x) {
     const int e = ids[s];
     if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+    else bad = true;
   }
+  if (err != nullptr && __ballot(bad) != 0 && (threadIdx.x & 63) == 0)
+    atomicOr(err, MOE_FLAG_BAD_EXPERT_ID);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     hist[static_cast<int64_t>(blockIdx.x) * E + e] = h[e];
@@ -212,7 +216,7 @@ dispatch_small_kernel(const int32_t* __restrict__ ids, const float* __restrict__
                       int32_t* __restrict__ dropped, int32_t* __restrict__ tiles1,
                       int bm1, int32_t* __restrict__ tiles2, int bm2,
                       int32_t* __restrict__ sorted_token, float* __restrict__ sorted_w,
-                      int32_t* __restrict__ slot_row) {
+                      int32_t* __restrict__ slot_row, int32_t* __restrict__ err) {
   __shared__ int wsum[16];
   __shared__ int32_t h[1024];
   __shared__ int32_t run[1024];
@@ -221,10 +225,14 @@ dispatch_small_kernel(const int32_t* __restrict__ ids, const float* __restrict__
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += blockDim.x) h[e] = 0;
   __syncthreads();
+  bool bad = false;  // an id outside [0,E): its slot is dropped
   for (int64_t s = tid; s < S; s += blockDim.x) {
     const int e = ids[s];
     if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+    else bad = true;
   }
+  if (err != nullptr && __ballot(bad) != 0 && (tid & 63) == 0)
+    atomicOr(err, MOE_FLAG_BAD_EXPERT_ID);
   __syncthreads();
   const int32_t cnt = tid < E ? h[tid] : 0;
   const int off = expert_prefixes(tid, E, cnt, S, cap, counts, offsets, dropped,
@@ -304,7 +312,8 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
                            int32_t* hist, int nblocks, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_token,
                            float* sorted_w, int32_t* slot_row, int32_t* dropped,
-                           int32_t* tiles1, int32_t* tiles2, hipStream_t s) {
+                           int32_t* tiles1, int32_t* tiles2, int32_t* err,
+                           hipStream_t s) {
   const size_t hsz = static_cast<size_t>(D.E) * sizeof(int32_t);
   int nbits = 0;
   while ((1 << nbits) < D.E) ++nbits;
@@ -312,11 +321,11 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, ids, w,
                        D.slots, D.k, D.E, D.cap, nbits, counts, offsets, dropped,
                        tiles1, kGemm1BM, tiles2, kGemm2BM, sorted_token, sorted_w,
-                       slot_row);
+                       slot_row, err);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(count_kernel, dim3(nblocks), dim3(256), hsz, s, ids,
-                     D.slots, D.E, hist);
+                     D.slots, D.E, hist, err);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, hist,
                      nblocks, D.E, D.slots, D.cap, counts, offsets, dropped,
                      tiles1, kGemm1BM, tiles2, kGemm2BM);

@@ -97,6 +97,7 @@ struct GemmArgs {
   int ksplit;                   // K splits (1 or 2; 2 only for down)
   int ldo;                      // output row length (F or d)
   int NT;                       // N tiles
+  int32_t* err;                 // MOE_FLAG_H_SATURATED is OR-ed in (or nullptr)
 };
 
 // byte offset of 16-byte chunk c (0..7) of row r inside a swizzled tile.
@@ -125,8 +126,11 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + __expf(-z));
 }
 
-// hidden activation -> fp16, round to nearest even, saturating at +-65504
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+// hidden activation -> fp16, round to nearest even, saturating at +-65504;
+// `sat` records a value outside that range (or NaN, which the clamp turns
+// into -65504)
+__device__ __forceinline__ uint32_t pack_h2(float a, float b, bool& sat) {
+  sat |= !(fabsf(a) <= 65504.f) || !(fabsf(b) <= 65504.f);
   a = fminf(fmaxf(a, -65504.f), 65504.f);
   b = fminf(fmaxf(b, -65504.f), 65504.f);
   const _Float16 ha = static_cast<_Float16>(a), hb = static_cast<_Float16>(b);
@@ -431,6 +435,7 @@ grouped_gemm_kernel(GemmArgs g) {
   // ---------------- epilogue
   // lane holds, for block (nb, mb) and item v: output column
   //   colbase(nb) + 8*(v/4) + 4*(lane/32) + v%4, row arow_l[mb].
+  bool sat = false;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const int m = m0 + arow_l[mb];
@@ -448,8 +453,8 @@ grouped_gemm_kernel(GemmArgs g) {
         for (int v = 0; v < 4; ++v)
           h[v] = silu(acc[0][mb][4 * q + v]) * acc[1][mb][4 * q + v];
         uint2 pk;
-        pk.x = pack_h2(h[0], h[1]);
-        pk.y = pack_h2(h[2], h[3]);
+        pk.x = pack_h2(h[0], h[1], sat);
+        pk.y = pack_h2(h[2], h[3], sat);
         *reinterpret_cast<uint2*>(orow + col) = pk;
       }
     } else {
@@ -471,14 +476,16 @@ grouped_gemm_kernel(GemmArgs g) {
               h[v] = z > 0.f ? z : 0.f;
             }
             uint2 pk;
-            pk.x = pack_h2(h[0], h[1]);
-            pk.y = pack_h2(h[2], h[3]);
+            pk.x = pack_h2(h[0], h[1], sat);
+            pk.y = pack_h2(h[2], h[3], sat);
             *reinterpret_cast<uint2*>(orow + col) = pk;
           }
         }
       }
     }
   }
+  if (MODE != kDown && g.err != nullptr && __ballot(sat) != 0 && lane == 0)
+    atomicOr(g.err, MOE_FLAG_H_SATURATED);
 }
 
 int ntiles(int mode, int N) {
@@ -521,7 +528,7 @@ int down_splits(const Dims& D) {
 
 hipError_t launch_shared_bf16(const Dims& D, const void* x,
                               const moe_expert_weights& w, void* Hs, void* Ys,
-                              hipStream_t s) {
+                              int32_t* err, hipStream_t s) {
   const int up_mode = D.swiglu ? kSwiGLU : kReLU;
   const int64_t mt = (D.T + BM - 1) / BM;
   const int64_t mat = static_cast<int64_t>(D.Fs) * D.d;  // one [Fs][d] matrix
@@ -546,8 +553,9 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
     g.ldo = D.Fs;
     g.NT = ntiles(up_mode, D.Fs);
     g.ksplit = 1;
-    hipError_t err = launch_one(up_mode, false, g, mt, s);
-    if (err != hipSuccess) return err;
+    g.err = err;
+    hipError_t e = launch_one(up_mode, false, g, mt, s);
+    if (e != hipSuccess) return e;
     GemmArgs h{};
     h.a = static_cast<const uint16_t*>(Hs);
     h.a_bytes = static_cast<uint32_t>(D.T * D.Fs * 2);
@@ -561,8 +569,8 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
     h.ldo = D.d;
     h.NT = ntiles(kDown, D.d);
     h.ksplit = 1;
-    err = launch_one(kDown, false, h, mt, s);
-    if (err != hipSuccess) return err;
+    e = launch_one(kDown, false, h, mt, s);
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
@@ -571,7 +579,8 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
                            const int32_t* tiles1, const int32_t* tiles2,
                            const int32_t* sorted_token, const void* x,
                            const moe_expert_weights& w, void* H, void* Hs,
-                           void* Y, float* Ypart, void* Ys, hipStream_t s) {
+                           void* Y, float* Ypart, void* Ys, int32_t* err,
+                           hipEvent_t mid, hipStream_t s) {
   const int up_mode = D.swiglu ? kSwiGLU : kReLU;
   // kept rows are at most min(T*k, E*capacity); cap is already <= T*k
   const int64_t nmax = std::min<int64_t>(D.slots, D.cap * D.E);
@@ -598,8 +607,10 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
     g.ldo = D.F;
     g.NT = ntiles(up_mode, D.F);
     g.ksplit = 1;
-    hipError_t err = launch_one(up_mode, true, g, nmax / BM + D.E, s);
-    if (err != hipSuccess) return err;
+    g.err = err;
+    hipError_t e = launch_one(up_mode, true, g, nmax / BM + D.E, s);
+    if (e != hipSuccess) return e;
+    if (mid != nullptr && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
   }
   {
     GemmArgs g{};
@@ -618,10 +629,10 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
     g.ksplit = down_splits(D);
     g.part = Ypart;
     if (g.ksplit > 1 && Ypart == nullptr) return hipErrorInvalidValue;
-    hipError_t err = launch_one(kDown, false, g, nmax / BM + D.E, s);
-    if (err != hipSuccess) return err;
+    hipError_t e = launch_one(kDown, false, g, nmax / BM + D.E, s);
+    if (e != hipSuccess) return e;
   }
-  if (D.S > 0) return launch_shared_bf16(D, x, w, Hs, Ys, s);
+  if (D.S > 0) return launch_shared_bf16(D, x, w, Hs, Ys, err, s);
   return hipSuccess;
 }
 

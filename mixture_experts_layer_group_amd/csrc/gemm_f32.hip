@@ -77,7 +77,7 @@ f32_down_kernel(const int32_t* __restrict__ offsets, int E,
 hipError_t launch_ffn_f32(const Dims& D, const int32_t* offsets,
                           const int32_t* sorted_token, const void* x,
                           const moe_expert_weights& w, void* H, void* Hs,
-                          void* Y, void* Ys, hipStream_t s) {
+                          void* Y, void* Ys, hipEvent_t mid, hipStream_t s) {
   const float* xf = static_cast<const float*>(x);
   // FUSED_GATE_UP: each expert's [F][d] gate rows, then its up rows
   const int64_t mat = static_cast<int64_t>(D.F) * D.d;
@@ -89,6 +89,10 @@ hipError_t launch_ffn_f32(const Dims& D, const int32_t* offsets,
                        dim3(256), 0, s, offsets, D.E, sorted_token, xf, wg, wu,
                        D.fused ? 2 * mat : mat, static_cast<float*>(H),
                        D.slots, D.d, D.F, D.swiglu ? 1 : 0, 0);
+    if (mid != nullptr) {
+      const hipError_t e = hipEventRecord(mid, s);
+      if (e != hipSuccess) return e;
+    }
     const int64_t m = D.slots * D.d;
     hipLaunchKernelGGL(f32_down_kernel, dim3(static_cast<unsigned>((m + 255) / 256)),
                        dim3(256), 0, s, offsets, D.E, static_cast<const float*>(H),

@@ -34,31 +34,6 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-// The value held by lane (this lane xor D), D in {4, 8, 16, 32}: the row
-// shifts by 4 (each direction serves the lanes whose partner stays inside
-// their row of 16), the row rotation by 8, and the gfx950 row swaps for 16
-// and 32.  None goes through LDS.
-template <int D>
-__device__ __forceinline__ float xor_move(float v, int lane) {
-  if constexpr (D == 4) {
-    const float dn = dpp_f<0x114>(v);  // row_shr:4, from lane l-4
-    const float up = dpp_f<0x104>(v);  // row_shl:4, from lane l+4
-    return (lane & 4) ? dn : up;
-  } else if constexpr (D == 8) {
-    return dpp_f<0x128>(v);  // row_ror:8, xor 8 inside a row of 16
-  } else if constexpr (D == 16) {
-    // odd rows of the first result hold the even rows, and the other way
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
-                                                    false, false);
-    return __uint_as_float((lane & 16) ? r[0] : r[1]);
-  } else {
-    static_assert(D == 32, "distance");
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
-                                                    false, false);
-    return __uint_as_float((lane & 32) ? r[0] : r[1]);
-  }
-}
-
 // In-place sum of V per-lane values over the lanes that differ only in the
 // bits D, D/2, ..., 4 (the K slices of a unit group).  Butterfly with
 // halving: at distance D the lane with bit D set keeps the upper half of its
@@ -310,6 +285,7 @@ struct U4Args {
   int E;
   int N;                        // units (output columns) per expert
   int rstride;                  // rows from one expert's matrix to the next
+  int32_t* err;                 // MOE_FLAG_H_SATURATED is OR-ed in (or nullptr)
 };
 
 // exclusive prefix over the lanes of a wave, and the wave total: an
@@ -582,6 +558,10 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
       }
   };
 
+  // a hidden activation outside the fp16 range (or NaN); reported once,
+  // after the item loop, so the flag adds no memory operation between the
+  // ring's loads and their waits
+  bool sat = false;
   // the item in stage st (fetched with kRegs): units u0.. of the expert,
   // chunk rows row0..
   auto compute = [&](const uint8_t* st, int row0, int rows, int u0) {
@@ -661,6 +641,7 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
       const int64_t o = static_cast<int64_t>(row0 + i4) * g.N + u;
       if (PAIR) {  // hidden activation, fp16 (saturating)
         float h = gv / (1.f + __expf(-gv)) * upv;
+        sat |= !(fabsf(h) <= 65504.f);
         h = fminf(fmaxf(h, -65504.f), 65504.f);
         static_cast<_Float16*>(g.out)[o] = static_cast<_Float16>(h);
       } else {  // expert output, fp32
@@ -706,6 +687,8 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
     }
     compute(ring + (t % NS) * SL::kBytes, row0, rows, u0);
   }
+  if (PAIR && g.err != nullptr && __ballot(sat) != 0 && lane == 0)
+    atomicOr(g.err, MOE_FLAG_H_SATURATED);
 }
 
 #define MOE_U4S_KERNEL(P, K)                                                    \
@@ -767,7 +750,7 @@ hipError_t launch_stream(int K, const U4Args& g, hipStream_t s) {
 hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
                          const int32_t* sorted_token, const void* x,
                          const moe_expert_weights& w, void* H, void* Y,
-                         hipStream_t s) {
+                         int32_t* err, hipEvent_t mid, hipStream_t s) {
   if (!supported_k(D.d) || !supported_k(D.F) || !D.swiglu || group != 64 ||
       D.E > kMaxExperts)
     return hipErrorInvalidValue;
@@ -795,11 +778,13 @@ hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
     g.b[1] = static_cast<const uint8_t*>(w.up_bias);
   }
   g.out = H;
+  g.err = err;
   g.E = D.E;
   g.N = D.F;
   g.rstride = D.fused ? 2 * D.F : D.F;
-  hipError_t err = launch_stream<true>(D.d, g, s);
-  if (err != hipSuccess) return err;
+  hipError_t e = launch_stream<true>(D.d, g, s);
+  if (e != hipSuccess) return e;
+  if (mid != nullptr && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
   U4Args h{};
   h.offsets = offsets;
   h.sorted_token = nullptr;

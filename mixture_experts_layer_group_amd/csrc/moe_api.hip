@@ -139,9 +139,8 @@ WsLayout layout_of(const Dims& D) {
     o = align_up(o + bytes);
     return at;
   };
-  const RouterPlan rp = router_plan(D, D.router_dtype);
+  const RouterPlan rp = router_plan(D);
   L.logits = take(static_cast<size_t>(rp.S) * T * E * 4);
-  L.w3 = take(rp.mfma && rp.npass == 3 ? 3 * E * static_cast<size_t>(D.d) * 2 : 0);
   L.probpart = take(static_cast<size_t>(L.route_blocks) * E * 4);
   L.hist = take(static_cast<size_t>(L.dispatch_blocks) * E * 4);
   L.tiles1 = take((E + 1) * 4);
@@ -207,21 +206,13 @@ moe_status do_route(const moe_spec& sp, const Dims& D, const WsLayout& L,
                     const void* x, const void* wr, const float* bias,
                     const int32_t* forced, int32_t* rejected,
                     int32_t* ids, float* w, float* logits, float* prob_sum,
-                    void* ws, hipStream_t s) {
-  const RouterPlan rp = router_plan(D, sp.router_dtype);
-  hipError_t e;
-  float* Lg;
-  float* Lout = nullptr;
-  if (rp.mfma) {
-    // partial logits in the workspace; the selection adds them and hands
-    // the sums to the caller's buffer if one was given
-    Lg = at<float>(ws, L.logits);
-    Lout = logits;
-    e = launch_router_mfma(D, rp, x, wr, at<uint16_t>(ws, L.w3), Lg, s);
-  } else {
-    Lg = logits ? logits : at<float>(ws, L.logits);
-    e = launch_router_logits(D, sp.act_dtype, sp.router_dtype, x, wr, Lg, s);
-  }
+                    int32_t* err, void* ws, hipStream_t s) {
+  const RouterPlan rp = router_plan(D);
+  // split reductions write partial planes to the workspace; the selection
+  // adds them and hands the sums to the caller's buffer if one was given
+  float* Lg = (rp.S > 1 || logits == nullptr) ? at<float>(ws, L.logits) : logits;
+  float* Lout = rp.S > 1 ? logits : nullptr;
+  hipError_t e = launch_router_logits(D, rp, sp.act_dtype, sp.router_dtype, x, wr, Lg, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   const bool want_p = prob_sum != nullptr && sp.router == MOE_ROUTER_SOFTMAX_TOPK;
   float* part = want_p ? at<float>(ws, L.probpart) : nullptr;
@@ -229,40 +220,51 @@ moe_status do_route(const moe_spec& sp, const Dims& D, const WsLayout& L,
     e = launch_zero_i32(rejected, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
-  e = launch_router_select(D, sp, Lg, rp.mfma ? rp.S : 1, Lout, bias, forced,
-                           rejected, ids, w, part, L.route_blocks, s);
+  e = launch_router_select(D, sp, Lg, rp.S, Lout, bias, forced,
+                           rejected, ids, w, part, err, L.route_blocks, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (want_p) return hip_status(launch_prob_finalize(D, part, L.route_blocks, prob_sum, s));
   return MOE_OK;
 }
 
+// ev (may be null): three events recorded before the first expert kernel,
+// between the routed gate/up and down kernels, and after the last one
 moe_status do_ffn(const moe_spec& sp, const Dims& D, const WsLayout& L,
                   const int32_t* offsets, const int32_t* sorted_token,
                   const void* x, const moe_expert_weights& w, void* y_rows,
-                  void* y_shared, void* ws, bool fused, hipStream_t s) {
+                  void* y_shared, int32_t* err, void* const* ev, void* ws,
+                  bool fused, hipStream_t s) {
   void* H = at<void>(ws, L.H);
   void* Hs = at<void>(ws, L.Hs);
-  if (!D.bf16) {
-    return hip_status(launch_ffn_f32(D, offsets, sorted_token, x, w, H, Hs,
-                                     y_rows, y_shared, s));
-  }
-  if (D.u4) {
-    hipError_t e = launch_ffn_u4(D, sp.quant_group, offsets, sorted_token, x, w,
-                                 H, y_rows, s);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    if (D.S > 0) return hip_status(launch_shared_bf16(D, x, w, Hs, y_shared, s));
-    return MOE_OK;
+  hipEvent_t mid = ev ? static_cast<hipEvent_t>(ev[1]) : nullptr;
+  hipError_t e = hipSuccess;
+  if (!D.bf16 || D.u4) {
+    if (ev && (e = hipEventRecord(static_cast<hipEvent_t>(ev[0]), s)) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (!D.bf16) {
+      e = launch_ffn_f32(D, offsets, sorted_token, x, w, H, Hs, y_rows, y_shared, mid, s);
+    } else {
+      e = launch_ffn_u4(D, sp.quant_group, offsets, sorted_token, x, w, H, y_rows, err,
+                        mid, s);
+      if (e == hipSuccess && D.S > 0) e = launch_shared_bf16(D, x, w, Hs, y_shared, err, s);
+    }
+    if (e == hipSuccess && ev) e = hipEventRecord(static_cast<hipEvent_t>(ev[2]), s);
+    return hip_status(e);
   }
   int32_t* t1 = at<int32_t>(ws, L.tiles1);
   int32_t* t2 = at<int32_t>(ws, L.tiles2);
   if (!fused) {  // the fused layer's dispatch already wrote the tile prefixes
-    hipError_t e = launch_tile_prefix(D, offsets, t1, t2, s);
+    e = launch_tile_prefix(D, offsets, t1, t2, s);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
+  if (ev && (e = hipEventRecord(static_cast<hipEvent_t>(ev[0]), s)) != hipSuccess)
+    return MOE_ERR_HIP;
   float* part = down_splits(D) > 1 ? at<float>(ws, L.Ypart) : nullptr;
-  hipError_t e = launch_ffn_bf16(D, offsets, t1, t2, sorted_token, x, w, H, Hs,
-                                 y_rows, part, y_shared, s);
+  e = launch_ffn_bf16(D, offsets, t1, t2, sorted_token, x, w, H, Hs, y_rows, part,
+                      y_shared, err, mid, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (ev && (e = hipEventRecord(static_cast<hipEvent_t>(ev[2]), s)) != hipSuccess)
+    return MOE_ERR_HIP;
   // the stage API returns whole expert rows; the fused layer lets the
   // combine add the second split instead
   if (part && !fused)
@@ -300,8 +302,8 @@ moe_status moe_workspace_size(const moe_spec* spec, int64_t T, size_t* bytes) {
 moe_status moe_route(const moe_spec* spec, int64_t T, const void* x,
                      const void* w_router, const float* expert_bias,
                      int32_t* topk_ids, float* topk_w, float* logits,
-                     float* prob_sum, void* workspace, size_t ws_bytes,
-                     moe_stream_t stream) {
+                     float* prob_sum, int32_t* errors, void* workspace,
+                     size_t ws_bytes, moe_stream_t stream) {
   moe_status st = validate(spec, T);
   if (st != MOE_OK) return st;
   if (expert_bias != nullptr && spec->router == MOE_ROUTER_SOFTMAX_TOPK)
@@ -313,8 +315,8 @@ moe_status moe_route(const moe_spec* spec, int64_t T, const void* x,
   const WsLayout L = layout_of(D);
   if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   return do_route(*spec, D, L, x, w_router, expert_bias, nullptr, nullptr,
-                  topk_ids, topk_w,
-                  logits, prob_sum, workspace, static_cast<hipStream_t>(stream));
+                  topk_ids, topk_w, logits, prob_sum, errors, workspace,
+                  static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_route_forced(const moe_spec* spec, int64_t T, const void* x,
@@ -333,7 +335,7 @@ moe_status moe_route_forced(const moe_spec* spec, int64_t T, const void* x,
   const WsLayout L = layout_of(D);
   if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   return do_route(*spec, D, L, x, w_router, nullptr, forced_ids, rejected,
-                  topk_ids, topk_w, logits, prob_sum, workspace,
+                  topk_ids, topk_w, logits, prob_sum, nullptr, workspace,
                   static_cast<hipStream_t>(stream));
 }
 
@@ -342,8 +344,8 @@ moe_status moe_dispatch(const moe_spec* spec, int64_t T,
                         int32_t* counts_pre, int32_t* offsets,
                         int32_t* sorted_token, float* sorted_w,
                         int32_t* slot_row, int32_t* dropped, const void* x,
-                        void* x_perm, void* workspace, size_t ws_bytes,
-                        moe_stream_t stream) {
+                        void* x_perm, int32_t* errors, void* workspace,
+                        size_t ws_bytes, moe_stream_t stream) {
   moe_status st = validate(spec, T);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
@@ -359,7 +361,7 @@ moe_status moe_dispatch(const moe_spec* spec, int64_t T,
   hipError_t e = launch_dispatch(D, topk_ids, topk_w, at<int32_t>(workspace, L.hist),
                                  L.dispatch_blocks, counts_pre, offsets,
                                  sorted_token, sorted_w, slot_row, dropped,
-                                 nullptr, nullptr, s);
+                                 nullptr, nullptr, errors, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (x) return hip_status(launch_gather_rows(D, offsets, sorted_token, x, x_perm, s));
   return MOE_OK;
@@ -368,8 +370,9 @@ moe_status moe_dispatch(const moe_spec* spec, int64_t T,
 moe_status moe_grouped_ffn(const moe_spec* spec, int64_t T,
                            const int32_t* offsets, const int32_t* sorted_token,
                            const void* x, const moe_expert_weights* weights,
-                           void* y_rows, void* y_shared, void* workspace,
-                           size_t ws_bytes, moe_stream_t stream) {
+                           void* y_rows, void* y_shared, int32_t* errors,
+                           void* workspace, size_t ws_bytes,
+                           moe_stream_t stream) {
   moe_status st = validate(spec, T);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
@@ -383,7 +386,8 @@ moe_status moe_grouped_ffn(const moe_spec* spec, int64_t T,
   const WsLayout L = layout_of(D);
   if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   return do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, y_rows,
-                y_shared, workspace, false, static_cast<hipStream_t>(stream));
+                y_shared, errors, nullptr, workspace, false,
+                static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_combine(const moe_spec* spec, int64_t T, const void* y_rows,
@@ -433,20 +437,19 @@ moe_status moe_layer_forward(const moe_spec* spec, int64_t T, const void* x,
   float* sorted_w = at<float>(ws, L.sorted_w);
 
   st = do_route(*spec, D, L, x, w_router, expert_bias, nullptr, nullptr, ids,
-                tw, o.logits,
-                o.prob_sum, ws, s);
+                tw, o.logits, o.prob_sum, o.errors, ws, s);
   if (st != MOE_OK) return st;
   const bool mfma_path = D.bf16 && !D.u4;
   hipError_t e = launch_dispatch(
       D, ids, tw, at<int32_t>(ws, L.hist), L.dispatch_blocks, counts, offsets,
       sorted_token, sorted_w, slot_row, dropped,
       mfma_path ? at<int32_t>(ws, L.tiles1) : nullptr,
-      mfma_path ? at<int32_t>(ws, L.tiles2) : nullptr, s);
+      mfma_path ? at<int32_t>(ws, L.tiles2) : nullptr, o.errors, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   void* Y = at<void>(ws, L.Y);
   void* Ys = at<void>(ws, L.Ys);
-  st = do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, Y, Ys, ws,
-              mfma_path, s);
+  st = do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, Y, Ys, o.errors,
+              o.ffn_events, ws, mfma_path, s);
   if (st != MOE_OK) return st;
   const float* part = (mfma_path && down_splits(D) > 1) ? at<float>(ws, L.Ypart) : nullptr;
   return hip_status(launch_combine(D, Y, part, slot_row, tw, D.S > 0 ? Ys : nullptr,

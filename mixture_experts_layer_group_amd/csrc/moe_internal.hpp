@@ -67,6 +67,35 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
+// The value held by lane (this lane xor D), D in {1, 2, 4, 8, 16, 32}: DPP
+// quad permutations for 1 and 2, the row shifts by 4 (each direction serves
+// the lanes whose partner stays inside their row of 16), the row rotation by
+// 8, and the gfx950 row swaps for 16 and 32.  None goes through LDS.
+template <int D>
+__device__ __forceinline__ float xor_move(float v, int lane) {
+  if constexpr (D == 1) {
+    return dpp_f<kDppXor1>(v);
+  } else if constexpr (D == 2) {
+    return dpp_f<kDppXor2>(v);
+  } else if constexpr (D == 4) {
+    const float dn = dpp_f<0x114>(v);  // row_shr:4, from lane l-4
+    const float up = dpp_f<0x104>(v);  // row_shl:4, from lane l+4
+    return (lane & 4) ? dn : up;
+  } else if constexpr (D == 8) {
+    return dpp_f<0x128>(v);  // row_ror:8, xor 8 inside a row of 16
+  } else if constexpr (D == 16) {
+    // odd rows of the first result hold the even rows, and the other way
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float((lane & 16) ? r[0] : r[1]);
+  } else {
+    static_assert(D == 32, "distance");
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                    false, false);
+    return __uint_as_float((lane & 32) ? r[0] : r[1]);
+  }
+}
+
 // ---------------------------------------------------------------- sizes
 // Per-call problem sizes derived from a validated spec.
 struct Dims {
@@ -82,20 +111,24 @@ struct Dims {
   int router_dtype;   // MOE_DTYPE_* of the router weights
 };
 
-// Router logits plan for bf16 activations (matrix cores, router_mfma.hip):
-// tiles of 128 tokens x BN experts, the reduction over d split over S
-// workgroups whose partial logits the selection adds in order; npass = 3
-// when fp32 router weights are split into three bf16 parts.
+// Router logits plan (router.hip), all on the vector ALUs with fp32
+// accumulation: a row-dot kernel for decode-sized batches, a kernel for
+// few experts (a wave per 64/EB tokens, partial sums reduced across lanes)
+// and 128 x 128 tiles for many; the last two may split the reduction over d
+// over S blocks, each writing a plane of partial logits ([S][T][E]) that
+// the selection adds in plane order.
+enum { kRouterRowdot = 0, kRouterSmallE = 1, kRouterTiled = 2 };
 struct RouterPlan {
-  bool mfma;       // false: fp32 activations, vector-ALU kernels, S = 1
-  int npass, BN, mtiles, ntiles, kt_total, kt_split, S;
+  int kind;  // kRouter*
+  int S;     // partial-logit planes (1 unless tiled)
+  int kper;  // reduction length of one split
 };
-RouterPlan router_plan(const Dims& D, int router_dtype);
+RouterPlan router_plan(const Dims& D);
 constexpr int kMaxLogitPlanes = 16;  // largest S
 
 // Workspace carve-up (byte offsets, each 256-aligned).
 struct WsLayout {
-  size_t logits, w3, probpart, hist, tiles1, tiles2;  // logits: [S][T][E] partials
+  size_t logits, probpart, hist, tiles1, tiles2;  // logits: [S][T][E] partials
   size_t topk_ids, topk_w, counts, offsets, sorted_token, sorted_w, slot_row,
       dropped;
   size_t H, Hs, Y, Ypart, Ys;
@@ -122,24 +155,22 @@ constexpr int kGemm2BM = 256;
 int down_splits(const Dims& D);
 
 // ---------------------------------------------------------------- launchers
+// Every FFN launcher records `mid` (when not null) on the stream between its
+// gate/up kernel and its down kernel, for profiling.
 // router.hip
-hipError_t launch_router_logits(const Dims& D, int act_dtype, int router_dtype,
-                                const void* x, const void* wr, float* logits,
-                                hipStream_t s);
+hipError_t launch_router_logits(const Dims& D, const RouterPlan& p, int act_dtype,
+                                int router_dtype, const void* x, const void* wr,
+                                float* logits, hipStream_t s);
 // logits: S planes of partial logits [S][T][E], added in plane order;
 // logits_out (may be null) receives the summed logits
 hipError_t launch_router_select(const Dims& D, const moe_spec& sp,
                                 const float* logits, int S, float* logits_out,
                                 const float* bias, const int32_t* forced,
                                 int32_t* rejected, int32_t* ids, float* w,
-                                float* probpart, int nblocks, hipStream_t s);
+                                float* probpart, int32_t* err, int nblocks,
+                                hipStream_t s);
 // *p = 0 by a one-thread kernel
 hipError_t launch_zero_i32(int32_t* p, hipStream_t s);
-// router_mfma.hip: partial logits of plan p into part ([p.S][T][E]); w3
-// holds 3*E*d bf16 when p.npass == 3
-hipError_t launch_router_mfma(const Dims& D, const RouterPlan& p, const void* x,
-                              const void* wr, uint16_t* w3, float* part,
-                              hipStream_t s);
 hipError_t launch_prob_finalize(const Dims& D, const float* probpart,
                                 int nblocks, float* prob_sum, hipStream_t s);
 
@@ -148,7 +179,8 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
                            int32_t* hist, int nblocks, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_token,
                            float* sorted_w, int32_t* slot_row, int32_t* dropped,
-                           int32_t* tiles1, int32_t* tiles2, hipStream_t s);
+                           int32_t* tiles1, int32_t* tiles2, int32_t* err,
+                           hipStream_t s);
 hipError_t launch_gather_rows(const Dims& D, const int32_t* offsets,
                               const int32_t* sorted_token, const void* x,
                               void* x_perm, hipStream_t s);
@@ -160,7 +192,8 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
                            const int32_t* tiles1, const int32_t* tiles2,
                            const int32_t* sorted_token, const void* x,
                            const moe_expert_weights& w, void* H, void* Hs,
-                           void* Y, float* Ypart, void* Ys, hipStream_t s);
+                           void* Y, float* Ypart, void* Ys, int32_t* err,
+                           hipEvent_t mid, hipStream_t s);
 // Y[r] += Ypart[r] for the kept rows (r < offsets[E]): folds the second K
 // split into the expert outputs with the combine's own fp32 addition
 hipError_t launch_fold_split(const Dims& D, const int32_t* offsets, float* Y,
@@ -169,16 +202,16 @@ hipError_t launch_fold_split(const Dims& D, const int32_t* offsets, float* Y,
 hipError_t launch_ffn_f32(const Dims& D, const int32_t* offsets,
                           const int32_t* sorted_token, const void* x,
                           const moe_expert_weights& w, void* H, void* Hs,
-                          void* Y, void* Ys, hipStream_t s);
+                          void* Y, void* Ys, hipEvent_t mid, hipStream_t s);
 // gemm_u4.hip (bf16 activations, 4-bit affine routed weights, VALU)
 hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
                          const int32_t* sorted_token, const void* x,
                          const moe_expert_weights& w, void* H, void* Y,
-                         hipStream_t s);
+                         int32_t* err, hipEvent_t mid, hipStream_t s);
 // shared experts with bf16 weights on the MFMA kernel (used by the u4 path)
 hipError_t launch_shared_bf16(const Dims& D, const void* x,
                               const moe_expert_weights& w, void* Hs, void* Ys,
-                              hipStream_t s);
+                              int32_t* err, hipStream_t s);
 
 // stats.hip: routing health and the aux-loss-free bias update
 hipError_t launch_routing_health(const Dims& D, const int32_t* counts,

@@ -14,6 +14,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -47,140 +49,174 @@ __device__ __forceinline__ void ld8(const uint16_t* p, int64_t i, float* v) {
 }
 
 // ------------------------------------------------------------------ logits
-// Tiled fp32 GEMM for many tokens: a 64x64 (token x expert) tile per block,
-// 4x4 outputs per thread, K staged through LDS in steps of 32.
-constexpr int LT = 64, LE = 64, LK = 32;
+// Many tokens and many experts: a 128 x 128 (token x expert) tile per
+// 256-thread block, 8 x 8 outputs per thread, K staged through LDS in
+// chunks of 32, double-buffered (the next chunk is loaded into registers
+// while the current one is multiplied).  The reduction over d may be split
+// over blockIdx.z: split q writes its partial logits to plane q
+// ([S][T][E]) and the selection adds the planes in plane order, so the
+// result does not depend on timing.  Every split is at most kper long and
+// starts at a multiple of 32; d is a multiple of 8.
+//
+// Every term is one fp32 FMA (one rounding per product added), so the
+// logits meet the forward error bound of a d-term fp32 dot product in any
+// order.  bf16 x bf16 is not sent through v_dot2_f32_bf16: measured on
+// gfx950 its result can differ from the exact a0*b0 + a1*b1 + c by up to
+// 2.5 units of fp32 rounding of |a0 b0| + |a1 b1| + |c|, which over d/2
+// steps exceeds that bound.
+constexpr int RT = 128, RE = 128, RK = 32;
 
 template <typename XT, typename WT>
 __global__ void __launch_bounds__(256)
-logits_tiled_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
-                    float* __restrict__ L, int64_t T, int E, int d) {
-  __shared__ float xs[LK][LT + 4];
-  __shared__ float ws[LK][LE + 4];
+logits_tile_fma_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
+                       float* __restrict__ L, int64_t T, int E, int d, int kper) {
+  __shared__ __attribute__((aligned(16))) float xs[2][RK][RT + 4];
+  __shared__ __attribute__((aligned(16))) float ws[2][RK][RE + 4];
   const int tid = threadIdx.x;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * LT;
-  const int e0 = blockIdx.y * LE;
-  const int tx = tid % 16, ty = tid / 16;
-  float acc[4][4] = {};
-  const int lr = tid / 4;        // row loaded by this thread
-  const int lk = (tid % 4) * 8;  // its 8-element K chunk
-  const bool vec = (d % 8) == 0;
-  for (int k0 = 0; k0 < d; k0 += LK) {
-    float v[8];
-    {
-      const int64_t t = t0 + lr;
-      const int k = k0 + lk;
-      if (t < T && vec && k + 8 <= d) {
-        ld8(x, t * d + k, v);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * RT;
+  const int e0 = blockIdx.y * RE;
+  const int kbeg = blockIdx.z * kper;
+  const int kend = min(d, kbeg + kper);
+  const int ty = tid / 16, tx = tid % 16;
+  // loader: tile row lr, 16 consecutive K elements from lk
+  const int lr = tid >> 1, lk = (tid & 1) * 16;
+  const int64_t xt = t0 + lr;
+  const int we = e0 + lr;
+  float acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+  float xv[16], wv[16];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + lk + 8 * h;
+      if (xt < T && k < kend) {
+        ld8(x, xt * d + k, xv + 8 * h);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          v[j] = (t < T && k + j < d) ? ld1(x, t * d + k + j) : 0.f;
+        for (int j = 0; j < 8; ++j) xv[8 * h + j] = 0.f;
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xs[lk + j][lr] = v[j];
-    }
-    {
-      const int e = e0 + lr;
-      const int k = k0 + lk;
-      if (e < E && vec && k + 8 <= d) {
-        ld8(wr, static_cast<int64_t>(e) * d + k, v);
+      if (we < E && k < kend) {
+        ld8(wr, static_cast<int64_t>(we) * d + k, wv + 8 * h);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          v[j] = (e < E && k + j < d)
-                     ? ld1(wr, static_cast<int64_t>(e) * d + k + j)
-                     : 0.f;
+        for (int j = 0; j < 8; ++j) wv[8 * h + j] = 0.f;
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ws[lk + j][lr] = v[j];
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < LK; ++kk) {
-      float a[4], b[4];
+  };
+  auto lstore = [&](int b) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = xs[kk][ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = ws[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    for (int j = 0; j < 16; ++j) {
+      xs[b][lk + j][lr] = xv[j];
+      ws[b][lk + j][lr] = wv[j];
     }
+  };
+  const int nk = kend > kbeg ? (kend - kbeg + RK - 1) / RK : 0;
+  if (nk > 0) {
+    gload(kbeg);
+    lstore(0);
     __syncthreads();
   }
+  for (int c = 0; c < nk; ++c) {
+    const int b = c & 1;
+    if (c + 1 < nk) gload(kbeg + (c + 1) * RK);
+#pragma unroll 4
+    for (int kk = 0; kk < RK; ++kk) {
+      const float4 a0 = *reinterpret_cast<const float4*>(&xs[b][kk][ty * 8]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&xs[b][kk][ty * 8 + 4]);
+      const float4 b0 = *reinterpret_cast<const float4*>(&ws[b][kk][tx * 8]);
+      const float4 b1 = *reinterpret_cast<const float4*>(&ws[b][kk][tx * 8 + 4]);
+      const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float w[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t t = t0 + ty * 4 + i;
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], w[j], acc[i][j]);
+    }
+    // buffer b^1 was last read before the previous barrier
+    if (c + 1 < nk) lstore(b ^ 1);
+    __syncthreads();
+  }
+  float* P = L + static_cast<int64_t>(blockIdx.z) * T * E;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t t = t0 + ty * 8 + i;
     if (t >= T) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) L[t * E + e] = acc[i][j];
+    for (int j = 0; j < 8; ++j) {
+      const int e = e0 + tx * 8 + j;
+      if (e < E) P[t * E + e] = acc[i][j];
     }
   }
 }
 
-// Few experts (E <= 16): each wave owns 4 tokens; lanes split K 8 elements
-// at a time (16-byte loads of x), the router rows are staged through LDS in
-// K chunks of 32 KiB, and each lane keeps 4 x EB partial dot products that
-// are reduced across the wave at the end.  16 tokens per block gives
-// T/16 blocks (256 for 4096 tokens) instead of T/64 tiles that would each
-// waste most of their 64 expert columns.
+// Few experts (E <= 16): a wave takes TPW = 64/EB tokens and one slice of
+// the reduction (blockIdx.y, kper long); lane l handles K elements l*8..+7
+// of every 512 of the slice, so the loads of a token row and of a router
+// row are contiguous across the wave.  Each lane keeps TPW x EB partial
+// dot products (64 of them); a halving butterfly across the lanes then
+// leaves lane l with the whole slice's sum for token l/EB, expert l%EB,
+// which it writes to the slice's plane of partial logits ([S][T][E]).
+template <int D, int CNT>
+__device__ __forceinline__ void halve(float (&v)[64], int lane) {
+  if constexpr (D >= 1) {
+    constexpr int kHalf = CNT / 2;
+    const bool upper = (lane & D) != 0;
+#pragma unroll
+    for (int i = 0; i < kHalf; ++i) {
+      const float send = upper ? v[i] : v[i + kHalf];
+      const float keep = upper ? v[i + kHalf] : v[i];
+      v[i] = keep + xor_move<D>(send, lane);
+    }
+    halve<D / 2, kHalf>(v, lane);
+  }
+}
+
 template <typename XT, typename WT, int EB>
 __global__ void __launch_bounds__(256)
-logits_small_e_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
-                      float* __restrict__ L, int64_t T, int E, int d) {
-  constexpr int TPW = 4;                // tokens per wave
-  constexpr int KC = 8192 / EB;         // K chunk: EB * KC floats = 32 KiB
-  __shared__ __attribute__((aligned(16))) float ws[EB * KC];
+logits_few_e_kernel(const XT* __restrict__ x, const WT* __restrict__ wr,
+                    float* __restrict__ L, int64_t T, int E, int d, int kper) {
+  constexpr int TPW = kWave / EB;  // tokens per wave
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
-  const int64_t t0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * TPW;
-  float acc[TPW][EB];
+  const int64_t t0 = (static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave) * TPW;
+  const int kbeg = blockIdx.y * kper;
+  const int kend = min(d, kbeg + kper);
+  float acc[64];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i)
-#pragma unroll
-    for (int e = 0; e < EB; ++e) acc[i][e] = 0.f;
-  for (int k0 = 0; k0 < d; k0 += KC) {
-    const int kc = min(KC, d - k0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < EB * kc; i += blockDim.x) {
-      const int e = i / kc, k = i % kc;
-      ws[e * KC + k] = e < E ? ld1(wr, static_cast<int64_t>(e) * d + k0 + k) : 0.f;
-    }
-    __syncthreads();
-    for (int k = lane * 8; k < kc; k += kWave * 8) {
-      float xv[TPW][8];
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        if (t0 + i < T) {
-          ld8(x, (t0 + i) * d + k0 + k, xv[i]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) xv[i][j] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < EB; ++e) {
-        const float4 w0 = *reinterpret_cast<const float4*>(&ws[e * KC + k]);
-        const float4 w1 = *reinterpret_cast<const float4*>(&ws[e * KC + k + 4]);
-        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int i = 0; i < TPW; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][e] = fmaf(xv[i][j], wv[j], acc[i][e]);
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < TPW; ++i)
+  for (int i = 0; i < 64; ++i) acc[i] = 0.f;
+  for (int k = kbeg + lane * 8; k < kend; k += kWave * 8) {
+    float wv[EB][8];
 #pragma unroll
     for (int e = 0; e < EB; ++e) {
-      const float v = wave_sum(acc[i][e]);
-      if (lane == e && e < E && t0 + i < T) L[(t0 + i) * E + e] = v;
+      if (e < E) {
+        ld8(wr, static_cast<int64_t>(e) * d + k, wv[e]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wv[e][j] = 0.f;
+      }
     }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      float xv[8];
+      if (t0 + t < T) {
+        ld8(x, (t0 + t) * d + k, xv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xv[j] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < EB; ++e)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[t * EB + e] = fmaf(xv[j], wv[e][j], acc[t * EB + e]);
+    }
+  }
+  // lane l ends with the sum of value l (token l / EB, expert l % EB)
+  halve<32, 64>(acc, lane);
+  const int64_t t = t0 + lane / EB;
+  const int e = lane % EB;
+  if (t < T && e < E) L[(static_cast<int64_t>(blockIdx.y) * T + t) * E + e] = acc[0];
 }
 
 // Few tokens (decode): one wave per (expert row, 4 tokens), lanes split K.
@@ -278,9 +314,10 @@ select_body(const float* __restrict__ L, int S, float* __restrict__ Lout,
             const float* __restrict__ bias, const int32_t* __restrict__ forced,
             int32_t* __restrict__ rejected,
             int32_t* __restrict__ ids, float* __restrict__ wout,
-            float* __restrict__ probpart, int64_t T, int E, int k,
-            int norm, float scaling, int n_group, int topk_group) {
+            float* __restrict__ probpart, int32_t* __restrict__ err, int64_t T,
+            int E, int k, int norm, float scaling, int n_group, int topk_group) {
   constexpr int router = ROUTER;
+  bool nonfinite = false;  // a logit that is NaN or infinite
   __shared__ float sel_lds[NW][EPL * kWave];
   __shared__ float pacc[NW][EPL * kWave];
   const int lane = threadIdx.x % kWave;
@@ -316,6 +353,7 @@ select_body(const float* __restrict__ L, int S, float* __restrict__ Lout,
             if (q < S) lv += pv[q];
         }
         if (Lout) Lout[t * E + e] = lv;
+        nonfinite |= !(fabsf(lv) <= 3.402823466e38f);
       }
       v[j] = lv;
       sc[j] = 0.f;
@@ -455,6 +493,8 @@ select_body(const float* __restrict__ L, int S, float* __restrict__ Lout,
       wout[t * k + lane] = reject ? 0.f : wk;
     }
   }
+  if (err != nullptr && __ballot(nonfinite) != 0 && lane == 0)
+    atomicOr(err, MOE_FLAG_NONFINITE_LOGIT);
   if (want_p) {
 #pragma unroll
     for (int j = 0; j < EPL; ++j) pacc[wv][lane + kWave * j] = pa[j];
@@ -473,11 +513,11 @@ select_kernel(const float* __restrict__ L, int S, float* __restrict__ Lout,
               const float* __restrict__ bias, const int32_t* __restrict__ forced,
               int32_t* __restrict__ rejected,
               int32_t* __restrict__ ids, float* __restrict__ wout,
-              float* __restrict__ probpart, int64_t T, int E, int k,
-              int norm, float scaling, int n_group, int topk_group) {
+              float* __restrict__ probpart, int32_t* __restrict__ err, int64_t T,
+              int E, int k, int norm, float scaling, int n_group, int topk_group) {
   select_body<EPL, kSelectWaves, ROUTER, FORCED>(L, S, Lout, bias, forced, rejected, ids,
-                                                 wout, probpart, T, E, k, norm, scaling,
-                                                 n_group, topk_group);
+                                                 wout, probpart, err, T, E, k, norm,
+                                                 scaling, n_group, topk_group);
 }
 
 
@@ -494,41 +534,70 @@ __global__ void prob_finalize_kernel(const float* __restrict__ part, int nb,
 __global__ void zero_i32_kernel(int32_t* p) { *p = 0; }
 
 template <typename XT, typename WT>
-hipError_t logits_dispatch(const Dims& D, const void* x, const void* wr,
-                           float* L, hipStream_t s) {
+hipError_t logits_dispatch(const Dims& D, const RouterPlan& p, const void* x,
+                           const void* wr, float* L, hipStream_t s) {
   const XT* xp = static_cast<const XT*>(x);
   const WT* wp = static_cast<const WT*>(wr);
-  if (D.T <= 64 && (D.d % 8) == 0) {
+  if (p.kind == kRouterRowdot) {
     dim3 grid((D.E + 3) / 4, static_cast<unsigned>((D.T + 3) / 4));
     hipLaunchKernelGGL((logits_rowdot_kernel<XT, WT>), grid, dim3(256), 0, s,
                        xp, wp, L, D.T, D.E, D.d);
-  } else if (D.E <= 16 && (D.d % 8) == 0) {
-    dim3 grid(static_cast<unsigned>((D.T + 15) / 16));
+  } else if (p.kind == kRouterSmallE) {
+    const int tpw = D.E <= 8 ? 8 : 4;  // 64 / EB tokens per wave
+    dim3 grid(static_cast<unsigned>((D.T + 4 * tpw - 1) / (4 * tpw)), p.S);
     if (D.E <= 8)
-      hipLaunchKernelGGL((logits_small_e_kernel<XT, WT, 8>), grid, dim3(256), 0,
-                         s, xp, wp, L, D.T, D.E, D.d);
+      hipLaunchKernelGGL((logits_few_e_kernel<XT, WT, 8>), grid, dim3(256), 0,
+                         s, xp, wp, L, D.T, D.E, D.d, p.kper);
     else
-      hipLaunchKernelGGL((logits_small_e_kernel<XT, WT, 16>), grid, dim3(256), 0,
-                         s, xp, wp, L, D.T, D.E, D.d);
+      hipLaunchKernelGGL((logits_few_e_kernel<XT, WT, 16>), grid, dim3(256), 0,
+                         s, xp, wp, L, D.T, D.E, D.d, p.kper);
   } else {
-    dim3 grid(static_cast<unsigned>((D.T + LT - 1) / LT), (D.E + LE - 1) / LE);
-    hipLaunchKernelGGL((logits_tiled_kernel<XT, WT>), grid, dim3(256), 0, s,
-                       xp, wp, L, D.T, D.E, D.d);
+    dim3 grid(static_cast<unsigned>((D.T + RT - 1) / RT), (D.E + RE - 1) / RE, p.S);
+    hipLaunchKernelGGL((logits_tile_fma_kernel<XT, WT>), grid, dim3(256), 0, s,
+                       xp, wp, L, D.T, D.E, D.d, p.kper);
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_router_logits(const Dims& D, int act_dtype, int router_dtype,
-                                const void* x, const void* wr, float* logits,
-                                hipStream_t s) {
+RouterPlan router_plan(const Dims& D) {
+  RouterPlan p{};
+  p.S = 1;
+  p.kper = D.d;
+  if (D.T <= 64) {
+    p.kind = kRouterRowdot;
+  } else if (D.E <= 16) {
+    p.kind = kRouterSmallE;
+    // about 8 waves per CU of a 256-CU part; slices of whole 512-element
+    // steps of a wave
+    const int64_t waves = (D.T + (D.E <= 8 ? 8 : 4) - 1) / (D.E <= 8 ? 8 : 4);
+    const int steps = (D.d + 511) / 512;
+    int S = static_cast<int>(std::min<int64_t>(kMaxLogitPlanes, (2048 + waves - 1) / waves));
+    S = std::max(1, std::min(S, steps));
+    p.kper = (steps + S - 1) / S * 512;
+    p.S = (D.d + p.kper - 1) / p.kper;
+  } else {
+    p.kind = kRouterTiled;
+    // about two blocks per CU of a 256-CU part, each split at least 256 long
+    const int64_t tiles = ((D.T + RT - 1) / RT) * ((D.E + RE - 1) / RE);
+    int S = static_cast<int>(std::min<int64_t>(kMaxLogitPlanes, (512 + tiles - 1) / tiles));
+    S = std::max(1, std::min(S, D.d / 256));
+    p.kper = ((D.d + S - 1) / S + RK - 1) / RK * RK;
+    p.S = (D.d + p.kper - 1) / p.kper;
+  }
+  return p;
+}
+
+hipError_t launch_router_logits(const Dims& D, const RouterPlan& p, int act_dtype,
+                                int router_dtype, const void* x, const void* wr,
+                                float* logits, hipStream_t s) {
   const bool xb = act_dtype == MOE_DTYPE_BF16;
   const bool wb = router_dtype == MOE_DTYPE_BF16;
-  if (xb && wb) return logits_dispatch<uint16_t, uint16_t>(D, x, wr, logits, s);
-  if (xb) return logits_dispatch<uint16_t, float>(D, x, wr, logits, s);
-  if (wb) return logits_dispatch<float, uint16_t>(D, x, wr, logits, s);
-  return logits_dispatch<float, float>(D, x, wr, logits, s);
+  if (xb && wb) return logits_dispatch<uint16_t, uint16_t>(D, p, x, wr, logits, s);
+  if (xb) return logits_dispatch<uint16_t, float>(D, p, x, wr, logits, s);
+  if (wb) return logits_dispatch<float, uint16_t>(D, p, x, wr, logits, s);
+  return logits_dispatch<float, float>(D, p, x, wr, logits, s);
 }
 
 hipError_t launch_zero_i32(int32_t* p, hipStream_t s) {
@@ -540,14 +609,15 @@ hipError_t launch_router_select(const Dims& D, const moe_spec& sp,
                                 const float* logits, int S, float* logits_out,
                                 const float* bias, const int32_t* forced,
                                 int32_t* rejected, int32_t* ids, float* w,
-                                float* probpart, int nblocks, hipStream_t s) {
+                                float* probpart, int32_t* err, int nblocks,
+                                hipStream_t s) {
   const int epl = (D.E + kWave - 1) / kWave;
   const float scaling =
       sp.router == MOE_ROUTER_SIGMOID_GROUP ? sp.routed_scaling : 1.0f;
 #define MOE_SELECT3(N, R, F)                                                   \
   hipLaunchKernelGGL((select_kernel<N, R, F>), dim3(nblocks), dim3(256), 0, s,  \
                      logits, S, logits_out, bias, forced, rejected, ids, w,     \
-                     probpart, D.T, D.E, D.k, sp.norm_topk_prob, scaling,       \
+                     probpart, err, D.T, D.E, D.k, sp.norm_topk_prob, scaling,  \
                      sp.n_group, sp.topk_group)
 #define MOE_SELECT(N)                                                           \
   {                                                                             \

@@ -17,7 +17,7 @@ namespace {
 constexpr int kHealthThreads = 1024;
 constexpr float kCollapseRatio = 0.5f;
 
-// block-wide fp32 sum / max and int sums over the 16 waves, fixed order
+// block-wide fp32 sum over the 16 waves, fixed order
 __device__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
@@ -28,14 +28,36 @@ __device__ float block_sum(float v, float* red) {
   for (int i = 0; i < kHealthThreads / kWave; ++i) s += red[i];
   return s;
 }
-__device__ float block_max(float v, float* red) {
-  v = wave_max(v);
+// block-wide int sum / max over the 16 waves (exact in any order: the
+// totals fit int32 because T*k <= 2^31 - 1)
+__device__ int wave_isum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ int wave_imax(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ int block_isum(int v, int* red) {
+  v = wave_isum(v);
   const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
   __syncthreads();
   if (lane == 0) red[w] = v;
   __syncthreads();
-  float s = red[0];
-  for (int i = 1; i < kHealthThreads / kWave; ++i) s = fmaxf(s, red[i]);
+  int s = 0;
+  for (int i = 0; i < kHealthThreads / kWave; ++i) s += red[i];
+  return s;
+}
+__device__ int block_imax(int v, int* red) {
+  v = wave_imax(v);
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  int s = red[0];
+  for (int i = 1; i < kHealthThreads / kWave; ++i) s = max(s, red[i]);
   return s;
 }
 
@@ -45,15 +67,18 @@ health_kernel(const int32_t* __restrict__ counts, const int32_t* __restrict__ of
               float* __restrict__ bias, float step, moe_health* __restrict__ h,
               int64_t T, int k, int E) {
   __shared__ float red[kHealthThreads / kWave];
+  __shared__ int ired[kHealthThreads / kWave];
   const int e = threadIdx.x;
   const bool on = e < E;
   const int kept = on ? offsets[e + 1] - offsets[e] : 0;
   const int cnt = on ? counts[e] : 0;
-  // integer totals (exact): kept and pre-drop slots
-  const float kept_total = block_sum(static_cast<float>(kept), red);
-  const float cnt_total = block_sum(static_cast<float>(cnt), red);
-  const float cnt_max = block_max(on ? static_cast<float>(cnt) : 0.f, red);
-  const float kmax = block_max(on ? static_cast<float>(kept) : 0.f, red);
+  // integer totals and maxima, exact: kept and pre-drop slots
+  const int kept_i = block_isum(kept, ired);
+  const int cnt_i = block_isum(cnt, ired);
+  const float kept_total = static_cast<float>(kept_i);
+  const float cnt_total = static_cast<float>(cnt_i);
+  const float cnt_max = static_cast<float>(block_imax(cnt, ired));
+  const float kmax = static_cast<float>(block_imax(kept, ired));
   // entropy of the normalised kept shares
   const float q = (on && kept_total > 0.f) ? static_cast<float>(kept) / kept_total : 0.f;
   const float ent = block_sum(q > 0.f ? -q * logf(q) : 0.f, red);
@@ -66,7 +91,7 @@ health_kernel(const int32_t* __restrict__ counts, const int32_t* __restrict__ of
   }
   if (bias && on && step != 0.f) {
     // load below the mean <=> E*count < total (exact in integers)
-    const int64_t total = static_cast<int64_t>(cnt_total);
+    const int64_t total = cnt_i;
     const int64_t lhs = static_cast<int64_t>(E) * cnt;
     const float s = lhs < total ? 1.f : (lhs > total ? -1.f : 0.f);
     bias[e] = bias[e] + step * s;
@@ -84,7 +109,7 @@ health_kernel(const int32_t* __restrict__ counts, const int32_t* __restrict__ of
     r.dropped_fraction = static_cast<float>(dropped[0]) / (Tf * k);
     r.load_peak_over_mean = cnt_total > 0.f ? cnt_max / (cnt_total / static_cast<float>(E)) : 0.f;
     r.collapsed = ratio < kCollapseRatio ? 1 : 0;
-    r.kept_total = static_cast<int32_t>(kept_total);
+    r.kept_total = kept_i;
     *h = r;
   }
 }

@@ -58,7 +58,7 @@ def as_f64(a: np.ndarray) -> np.ndarray:
     a = np.asarray(a)
     if a.dtype == np.uint16:
         return bf16_to_f64(a)
-    return a.astype(np.float64)
+    return a.astype(np.float64, copy=False)
 
 
 def dequant_u4_affine(packed: np.ndarray, scale: np.ndarray, bias: np.ndarray,
@@ -381,9 +381,9 @@ class ExpertBank:
     uint16 bf16 bits), and for 4-bit weights q_* (uint32 packed), s_*, b_*
     (uint16 bf16 bits).
 
-    ``fused``: the gate and up projections are stored together, [dockyard
-    MoE Spec and Routing] "Weight layout" (FUSED_GATE_UP) and "Bundle layout
-    and the up-first order": one [2F, K] slice per expert under w_gate_up
+    ``fused``: the gate and up projections are stored together, [edge0]
+    "Weight layout" (FUSED_GATE_UP) and "Bundle layout and the up-first
+    order": one [2F, K] slice per expert under w_gate_up
     (q_/s_/b_gate_up for 4-bit, sh_gate_up for shared experts) whose first F
     rows are the gate and the last F the up projection, so that splitting
     x @ W^T in two halves gives (gate, up).

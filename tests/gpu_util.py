@@ -67,46 +67,116 @@ def run_layer(cfg, inp, T: Optional[int] = None):
         if cfg.router == synth.SOFTMAX_TOPK else None,
         "slot_row": torch.full((T, k), -7, dtype=torch.int32, device=dev),
         "sorted_token": torch.full((max(1, T * k),), -7, dtype=torch.int32, device=dev),
+        "errors": torch.zeros(1, dtype=torch.int32, device=dev),
     }
     ws = moe.workspace(spec, T)
     stats = moe.layer_stats(**{n: r[n] for n in moe._S_FIELDS})
     moe.moe_layer_forward(spec, T, inp["x"], inp["w_router"], inp["expert_bias"],
                           inp, r["out"], stats=stats, workspace=ws)
     torch.cuda.synchronize()
+    # seeded inputs of the workloads are finite and O(1): no condition of
+    # the device error word may be raised
+    assert int(r["errors"].item()) == 0, f"device error word {int(r['errors'].item())}"
     return r
 
 
-def bank_for(cfg, inp) -> oracle.ExpertBank:
-    """Oracle expert bank that copies one expert's tensors to the host on
-    demand (exact copies of what the GPU read)."""
+def bank_for(cfg, inp, experts: Optional[Sequence[int]] = None,
+             threads: int = 8) -> oracle.ExpertBank:
+    """Oracle expert bank over exact host copies of what the GPU read.
+
+    Without ``experts`` each stored tensor is copied to the host on demand.
+    With ``experts`` (the routed experts in the order the oracle visits
+    them, i.e. ascending) a pool of ``threads`` copies and decodes them to
+    fp64 ahead of the oracle, a bounded number at a time: the oracle's
+    arithmetic is unchanged (it receives the matrices its own ``as_f64``
+    decoded), only the decoding of large expert stacks runs in parallel."""
     cache: Dict = {}
 
-    def fetch(name, e):
-        key = (name, e)
-        if key not in cache:
-            if len(cache) > 48:
-                cache.clear()
-            cache[key] = synth.host_array(inp[name][e])
-        return cache[key]
+    def raw(name, e):
+        return synth.host_array(inp[name][e])
+
+    if experts is None:
+        def fetch(name, e):
+            key = (name, e)
+            if key not in cache:
+                if len(cache) > 48:
+                    cache.clear()
+                cache[key] = raw(name, e)
+            return cache[key]
+    else:
+        import concurrent.futures
+        import threading
+        u4 = cfg.weight_dtype == synth.U4
+        fused = cfg.layout == synth.FUSED_GATE_UP
+        if u4:
+            names = ["q_gate_up", "s_gate_up", "b_gate_up"] if fused else \
+                [p + m for m in ("gate", "up") for p in ("q_", "s_", "b_")]
+            names += ["q_down", "s_down", "b_down"]
+        else:
+            names = ["w_gate_up"] if fused else \
+                ["w_gate"] + (["w_up"] if cfg.act == synth.SWIGLU else [])
+            names += ["w_down"]
+        order = [(n, e) for e in experts for n in names]
+        pos = {key: i for i, key in enumerate(order)}
+        pool = concurrent.futures.ThreadPoolExecutor(threads)
+        futs: Dict = {}
+        lock = threading.Lock()
+        ahead = 4 * threads
+        nxt = [0]
+
+        def decode(key):
+            a = raw(*key)
+            return a if u4 else oracle.as_f64(a)
+
+        def submit_upto(i):
+            with lock:
+                while nxt[0] < len(order) and nxt[0] <= i + ahead:
+                    key = order[nxt[0]]
+                    futs[key] = pool.submit(decode, key)
+                    nxt[0] += 1
+
+        def fetch(name, e):
+            key = (name, e)
+            if key in pos:
+                submit_upto(pos[key])
+                fut = futs.pop(key, None)
+                if fut is not None:
+                    return fut.result()
+            if name.startswith("sh_") or key not in pos:
+                return raw(name, e)
+            return decode(key)
 
     return oracle.ExpertBank(fetch, cfg.act, u4=cfg.weight_dtype == synth.U4,
                              group=cfg.quant_group,
                              fused=cfg.layout == synth.FUSED_GATE_UP)
 
 
+def last_tile_tokens(disp, per_expert: int = 1, bm: int = 256):
+    """Tokens whose rows lie in the last M tile of each expert's group (the
+    ragged tail the grouped GEMM handles specially), up to ``per_expert``
+    of them per expert."""
+    off = disp["offsets"]
+    st = disp["sorted_token"]
+    out = []
+    for e in range(len(off) - 1):
+        n = int(off[e + 1] - off[e])
+        if n == 0:
+            continue
+        start = int(off[e]) + (n - 1) // bm * bm
+        rows = list(range(int(off[e + 1]) - 1, start - 1, -1))[:per_expert]
+        out += [int(st[r]) for r in rows]
+    return out
+
+
 def logits_bound(x_h, wr_h, d):
-    """Forward error bound of an fp32-accumulated dot product, in any
-    summation order, gamma_n * sum |x||w|.  bf16 activations with fp32
-    router weights are evaluated as 3d exact bf16 products (each weight
-    split into three bf16 parts whose magnitudes add up to at most
-    (1 + 2^-7)|w|), so n = 3d there; otherwise n = d."""
+    """Forward error bound of an fp32-accumulated dot product of d exact
+    products, in any summation order: gamma_d * sum |x||w|, gamma_d =
+    d u / (1 - d u), u = 2^-24."""
     u = 2.0 ** -24
-    split = x_h.dtype == np.uint16 and wr_h.dtype == np.float32
-    n = 3 * d if split else d
-    gamma = n * u / (1 - n * u)
+    gamma = d * u / (1 - d * u)
     X = np.abs(oracle.as_f64(x_h))
     W = np.abs(oracle.as_f64(wr_h))
-    return gamma * (1.0 + 2.0 ** -7 if split else 1.0) * (X @ W.T)
+    return gamma * (X @ W.T)
 
 
 def check_route(cfg, inp, r, full_logits_check=True):
@@ -160,10 +230,16 @@ def check_dispatch(cfg, ids_g, r):
     return d
 
 
-def check_output(cfg, inp, r, ids_g, w_o, disp, tokens: Optional[Sequence[int]] = None):
+def check_output(cfg, inp, r, ids_g, w_o, disp, tokens: Optional[Sequence[int]] = None,
+                 prefetch: bool = False):
     tol = BF16_TOL if cfg.act_dtype == synth.BF16 else F32_TOL
     toks = list(range(cfg.T)) if tokens is None else list(tokens)
-    bank = bank_for(cfg, inp)
+    experts = None
+    if prefetch:
+        sr = disp["slot_row"]
+        experts = sorted({int(ids_g[t, i]) for t in toks for i in range(cfg.top_k)
+                          if sr[t, i] >= 0})
+    bank = bank_for(cfg, inp, experts)
     t0 = time.time()
     ref = oracle.ffn_and_combine(synth.host_array(inp["x"]), ids_g, w_o, disp, bank,
                                  spec_dict(cfg), toks)
@@ -240,8 +316,13 @@ def check_end_to_end_routing(cfg, inp, ids_g, L_gpu):
     assert not np.any(bad & ~flags)
 
 
-def full_check(cfg, inp, r, tokens=None, full_logits_check=True):
+def full_check(cfg, inp, r, tokens=None, full_logits_check=True, choose_tokens=None):
+    """Route, dispatch and output parity.  ``choose_tokens(disp)`` may pick
+    the output sample from the dispatch (e.g. the tokens of every expert's
+    last M tile); their expert matrices are then decoded in parallel."""
     ids_g, w_o, flags = check_route(cfg, inp, r, full_logits_check)
     disp = check_dispatch(cfg, ids_g, r)
-    check_output(cfg, inp, r, ids_g, w_o, disp, tokens)
+    if choose_tokens is not None:
+        tokens = choose_tokens(disp)
+    check_output(cfg, inp, r, ids_g, w_o, disp, tokens, prefetch=choose_tokens is not None)
     return ids_g, disp

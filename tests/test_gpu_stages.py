@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import mixture_experts_layer_group_amd as moe
 import oracle
 import synth
 from tests import gpu_util as gu
@@ -64,12 +65,21 @@ MEDIUM = {
     # its reduction is split in two K halves, with capacity drops
     "swiglu-bf16-splitk": C("swiglu-bf16-splitk", 113, T=600, d=256, E=4, top_k=2,
                             F=1024, capacity_factor=1.25),
-    # router tile widths of the matrix-core logits: 37 experts with fp32
-    # router weights (three bf16 parts, 64-wide tile, ragged expert tail) and
-    # 100 experts with bf16 router weights (128-wide tile)
+    # 128 x 128 vector-ALU logits tiles with ragged expert and token tails:
+    # 37 experts with fp32 router weights and 100 experts with bf16 router
+    # weights, one reduction split each
     "router-e37-fp32": C("router-e37-fp32", 114, T=400, d=192, E=37, top_k=3, F=64),
     "router-e100-bf16": C("router-e100-bf16", 115, T=300, d=128, E=100, top_k=5, F=64,
                           router_dtype=synth.BF16),
+    # the reduction over d split in 4 partial planes, the last one shorter
+    # (d = 1088: splits of 288, 288, 288, 224), fp32 and bf16 router weights,
+    # two expert tiles
+    "router-split-fp32": C("router-split-fp32", 123, T=300, d=1088, E=40, top_k=3, F=64),
+    "router-split-bf16": C("router-split-bf16", 124, T=260, d=1024, E=150, top_k=4, F=64,
+                           router_dtype=synth.BF16),
+    # fp32 activations through the tiled logits kernel (two splits)
+    "router-f32-tiled": C("router-f32-tiled", 125, T=200, d=512, E=64, top_k=2, F=32,
+                          act_dtype=synth.F32, weight_dtype=synth.F32),
     # bf16 shared expert with ReLU and many tokens (several M tiles)
     "relu-shared-tiles": C("relu-shared-tiles", 112, T=1100, d=256, E=8, top_k=2, F=256,
                            act=synth.RELU, shared_experts=1, shared_F=320),
@@ -241,3 +251,177 @@ def test_routing_health_collapsed_and_equal_loads():
     got, ref = _health_case(cfg, inp, 0.25)
     assert got["collapsed"] == 1 and abs(got["max_share"] - 0.5) < 1e-7
     assert abs(got["entropy_ratio"] - 1.0 / 3.0) < 1e-6
+
+
+def _route_only(cfg, inp, errors=None):
+    spec = moe.spec_from_config(cfg)
+    T, k = cfg.T, cfg.top_k
+    ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    tw = torch.zeros((T, k), dtype=torch.float32, device="cuda")
+    L = torch.zeros((T, cfg.E), dtype=torch.float32, device="cuda")
+    moe.moe_route(spec, T, inp["x"], inp["w_router"], inp["expert_bias"], ids, tw, L,
+                  workspace=moe.workspace(spec, T), errors=errors)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy(), tw.cpu().numpy().astype(np.float64), L.cpu().numpy()
+
+
+@pytest.mark.parametrize("E,n_group,topk_group,k", [(256, 8, 4, 8), (32, 4, 2, 3)])
+def test_sigmoid_group_exact_ties(E, n_group, topk_group, k):
+    """Zero router weights and zero bias: every logit is 0, every sigmoid
+    score 0.5, every group score 1.0.  Groups and experts tie everywhere, so
+    the lower groups and then the lower experts win: ids 0..k-1 and weights
+    0.5 / (k * 0.5 + 1e-20) * routed_scaling (0.3125 at k = 8, scaling 2.5)
+    -- the oracle's closed-form pin, now on the GPU's group tie-break.  A
+    bias that lifts one later group's experts moves the choice to that
+    group's first k experts, with the same weights."""
+    cfg = C("sigmoid-ties", 126, T=96, d=256, E=E, top_k=k, F=64,
+            router=synth.SIGMOID_GROUP, routed_scaling=2.5, n_group=n_group,
+            topk_group=topk_group, router_dtype=synth.BF16, bias_range=0.05)
+    inp = gu.make_inputs(cfg)
+    inp["w_router"].zero_()
+    inp["expert_bias"].zero_()
+    ids, w, L = _route_only(cfg, inp)
+    assert np.all(L == 0.0)
+    w_closed = 0.5 / (k * 0.5 + 1e-20) * 2.5
+    assert np.all(ids == np.arange(k)[None, :])
+    assert np.all(np.abs(w - w_closed) <= 1e-6)
+    # the oracle on the same (zero) logits agrees bit for bit
+    ids_o, w_o, _ = oracle.route_from_logits(L, gu.spec_dict(cfg),
+                                             synth.host_array(inp["expert_bias"]))
+    assert np.array_equal(ids, ids_o) and np.all(np.abs(w - w_o) <= 1e-6)
+    # lift the experts of group g: the tie inside the group picks its first k
+    G = E // n_group
+    g = n_group - 2
+    inp["expert_bias"][g * G:(g + 1) * G] = 0.125
+    ids, w, L = _route_only(cfg, inp)
+    assert np.all(ids == g * G + np.arange(k)[None, :])
+    assert np.all(np.abs(w - w_closed) <= 1e-6)  # raw sigmoid: the bias is not a weight
+    ids_o, _, _ = oracle.route_from_logits(L, gu.spec_dict(cfg),
+                                           synth.host_array(inp["expert_bias"]))
+    assert np.array_equal(ids, ids_o)
+    gu.log(f"  exact ties: ids 0..{k - 1}, w {w_closed}; lifted group {g}: ids "
+           f"{g * G}..{g * G + k - 1}")
+
+
+def test_error_word_bad_ids_and_clean_runs():
+    """moe_dispatch flags expert ids outside [0,E) (MOE_FLAG_BAD_EXPERT_ID)
+    and drops those slots; every other slot is dispatched as the oracle
+    dispatches the valid ids.  Clean calls leave the word at 0."""
+    cfg = C("bad-ids", 127, T=700, d=128, E=16, top_k=2, F=64, capacity_factor=1.5)
+    spec = moe.spec_from_config(cfg)
+    T, k, E = cfg.T, cfg.top_k, cfg.E
+    rs = np.random.default_rng(5)
+    ids_h = np.stack([rs.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    dev = "cuda"
+    for T_run in (T, 40):  # the multi-block and the one-block dispatch
+        ids_t = torch.from_numpy(ids_h[:T_run].copy()).to(dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        out = {n: torch.full(shape, -7, dtype=dt, device=dev) for n, shape, dt in (
+            ("counts", (E,), torch.int32), ("offsets", (E + 1,), torch.int32),
+            ("st", (T_run * k,), torch.int32), ("sw", (T_run * k,), torch.float32),
+            ("sr", (T_run, k), torch.int32), ("dropped", (1,), torch.int32))}
+        tw = torch.ones((T_run, k), dtype=torch.float32, device=dev)
+        ws = moe.workspace(spec, T_run)
+
+        def run(ids_dev):
+            moe.moe_dispatch(spec, T_run, ids_dev, tw, out["counts"], out["offsets"],
+                             out["st"], out["sw"], out["sr"], out["dropped"], workspace=ws,
+                             errors=err)
+            torch.cuda.synchronize()
+
+        run(ids_t)
+        assert int(err.item()) == 0, "a clean dispatch sets no flag"
+        bad = ids_h[:T_run].copy()
+        bad[3, 1] = E
+        bad[T_run - 1, 0] = -1
+        bad[T_run // 2, 1] = 1 << 20
+        run(torch.from_numpy(bad).to(dev))
+        assert int(err.item()) & moe.FLAG_BAD_EXPERT_ID
+        sr = out["sr"].cpu().numpy()
+        assert sr[3, 1] == -1 and sr[T_run - 1, 0] == -1 and sr[T_run // 2, 1] == -1
+        valid = (bad >= 0) & (bad < E)
+        counts = np.bincount(bad[valid], minlength=E)
+        assert np.array_equal(out["counts"].cpu().numpy(), counts)
+        cap = oracle.capacity_for(T_run, k, E, cfg.capacity_factor)
+        # the oracle's queue rule restricted to the valid slots
+        kept = np.zeros(E, dtype=np.int64)
+        rows = {}
+        for t in range(T_run):
+            for i in range(k):
+                e = int(bad[t, i])
+                if 0 <= e < E and kept[e] < cap:
+                    rows[(t, i)] = (e, int(kept[e]))
+                    kept[e] += 1
+        offs = np.concatenate([[0], np.cumsum(kept)])
+        assert np.array_equal(out["offsets"].cpu().numpy(), offs)
+        assert int(out["dropped"].item()) == T_run * k - int(offs[-1])
+        for (t, i), (e, rank) in rows.items():
+            assert sr[t, i] == offs[e] + rank
+        gu.log(f"  T={T_run}: 3 bad ids flagged and dropped, {int(offs[-1])} slots kept")
+
+
+def test_error_word_saturation_and_nonfinite():
+    """A hidden activation beyond the fp16 range sets MOE_FLAG_H_SATURATED
+    (bf16 and 4-bit paths) and is stored as +-65504; a NaN token row sets
+    MOE_FLAG_NONFINITE_LOGIT.  The normal inputs set neither."""
+    for cfg in (C("sat-bf16", 128, T=300, d=256, E=8, top_k=2, F=128),
+                C("sat-u4", 129, T=24, d=256, E=16, top_k=2, F=128,
+                  weight_dtype=synth.U4)):
+        inp = gu.make_inputs(cfg)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        spec = moe.spec_from_config(cfg)
+        out = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+        ws = moe.workspace(spec, cfg.T)
+        moe.moe_layer_forward(spec, cfg.T, inp["x"], inp["w_router"], None, inp, out,
+                              stats=moe.layer_stats(errors=err), workspace=ws)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0, f"{cfg.name}: normal inputs set {int(err.item())}"
+        # tokens 300x larger: gate and up ~ N(0, 300^2), so silu(g)*u passes
+        # 65504 for some hidden units
+        x_big = (inp["x"].float() * 300.0).to(torch.bfloat16)
+        moe.moe_layer_forward(spec, cfg.T, x_big, inp["w_router"], None, inp, out,
+                              stats=moe.layer_stats(errors=err), workspace=ws)
+        torch.cuda.synchronize()
+        assert int(err.item()) == moe.FLAG_H_SATURATED, f"{cfg.name}: {int(err.item())}"
+        gu.log(f"  {cfg.name}: saturation flagged")
+    # a NaN token: its logits are NaN; the other tokens route as before
+    cfg = C("nonfinite", 130, T=200, d=256, E=40, top_k=2, F=64)
+    inp = gu.make_inputs(cfg)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids0, w0, _ = _route_only(cfg, inp, errors=err)
+    assert int(err.item()) == 0
+    inp["x"][17] = float("nan")
+    ids1, w1, _ = _route_only(cfg, inp, errors=err)
+    assert int(err.item()) == moe.FLAG_NONFINITE_LOGIT
+    keep = np.ones(cfg.T, dtype=bool)
+    keep[17] = False
+    assert np.array_equal(ids0[keep], ids1[keep]) and np.array_equal(w0[keep], w1[keep])
+
+
+def test_routing_health_counts_beyond_fp32_integers():
+    """Pre-drop counts above 2^24 (not all representable in fp32): the
+    totals and the bias sign rule are exact.  E = 4, counts 2^24 + (1, 1,
+    3, -1): total 2^26 + 4, mean 2^24 + 1, so experts 0 and 1 stay, 2 moves
+    down and 3 up.  In fp32 the counts would read 2^24 + (0, 0, 4, -1) and
+    the total could not be 2^26 + 4, which moves experts 0 and 1."""
+    cfg = C("big-counts", 131, T=(1 << 24) + 1, d=64, E=4, top_k=4, F=64,
+            act_dtype=synth.F32, weight_dtype=synth.F32)
+    spec = moe.spec_from_config(cfg)
+    base = 1 << 24
+    counts_h = np.array([base + 1, base + 1, base + 3, base - 1], dtype=np.int32)
+    dev = "cuda"
+    counts = torch.from_numpy(counts_h).to(dev)
+    offsets = torch.from_numpy(np.concatenate([[0], np.cumsum(counts_h)]).astype(np.int32)).to(dev)
+    dropped = torch.zeros(1, dtype=torch.int32, device=dev)
+    bias = torch.zeros(4, dtype=torch.float32, device=dev)
+    h = moe.health_buffer()
+    moe.moe_routing_health(spec, cfg.T, counts, offsets, dropped, None, h, bias=bias,
+                           bias_step=0.5)
+    torch.cuda.synchronize()
+    got = moe.health_from_bytes(h)
+    assert got["kept_total"] == 4 * base + 4
+    assert bias.cpu().tolist() == [0.0, 0.0, -0.5, 0.5]
+    ref = oracle.bias_update(np.zeros(4), counts_h.astype(np.int64), 0.5)
+    assert np.array_equal(bias.cpu().numpy().astype(np.float64), ref)
+    st = oracle.layer_stats(counts_h, counts_h, 0, None, cfg.T, 4, 4)
+    assert abs(got["load_peak_over_mean"] - st["load_peak_over_mean"]) <= 1e-6

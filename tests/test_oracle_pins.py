@@ -183,6 +183,53 @@ def test_near_tie_flags():
     assert oracle.near_tie_flags(L, spec_g).tolist() == [True, False]
 
 
+
+def _sel_flag(bias_units, tie=0.0):
+    """near_tie_flags of one token with zero logits (every sigmoid score is
+    exactly 0.5) under SIGMOID_GROUP with E = 8, groups of 2, topk_group 2,
+    k = 2 (k < topk_group * G, so the expert margin inside the kept groups
+    is examined).  The selection scores are 0.5 + bias; ``bias_units`` are
+    multiples of 1/64 (exact in fp32) and ``tie`` an extra offset added to
+    expert 2's bias."""
+    b = np.array(bias_units, dtype=np.float64) / 64.0
+    b[2] += tie
+    spec = {"router": "sigmoid_group", "top_k": 2, "n_group": 4, "topk_group": 2}
+    L = np.zeros((1, 8), dtype=np.float32)
+    return bool(oracle.near_tie_flags(L, spec, b.astype(np.float32))[0])
+
+
+def test_near_tie_flags_sigmoid_expert_margin():
+    """The expert-level margin of SIGMOID_GROUP, hand-built.  Selection
+    scores (0.5 + bias) per group of two: group 0 {0.9375, 0.875}, group 1
+    {0.8125 + tie, 0.625}, group 2 / group 3 below; group sums keep groups 0
+    and 1 by a wide margin.  The kept scores ranked: 0.9375, 0.875,
+    0.8125 + tie, 0.625, so the k = 2 margin is 0.875 - (0.8125 + tie)."""
+    base = [28, 24, 20, 8, 0, 0, -8, -8]  # /64: 0.4375, 0.375, 0.3125, 0.125, ...
+    # margin 1/16: clear
+    assert not _sel_flag(base)
+    # margin 2^-21 (4.8e-7) < 1e-6: flagged; margin 2^-19 (1.9e-6): not
+    assert _sel_flag(base, tie=1 / 16 - 2.0 ** -21)
+    assert not _sel_flag(base, tie=1 / 16 - 2.0 ** -19)
+    # an exact tie at the k boundary
+    assert _sel_flag(base, tie=1 / 16)
+    # a tie between the first and second choice is not a boundary: the k-th
+    # and (k+1)-th scores (0.875 + 1/16 and 0.8125) stay 1/16 apart
+    top_tie = [28, 28, 20, 8, 0, 0, -8, -8]
+    assert not _sel_flag(top_tie)
+    # the (k+1)-th best score overall sits in a dropped group (group 2:
+    # {0.875 + 2^-22, 0.0625}, group sum 0.9375 < group 1's 1.4375) and
+    # ties the k-th; inside the kept groups the margin is 1/16, so the token
+    # is not flagged
+    dropped_tie = [28, 24, 20, 8, 24, -28, -8, -8]
+    b = np.array(dropped_tie, dtype=np.float64) / 64.0
+    b[4] += 2.0 ** -22
+    spec = {"router": "sigmoid_group", "top_k": 2, "n_group": 4, "topk_group": 2}
+    L = np.zeros((1, 8), dtype=np.float32)
+    assert not oracle.near_tie_flags(L, spec, b.astype(np.float32))[0]
+    # the same scores with every group kept: now that tie is the boundary
+    spec_all = dict(spec, topk_group=4)
+    assert oracle.near_tie_flags(L, spec_all, b.astype(np.float32))[0]
+
 # ---------------------------------------------------------------- dispatch
 def _dispatch_sorted(ids, E, cap):
     """The sort-based formulation of the third blog program: flatten slots,
