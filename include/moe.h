@@ -338,6 +338,29 @@ moe_status moe_layer_forward(const moe_spec* spec, int64_t T, const void* x,
                              const moe_layer_stats* stats, void* workspace,
                              size_t ws_bytes, moe_stream_t stream);
 
+/* Bytes of the library's static scratch array on each GPU (64 MiB). */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* moe_layer_forward without a workspace argument and without any device
+ * allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The workspace is a static array of MOE_STATIC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends; the call
+ * itself allocates nothing (no hipMalloc, no hipFree, no allocating library
+ * routine).  Every call on one GPU uses that GPU's same array: calls that
+ * overlap on one GPU (concurrent streams, or threads sharing a device) race
+ * and must be serialised by the caller.  The array keeps the last call's
+ * contents; nothing in the layer depends on them.
+ * Arguments, results and errors as moe_layer_forward; a layer whose
+ * moe_workspace_size exceeds MOE_STATIC_SCRATCH_BYTES returns
+ * MOE_ERR_WORKSPACE with nothing launched (e.g. decode-shaped batches fit,
+ * the 4096-token Mixtral-shaped layer does not).  MOE_ERR_HIP if the
+ * array's device address cannot be obtained. */
+moe_status moe_layer_forward_static(const moe_spec* spec, int64_t T, const void* x,
+                                    const void* w_router, const float* expert_bias,
+                                    const moe_expert_weights* weights, void* out,
+                                    const moe_layer_stats* stats, moe_stream_t stream);
+
 /* Routing health of one layer call, from its dispatch counts (device
  * struct, filled by moe_routing_health).  Definitions follow the "Mixture
  * of Experts" blog page (second program's RoutingHealth, third program's

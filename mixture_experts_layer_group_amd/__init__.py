@@ -29,7 +29,9 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_INVALID_TOPK"
                 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP", 7: "MOE_ERR_UNSUPPORTED"}
 EXPORTS = ("moe_spec_validate", "moe_capacity", "moe_workspace_size", "moe_route",
            "moe_route_forced", "moe_dispatch", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-           "moe_routing_health", "moe_status_string")
+           "moe_layer_forward_static", "moe_routing_health", "moe_status_string")
+# MOE_STATIC_SCRATCH_BYTES: the static scratch of moe_layer_forward_static
+STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class MoESpec(ctypes.Structure):
@@ -109,6 +111,9 @@ def library() -> ctypes.CDLL:
         lib.moe_layer_forward.argtypes = [sp, i64, vp, vp, vp,
                                           ctypes.POINTER(MoEExpertWeights), vp,
                                           ctypes.POINTER(MoELayerStats), vp, sz, vp]
+        lib.moe_layer_forward_static.argtypes = [sp, i64, vp, vp, vp,
+                                                 ctypes.POINTER(MoEExpertWeights), vp,
+                                                 ctypes.POINTER(MoELayerStats), vp]
         lib.moe_routing_health.argtypes = [sp, i64, vp, vp, vp, vp, vp, ctypes.c_float,
                                            vp, vp]
         for n in EXPORTS[:-1]:
@@ -286,6 +291,18 @@ def moe_layer_forward(spec, T, x, w_router, expert_bias, weights, out, stats=Non
                                        ctypes.byref(st) if st is not None else None,
                                        _ptr(workspace), ws_bytes, _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_static(spec, T, x, w_router, expert_bias, weights, out, stats=None,
+                             stream=None) -> None:
+    """moe_layer_forward on the library's static scratch (no allocation)."""
+    w = weights if isinstance(weights, MoEExpertWeights) else expert_weights(weights)
+    st = stats if (stats is None or isinstance(stats, MoELayerStats)) else layer_stats(**stats)
+    _check(library().moe_layer_forward_static(ctypes.byref(spec), T, _ptr(x), _ptr(w_router),
+                                              _ptr(expert_bias), ctypes.byref(w), _ptr(out),
+                                              ctypes.byref(st) if st is not None else None,
+                                              _stream(stream)),
+           "moe_layer_forward_static")
 
 
 def moe_routing_health(spec, T, counts_pre, offsets, dropped, prob_sum, health,

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "moe_internal.hpp"
 
@@ -272,6 +273,87 @@ moe_status do_ffn(const moe_spec& sp, const Dims& D, const WsLayout& L,
   return MOE_OK;
 }
 
+// The whole layer on a caller-owned workspace (or, for the no-allocation
+// entry point, the library's static scratch array): `workspace` may be null
+// only when ws_bytes is 0, which fails the size check below.
+moe_status layer_forward(const moe_spec* spec, int64_t T, const void* x,
+                         const void* w_router, const float* expert_bias,
+                         const moe_expert_weights* weights, void* out,
+                         const moe_layer_stats* stats, void* workspace,
+                         size_t ws_bytes, moe_stream_t stream) {
+  moe_status st = validate(spec, T);
+  if (st != MOE_OK) return st;
+  if (expert_bias != nullptr && spec->router == MOE_ROUTER_SOFTMAX_TOPK)
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !out || !aligned16(x) || !aligned16(w_router) || !aligned16(out))
+    return MOE_ERR_SHAPE;
+  st = check_weights(*spec, weights);
+  if (st != MOE_OK) return st;
+  const Dims D = dims_of(*spec, T);
+  const WsLayout L = layout_of(D);
+  if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = workspace;
+  moe_layer_stats z{};
+  const moe_layer_stats& o = stats ? *stats : z;
+  int32_t* ids = o.topk_ids ? o.topk_ids : at<int32_t>(ws, L.topk_ids);
+  float* tw = o.topk_w ? o.topk_w : at<float>(ws, L.topk_w);
+  int32_t* counts = o.counts_pre ? o.counts_pre : at<int32_t>(ws, L.counts);
+  int32_t* offsets = o.offsets ? o.offsets : at<int32_t>(ws, L.offsets);
+  int32_t* dropped = o.dropped ? o.dropped : at<int32_t>(ws, L.dropped);
+  int32_t* slot_row = o.slot_row ? o.slot_row : at<int32_t>(ws, L.slot_row);
+  int32_t* sorted_token = o.sorted_token ? o.sorted_token : at<int32_t>(ws, L.sorted_token);
+  float* sorted_w = at<float>(ws, L.sorted_w);
+
+  st = do_route(*spec, D, L, x, w_router, expert_bias, nullptr, nullptr, ids,
+                tw, o.logits, o.prob_sum, o.errors, ws, s);
+  if (st != MOE_OK) return st;
+  const bool mfma_path = D.bf16 && !D.u4;
+  hipError_t e = launch_dispatch(
+      D, ids, tw, at<int32_t>(ws, L.hist), L.dispatch_blocks, counts, offsets,
+      sorted_token, sorted_w, slot_row, dropped,
+      mfma_path ? at<int32_t>(ws, L.tiles1) : nullptr,
+      mfma_path ? at<int32_t>(ws, L.tiles2) : nullptr, o.errors, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  void* Y = at<void>(ws, L.Y);
+  void* Ys = at<void>(ws, L.Ys);
+  st = do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, Y, Ys, o.errors,
+              o.ffn_events, ws, mfma_path, s);
+  if (st != MOE_OK) return st;
+  const float* part = (mfma_path && down_splits(D) > 1) ? at<float>(ws, L.Ypart) : nullptr;
+  return hip_status(launch_combine(D, Y, part, slot_row, tw, D.S > 0 ? Ys : nullptr,
+                                   out, s));
+}
+
+// Scratch of the no-allocation entry point: a file-scope device array, so
+// each GPU the library runs on holds its own copy from the moment the code
+// object is loaded there until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device memory: the device address is
+// taken once per device with hipGetSymbolAddress and only that address is
+// passed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// device address of the current device's scratch array (looked up on the
+// first call on that device, with it current)
+moe_status static_scratch(void** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch[dev] = ptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch[dev] == nullptr) return MOE_ERR_HIP;
+  *p = g_scratch[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -411,49 +493,25 @@ moe_status moe_layer_forward(const moe_spec* spec, int64_t T, const void* x,
                              const moe_expert_weights* weights, void* out,
                              const moe_layer_stats* stats, void* workspace,
                              size_t ws_bytes, moe_stream_t stream) {
-  moe_status st = validate(spec, T);
-  if (st != MOE_OK) return st;
-  if (expert_bias != nullptr && spec->router == MOE_ROUTER_SOFTMAX_TOPK)
-    return MOE_ERR_INVALID_ARG;
-  if (T == 0) return MOE_OK;
-  if (!x || !w_router || !out || !aligned16(x) || !aligned16(w_router) || !aligned16(out))
-    return MOE_ERR_SHAPE;
-  st = check_weights(*spec, weights);
-  if (st != MOE_OK) return st;
-  const Dims D = dims_of(*spec, T);
-  const WsLayout L = layout_of(D);
-  if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  void* ws = workspace;
-  moe_layer_stats z{};
-  const moe_layer_stats& o = stats ? *stats : z;
-  int32_t* ids = o.topk_ids ? o.topk_ids : at<int32_t>(ws, L.topk_ids);
-  float* tw = o.topk_w ? o.topk_w : at<float>(ws, L.topk_w);
-  int32_t* counts = o.counts_pre ? o.counts_pre : at<int32_t>(ws, L.counts);
-  int32_t* offsets = o.offsets ? o.offsets : at<int32_t>(ws, L.offsets);
-  int32_t* dropped = o.dropped ? o.dropped : at<int32_t>(ws, L.dropped);
-  int32_t* slot_row = o.slot_row ? o.slot_row : at<int32_t>(ws, L.slot_row);
-  int32_t* sorted_token = o.sorted_token ? o.sorted_token : at<int32_t>(ws, L.sorted_token);
-  float* sorted_w = at<float>(ws, L.sorted_w);
+  return layer_forward(spec, T, x, w_router, expert_bias, weights, out, stats, workspace,
+                       ws_bytes, stream);
+}
 
-  st = do_route(*spec, D, L, x, w_router, expert_bias, nullptr, nullptr, ids,
-                tw, o.logits, o.prob_sum, o.errors, ws, s);
+moe_status moe_layer_forward_static(const moe_spec* spec, int64_t T, const void* x,
+                                    const void* w_router, const float* expert_bias,
+                                    const moe_expert_weights* weights, void* out,
+                                    const moe_layer_stats* stats, moe_stream_t stream) {
+  const moe_status st = validate(spec, T);
   if (st != MOE_OK) return st;
-  const bool mfma_path = D.bf16 && !D.u4;
-  hipError_t e = launch_dispatch(
-      D, ids, tw, at<int32_t>(ws, L.hist), L.dispatch_blocks, counts, offsets,
-      sorted_token, sorted_w, slot_row, dropped,
-      mfma_path ? at<int32_t>(ws, L.tiles1) : nullptr,
-      mfma_path ? at<int32_t>(ws, L.tiles2) : nullptr, o.errors, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  void* Y = at<void>(ws, L.Y);
-  void* Ys = at<void>(ws, L.Ys);
-  st = do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, Y, Ys, o.errors,
-              o.ffn_events, ws, mfma_path, s);
-  if (st != MOE_OK) return st;
-  const float* part = (mfma_path && down_splits(D) > 1) ? at<float>(ws, L.Ypart) : nullptr;
-  return hip_status(launch_combine(D, Y, part, slot_row, tw, D.S > 0 ? Ys : nullptr,
-                                   out, s));
+  if (T == 0) return layer_forward(spec, T, x, w_router, expert_bias, weights, out, stats,
+                                   nullptr, 0, stream);
+  void* ws = nullptr;
+  const moe_status sc = static_scratch(&ws);
+  if (sc != MOE_OK) return sc;
+  // a layer whose workspace exceeds the array fails the size check
+  // (MOE_ERR_WORKSPACE) before anything is launched
+  return layer_forward(spec, T, x, w_router, expert_bias, weights, out, stats, ws,
+                       MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_routing_health(const moe_spec* spec, int64_t T,

@@ -24,7 +24,7 @@ def header_symbols():
 def test_library_exports_every_declared_symbol():
     lib = moe.library()
     syms = header_symbols()
-    assert len(syms) == len(moe.EXPORTS) == 11
+    assert len(syms) == len(moe.EXPORTS) == 12
     for s in syms:
         assert hasattr(lib, s), s
     assert sorted(moe.EXPORTS) == syms
@@ -172,3 +172,14 @@ def test_fused_layout_rejects_separate_up_pointers():
         moe.moe_grouped_ffn(*args, {"gate": 16, "down": 16}, 16, None,
                             workspace=16, ws_bytes=16, stream=0)
     assert e.value.status == 5  # weights accepted; the workspace is short
+
+
+def test_static_scratch_constant_and_host_errors():
+    """The binding's copy of MOE_STATIC_SCRATCH_BYTES matches the header; the
+    no-allocation entry point validates the spec on the host first."""
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    m = re.search(r"#define MOE_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == moe.STATIC_SCRATCH_BYTES
+    with pytest.raises(moe.MoEError) as e:
+        moe.moe_layer_forward_static(base(top_k=0), 4, 0, 0, None, {}, 0, stream=0)
+    assert e.value.status == 2
