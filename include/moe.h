@@ -71,11 +71,15 @@ enum { MOE_LAYOUT_SEPARATE = 0, MOE_LAYOUT_FUSED_GATE_UP = 1 };
  *                            as +-65504
  *   MOE_FLAG_NONFINITE_LOGIT a router logit was NaN or infinite (an input
  *                            outside the contract; the routing of that
- *                            token is then undefined) */
+ *                            token is then undefined)
+ *   MOE_FLAG_X_SATURATED     a 4-bit layer on the tiled kernels met an
+ *                            activation outside the fp16 range (or NaN);
+ *                            its fp16 copy was stored as +-65504 */
 enum {
   MOE_FLAG_BAD_EXPERT_ID = 1,
   MOE_FLAG_H_SATURATED = 2,
-  MOE_FLAG_NONFINITE_LOGIT = 4
+  MOE_FLAG_NONFINITE_LOGIT = 4,
+  MOE_FLAG_X_SATURATED = 8
 };
 
 /* Everything the math depends on; the subset of the Edge0 page's MoESpec
@@ -183,9 +187,10 @@ typedef void* moe_stream_t;
  *   MOE_ERR_SHAPE               T < 0 or T*max(k,1) above 2^31 - 1
  *   MOE_ERR_UNSUPPORTED         F32 activations with non-F32 weights;
  *     d not a multiple of 8; BF16 activations whose d, F or shared_ffn is
- *     not a multiple of 64; E > 1024; k > 64; n_group > 64; U4_AFFINE with
- *     ReLU, or with d or F not a power of two in [64, 2048]; bf16 tensors
- *     (x, the hidden rows, one expert matrix) of 4 GiB or more */
+ *     not a multiple of 64; E > 1024; k > 64; n_group > 64; U4_AFFINE
+ *     whose d and F are neither powers of two up to 2048 with SwiGLU (the
+ *     weight-stream kernels) nor multiples of 128 (the tiled kernels);
+ *     bf16 tensors (x, the hidden rows, one expert matrix) of 4 GiB or more */
 moe_status moe_spec_validate(const moe_spec* spec, int64_t T);
 
 /* Per-expert capacity, "Mixture of Experts" blog page, first program's
@@ -295,6 +300,11 @@ moe_status moe_dispatch(const moe_spec* spec, int64_t T,
  * for the gate/up product, whose hidden activation is rounded to fp16
  * (saturating at +-65504), then fp16 x fp16 for the down product (the bf16
  * weights are converted exactly in registers); expert outputs stay fp32.
+ * 4-bit weights (Edge0 page, QuantSpec): decode-sized groups (under 32 kept
+ * rows per expert on average) stream each expert's codes once per 4 rows
+ * with the affine term factored per group; larger groups run 256 x 256
+ * matrix-core tiles that dequantise scale*q + bias to fp16 in the K loop,
+ * against an fp16 copy of x (MOE_FLAG_X_SATURATED if x leaves fp16 range).
  *  offsets, sorted_token  device, as produced by moe_dispatch
  *  x         device [T,d] act dtype
  *  weights   host struct of device pointers

@@ -73,6 +73,14 @@ constexpr int kWavesN = 4;                  // waves along N (2 along M)
 constexpr int MB = BM / 64, NB = 2;         // 32x32 blocks per wave: (BM/2) x 64
 constexpr int kLoadsA = kTileBytesA / 1024 / kWaves;  // 1 KiB direct loads per wave
 constexpr int kLoadsW = kTileBytesW / 1024 / kWaves;
+// 4-bit weights, per stage: the codes of the BN weight rows (32 B per row
+// per K step of 64), then one dword per row holding its scale, then one
+// holding its bias (the dword of the bf16 array that contains this K step's
+// group: with an even number of groups per row the pair never crosses a row)
+constexpr int kQCodeBytes = BN * 32;
+constexpr int kTileBytesQ = kQCodeBytes + BN * 8;
+static_assert(kQCodeBytes == kWaves * 1024 && BN == 4 * 64, "one code load per wave, "
+              "four 64-row dword loads each for scales and biases");
 static_assert(BM == kGemm2BM && BM % 64 == 0, "tile prefix BM mismatch");
 static_assert(kTileBytesA % (1024 * kWaves) == 0, "whole direct loads per wave");
 
@@ -98,6 +106,16 @@ struct GemmArgs {
   int ldo;                      // output row length (F or d)
   int NT;                       // N tiles
   int32_t* err;                 // MOE_FLAG_H_SATURATED is OR-ed in (or nullptr)
+  // 4-bit affine weights (U4 kernels): packed codes [N][K/8] uint32 and bf16
+  // scales / biases [N][K/64] of expert 0 (gate / in / down, and up)
+  const uint8_t* q0;
+  const uint8_t* q1;
+  const uint16_t* s0;
+  const uint16_t* s1;
+  const uint16_t* b0;
+  const uint16_t* b1;
+  int64_t qstride;              // rows from one expert's matrix to the next
+  uint32_t nibble_mask;         // 0x0F0F0F0F, passed in so it stays in a register
 };
 
 // byte offset of 16-byte chunk c (0..7) of row r inside a swizzled tile.
@@ -152,12 +170,44 @@ __device__ __forceinline__ half8 bf16x8_to_f16x8(bf16x8 v) {
   return __builtin_bit_cast(half8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-template <int MODE, bool GATHER>
+// 8 codes of one packed word (element i in nibble i) -> 8 weights s*q + b,
+// formed in fp32 (exact for the 4-bit codes) and rounded once to the MFMA
+// operand type (fp16 for the 4-bit products).  `mask` is 0x0F0F0F0F held in
+// a register, so the nibble pairs become the bytes that v_cvt_f32_ubyte0..3
+// read.
+template <bool F16>
+__device__ __forceinline__ uint4 dequant8(uint32_t w, float sc, float bi, uint32_t mask) {
+  const uint32_t lo = w & mask;         // codes 0, 2, 4, 6 in bytes 0..3
+  const uint32_t hi = (w >> 4) & mask;  // codes 1, 3, 5, 7
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = fmaf(sc, static_cast<float>((lo >> (8 * j)) & 0xffu), bi);
+    v[2 * j + 1] = fmaf(sc, static_cast<float>((hi >> (8 * j)) & 0xffu), bi);
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (F16) {
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      const h2 p = {static_cast<_Float16>(v[2 * j]), static_cast<_Float16>(v[2 * j + 1])};
+      o[j] = __builtin_bit_cast(uint32_t, p);
+    } else {
+      typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+      const b2 p = {static_cast<__bf16>(v[2 * j]), static_cast<__bf16>(v[2 * j + 1])};
+      o[j] = __builtin_bit_cast(uint32_t, p);
+    }
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <int MODE, bool GATHER, bool U4>
 __global__ void __launch_bounds__(kThreads, 1)
 grouped_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kTileBytesA + kTileBytesW)];
+  constexpr int kWBytes = U4 ? kTileBytesQ : kTileBytesW;  // weight stage
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kTileBytesA + kWBytes)];
   uint8_t* sA = smem;                    // [2][BM rows][128 B]
-  uint8_t* sW = smem + 2 * kTileBytesA;  // [2][BN rows][128 B]
+  uint8_t* sW = smem + 2 * kTileBytesA;  // [2][BN rows][128 B] (4-bit: codes, scales, biases)
 
   // ---------------- tile scheduling
   const int total_mt = g.tiles ? g.tiles[g.E] : (g.single_rows + BM - 1) / BM;
@@ -250,6 +300,37 @@ grouped_gemm_kernel(GemmArgs g) {
     if (n > g.N - 1) n = g.N - 1;
     voffW[j] = static_cast<uint32_t>(static_cast<int64_t>(n) * K * 2 + c * 16);
   }
+  // 4-bit weights: wave w loads the codes of tile rows 32w..32w+31 (lane l:
+  // row 32w + l/2, bytes 16*(l%2).. of the row's 32 per K step), then a
+  // quarter of the scales (waves 0-3) or biases (waves 4-7): 64 rows, one
+  // dword each.  Every descriptor carries its matrix's exact size.
+  const int64_t G = K / 64;  // groups per row (even)
+  auto tile_row_n = [&](int r) {
+    int n = (MODE == kSwiGLU) ? nt * (BN / 2) + (r & 127) : nt * BN + r;
+    return n > g.N - 1 ? g.N - 1 : n;
+  };
+  const uint8_t* qptr = nullptr;
+  const uint16_t* sbptr = nullptr;
+  int qbytes = 0, sbbytes = 0;
+  uint32_t voffQ = 0, voffSB = 0;
+  if constexpr (U4) {
+    const int64_t erow = static_cast<int64_t>(e) * g.qstride;  // expert's first row
+    const int rq = wave * 32 + (lane >> 1);
+    const bool up_q = MODE == kSwiGLU && rq >= 128;
+    qptr = (up_q ? g.q1 : g.q0) + erow * (K / 2);
+    qbytes = static_cast<int>(static_cast<int64_t>(g.N) * (K / 2));
+    voffQ = static_cast<uint32_t>(static_cast<int64_t>(tile_row_n(rq)) * (K / 2) +
+                                  (lane & 1) * 16);
+    const int rs = (wave & 3) * 64 + lane;
+    const bool up_s = MODE == kSwiGLU && rs >= 128;
+    sbptr = (wave < 4 ? (up_s ? g.s1 : g.s0) : (up_s ? g.b1 : g.b0)) + erow * G;
+    sbbytes = static_cast<int>(static_cast<int64_t>(g.N) * G * 2);
+    voffSB = static_cast<uint32_t>(static_cast<int64_t>(tile_row_n(rs)) * G * 2);
+  }
+  const __amdgpu_buffer_rsrc_t rsQ = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(qptr), (short)0, qbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsSB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(sbptr), (short)0, sbbytes, 0x00020000);
 
   // ---------------- per-lane fragment offsets
   // MFMA 32x32x16: lane l supplies row (l % 32), K elements 8*(l/32)..+8.
@@ -281,18 +362,30 @@ grouped_gemm_kernel(GemmArgs g) {
   auto issue = [&](int kt, int buf) {
     const int soff = (kbase + kt) * kRowBytes;  // K advance in bytes
     uint8_t* a = sA + buf * kTileBytesA;
-    uint8_t* w = sW + buf * kTileBytesW;
+    uint8_t* w = sW + buf * kWBytes;
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsA, (__attribute__((address_space(3))) void*)(a + (j * kWaves + wave) * 1024), 16,
           voffA[j], soff, 0, 0);
-#pragma unroll
-    for (int j = 0; j < kLoadsW; ++j)
+    if constexpr (U4) {
+      const int step = kbase + kt;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          j < kLoadsW / 2 ? rsW0 : rsW1,
-          (__attribute__((address_space(3))) void*)(w + (j * kWaves + wave) * 1024), 16,
-          voffW[j], soff, 0, 0);
+          rsQ, (__attribute__((address_space(3))) void*)(w + wave * 1024), 16, voffQ,
+          step * 32, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsSB,
+          (__attribute__((address_space(3))) void*)(w + kQCodeBytes + (wave >> 2) * (BN * 4) +
+                                                    (wave & 3) * 256),
+          4, voffSB, (step >> 1) * 4, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kLoadsW; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            j < kLoadsW / 2 ? rsW0 : rsW1,
+            (__attribute__((address_space(3))) void*)(w + (j * kWaves + wave) * 1024), 16,
+            voffW[j], soff, 0, 0);
+    }
   };
 
   // fragments are double-buffered in registers: the LDS reads for K
@@ -301,26 +394,62 @@ grouped_gemm_kernel(GemmArgs g) {
   // publishes it, ahead of the current tile's last MFMAs.  On the fp16 path
   // the weight fragments are read raw (bf16) and converted later in the
   // sub-step, so no conversion waits on its LDS read.
-  using frag_t = typename std::conditional<MODE == kDown, half8, bf16x8>::type;
+  // fp16 operands for the down product and for every 4-bit product (the
+  // activations of the 4-bit gate/up product are converted to fp16 before
+  // it; dequantised weights then keep 11 bits instead of bf16's 8)
+  constexpr bool kF16 = MODE == kDown || U4;
+  using frag_t = typename std::conditional<kF16, half8, bf16x8>::type;
   frag_t wf[2][NB], af[2][MB];
   bf16x8 wraw[2][NB];
+  // 4-bit weights: a lane's codes for the whole K step (4 words: K chunks
+  // 4*fh .. 4*fh+3 of its row), and the step's scale and bias of its rows.
+  // The K chunks of a step are taken in the order (sub-step ks, lane half
+  // fh) -> chunk 4*fh + ks on both operands (instead of 2*ks + fh): the same
+  // permutation of the reduction on both sides, so the product is
+  // unchanged, and each lane's codes are one 16-byte LDS read.
+  uint4 qw[NB];
+  float qs[NB], qb[NB];
   auto read_frags = [&](int buf, int ks, int fb) {
     const uint8_t* a = sA + buf * kTileBytesA;
-    const uint8_t* w = sW + buf * kTileBytesW;
-    const int ch = ks * 2 + fh;
+    const uint8_t* w = sW + buf * kWBytes;
+    const int ch = U4 ? fh * 4 + ks : ks * 2 + fh;
+    if constexpr (U4) {
+      if (ks == 0) {
+        // K step parity selects the bf16 half of the scale / bias dword
+        // (the down projection is never split, so the step index is the
+        // stage's parity)
+        const int hi = buf;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      if constexpr (MODE == kDown)
-        wraw[fb][nb] = *reinterpret_cast<const bf16x8*>(w + swz(wrow[nb], ch));
-      else
-        wf[fb][nb] = *reinterpret_cast<const bf16x8*>(w + swz(wrow[nb], ch));
+        for (int nb = 0; nb < NB; ++nb) {
+          qw[nb] = *reinterpret_cast<const uint4*>(w + wrow[nb] * 32 + fh * 16);
+          const uint32_t sv = *reinterpret_cast<const uint32_t*>(w + kQCodeBytes + wrow[nb] * 4);
+          const uint32_t bv =
+              *reinterpret_cast<const uint32_t*>(w + kQCodeBytes + BN * 4 + wrow[nb] * 4);
+          qs[nb] = __uint_as_float(hi ? (sv & 0xffff0000u) : (sv << 16));
+          qb[nb] = __uint_as_float(hi ? (bv & 0xffff0000u) : (bv << 16));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (MODE == kDown)
+          wraw[fb][nb] = *reinterpret_cast<const bf16x8*>(w + swz(wrow[nb], ch));
+        else
+          wf[fb][nb] = *reinterpret_cast<const bf16x8*>(w + swz(wrow[nb], ch));
+      }
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
       af[fb][mb] = *reinterpret_cast<const frag_t*>(a + swz(arow_l[mb], ch));
   };
-  auto convert = [&](int fb) {
-    if constexpr (MODE == kDown) {
+  auto convert = [&](int fb, int ks) {
+    if constexpr (U4) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t word = ks == 0 ? qw[nb].x : ks == 1 ? qw[nb].y : ks == 2 ? qw[nb].z : qw[nb].w;
+        wf[fb][nb] = __builtin_bit_cast(frag_t, dequant8<true>(word, qs[nb], qb[nb], g.nibble_mask));
+      }
+    } else if constexpr (MODE == kDown) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) wf[fb][nb] = bf16x8_to_f16x8(wraw[fb][nb]);
     }
@@ -330,7 +459,7 @@ grouped_gemm_kernel(GemmArgs g) {
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        if constexpr (MODE == kDown)
+        if constexpr (kF16)
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
               wf[fb][nb], af[fb][mb], acc[nb][mb], 0, 0, 0);
         else
@@ -346,7 +475,19 @@ grouped_gemm_kernel(GemmArgs g) {
   // direct loads in program order -- there the reads go first and the loads
   // are paired with the MFMAs.  The fp16 path places the weight
   // conversions (about 12 VALU ops per fragment) in the second half.
+  // 4-bit weights: the dequantisation (about 23 VALU ops per fragment, 2
+  // fragments per sub-step) is spread evenly over the sub-step's MFMAs.
+  constexpr int kDeqValu = 6;
   auto pace = [&]() {
+    if constexpr (U4) {
+#pragma unroll
+      for (int i = 0; i < NB * MB; ++i) {
+        if (i < MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x002, kDeqValu, 0);      // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NB + MB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
@@ -361,16 +502,17 @@ grouped_gemm_kernel(GemmArgs g) {
   // the sub-step that issues a K step's direct loads: fragment reads first,
   // then the loads spread evenly over its MFMAs
   auto pace_loads = [&]() {
-    constexpr int kV = kLoadsA + kLoadsW;  // direct loads in this sub-step
+    constexpr int kV = kLoadsA + (U4 ? 2 : kLoadsW);  // direct loads in this sub-step
     constexpr int NM = NB * MB;
     static_assert(kV <= 2 * NM, "load spread");
-    __builtin_amdgcn_sched_group_barrier(0x100, NB + MB, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x100, U4 ? MB + 3 * NB : NB + MB, 0);  // DS read
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int n_here = ((i + 1) * kV) / NM - (i * kV) / NM;
       if (n_here >= 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
       if (n_here >= 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM
-      if (MODE == kDown) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // VALU
+      if (U4) __builtin_amdgcn_sched_group_barrier(0x002, kDeqValu, 0);     // VALU
+      else if (MODE == kDown) __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
   };
@@ -384,15 +526,15 @@ grouped_gemm_kernel(GemmArgs g) {
     const int cur = kt & 1;
     read_frags(cur, 1, 1);
     mfmas(0);
-    convert(1);
+    convert(1, 1);
     pace();
     read_frags(cur, 2, 0);
     mfmas(1);
-    convert(0);
+    convert(0, 2);
     pace();
     read_frags(cur, 3, 1);
     mfmas(0);
-    convert(1);
+    convert(1, 3);
     pace();
     if constexpr (kind != 2) {
       // every read of this tile is issued: wait for them and for the next
@@ -408,12 +550,12 @@ grouped_gemm_kernel(GemmArgs g) {
       if constexpr (kind == 0) {
         issue(kt + 2, cur);
         mfmas(1);
-        convert(0);
+        convert(0, 0);
         pace_loads();
         if constexpr (MODE == kDown) __builtin_amdgcn_s_setprio(0);
       } else {
         mfmas(1);
-        convert(0);
+        convert(0, 0);
         pace();
         if constexpr (MODE == kDown) __builtin_amdgcn_s_setprio(0);
       }
@@ -427,7 +569,7 @@ grouped_gemm_kernel(GemmArgs g) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   read_frags(0, 0, 0);
-  convert(0);
+  convert(0, 0);
   for (int kt = 0; kt + 2 < KT; ++kt) tile(kt, std::integral_constant<int, 0>{});
   if (KT > 1) tile(KT - 2, std::integral_constant<int, 1>{});
   tile(KT - 1, std::integral_constant<int, 2>{});
@@ -488,27 +630,68 @@ grouped_gemm_kernel(GemmArgs g) {
     atomicOr(g.err, MOE_FLAG_H_SATURATED);
 }
 
+// bf16 activations -> fp16 for the 4-bit products, 8 per thread: exact
+// for every value of fp16's normal range; beyond +-65504 saturated (and
+// reported), below it rounded to fp16's subnormal grid (2^-24 apart)
+__global__ void __launch_bounds__(256)
+to_f16_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y, int64_t n8,
+              int32_t* __restrict__ err) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  bool sat = false;
+  if (i < n8) {
+    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a = __uint_as_float(w[j] << 16), b = __uint_as_float(w[j] & 0xffff0000u);
+      sat |= !(fabsf(a) <= 65504.f) || !(fabsf(b) <= 65504.f);
+      a = fminf(fmaxf(a, -65504.f), 65504.f);
+      b = fminf(fmaxf(b, -65504.f), 65504.f);
+      typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+      const h2 p = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+      o[j] = __builtin_bit_cast(uint32_t, p);
+    }
+    reinterpret_cast<uint4*>(y)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+  if (err != nullptr && __ballot(sat) != 0 && (threadIdx.x & 63) == 0)
+    atomicOr(err, MOE_FLAG_X_SATURATED);
+}
+
 int ntiles(int mode, int N) {
   const int cols = mode == kSwiGLU ? BN / 2 : BN;
   return (N + cols - 1) / cols;
 }
 
 hipError_t launch_one(int mode, bool gather, const GemmArgs& g, int64_t mt_upper,
-                      hipStream_t s) {
+                      hipStream_t s, bool u4 = false) {
   int64_t n = mt_upper * g.NT * g.ksplit;
   n = (n + 7) / 8 * 8;
   if (n <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(n)), block(kThreads);
+  if (u4) {
+    // routed experts only: the gate/up product gathers, the down one does not
+    if (g.ksplit != 1) return hipErrorInvalidValue;
+    if (mode == kSwiGLU && gather)
+      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, true, true>), grid, block, 0, s, g);
+    else if (mode == kReLU && gather)
+      hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, true, true>), grid, block, 0, s, g);
+    else if (mode == kDown && !gather)
+      hipLaunchKernelGGL((grouped_gemm_kernel<kDown, false, true>), grid, block, 0, s, g);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (mode == kSwiGLU && gather)
-    hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, true>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, true, false>), grid, block, 0, s, g);
   else if (mode == kSwiGLU)
-    hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, false, false>), grid, block, 0, s, g);
   else if (mode == kReLU && gather)
-    hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, true>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, true, false>), grid, block, 0, s, g);
   else if (mode == kReLU)
-    hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, false, false>), grid, block, 0, s, g);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<kDown, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<kDown, false, false>), grid, block, 0, s, g);
   return hipGetLastError();
 }
 
@@ -634,6 +817,76 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
   }
   if (D.S > 0) return launch_shared_bf16(D, x, w, Hs, Ys, err, s);
   return hipSuccess;
+}
+
+hipError_t launch_ffn_u4_tiled(const Dims& D, const int32_t* offsets, const int32_t* tiles1,
+                               const int32_t* tiles2, const int32_t* sorted_token,
+                               const void* x, void* X16, const moe_expert_weights& w, void* H,
+                               void* Y, int32_t* err, hipEvent_t mid, hipStream_t s) {
+  const int up_mode = D.swiglu ? kSwiGLU : kReLU;
+  const int64_t nmax = std::min<int64_t>(D.slots, D.cap * D.E);
+  // one (scale, bias) per 64 weights of a row, an even number per row
+  if (D.d % 128 != 0 || D.F % 128 != 0) return hipErrorInvalidValue;
+  {
+    const int64_t n8 = D.T * D.d / 8;
+    hipLaunchKernelGGL(to_f16_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256),
+                       0, s, static_cast<const uint16_t*>(x), static_cast<uint16_t*>(X16), n8,
+                       err);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    GemmArgs g{};
+    g.a = static_cast<const uint16_t*>(X16);
+    g.a_bytes = static_cast<uint32_t>(D.T * D.d * 2);
+    g.sorted_token = sorted_token;
+    g.offsets = offsets;
+    g.tiles = tiles1;
+    g.E = D.E;
+    g.q0 = static_cast<const uint8_t*>(w.gate);
+    g.s0 = static_cast<const uint16_t*>(w.gate_scale);
+    g.b0 = static_cast<const uint16_t*>(w.gate_bias);
+    if (D.fused) {  // [E][2F] rows: each expert's gate rows, then its up rows
+      g.q1 = g.q0 + static_cast<int64_t>(D.F) * (D.d / 2);
+      g.s1 = g.s0 + static_cast<int64_t>(D.F) * (D.d / 64);
+      g.b1 = g.b0 + static_cast<int64_t>(D.F) * (D.d / 64);
+      g.qstride = 2 * static_cast<int64_t>(D.F);
+    } else {
+      g.q1 = static_cast<const uint8_t*>(w.up);
+      g.s1 = static_cast<const uint16_t*>(w.up_scale);
+      g.b1 = static_cast<const uint16_t*>(w.up_bias);
+      g.qstride = D.F;
+    }
+    g.nibble_mask = 0x0F0F0F0Fu;
+    g.N = D.F;
+    g.K = D.d;
+    g.out = H;
+    g.ldo = D.F;
+    g.NT = ntiles(up_mode, D.F);
+    g.ksplit = 1;
+    g.err = err;
+    hipError_t e = launch_one(up_mode, true, g, nmax / BM + D.E, s, true);
+    if (e != hipSuccess) return e;
+    if (mid != nullptr && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
+  }
+  GemmArgs g{};
+  g.a = static_cast<const uint16_t*>(H);
+  g.a_bytes = static_cast<uint32_t>(D.slots * D.F * 2);
+  g.offsets = offsets;
+  g.tiles = tiles2;
+  g.E = D.E;
+  g.q0 = g.q1 = static_cast<const uint8_t*>(w.down);
+  g.s0 = g.s1 = static_cast<const uint16_t*>(w.down_scale);
+  g.b0 = g.b1 = static_cast<const uint16_t*>(w.down_bias);
+  g.qstride = D.d;
+  g.nibble_mask = 0x0F0F0F0Fu;
+  g.N = D.d;
+  g.K = D.F;
+  g.out = Y;
+  g.ldo = D.d;
+  g.NT = ntiles(kDown, D.d);
+  g.ksplit = 1;
+  return launch_one(kDown, false, g, nmax / BM + D.E, s, true);
 }
 
 }  // namespace moe

@@ -21,6 +21,7 @@
 //          epilogue writes H = silu(gate) * up (fp16, as on the
 //          matrix-core path)
 //   down : unit = output column n of W_down, writes Y (fp32)
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_internal.hpp"
@@ -746,6 +747,20 @@ hipError_t launch_stream(int K, const U4Args& g, hipStream_t s) {
 }
 
 }  // namespace
+
+// Average kept rows per expert from which the tiled matrix-core kernel
+// (256-row tiles, weights read once per tile) takes over from the weight
+// stream (weights read once per 4-row chunk).
+constexpr int kTiledRowsPerExpert = 32;
+
+bool u4_tiled(const Dims& D) {
+  const bool stream_ok = D.swiglu && supported_k(D.d) && supported_k(D.F) && D.E <= kMaxExperts;
+  const bool tiled_ok = D.d % 128 == 0 && D.F % 128 == 0;
+  if (!stream_ok) return true;  // the spec check lets through only shapes one of them takes
+  if (!tiled_ok) return false;
+  const int64_t rows = std::min<int64_t>(D.slots, D.cap * D.E);
+  return rows >= static_cast<int64_t>(kTiledRowsPerExpert) * D.E;
+}
 
 hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
                          const int32_t* sorted_token, const void* x,

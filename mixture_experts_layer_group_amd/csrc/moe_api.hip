@@ -76,14 +76,20 @@ moe_status validate(const moe_spec* sp, int64_t T) {
       (s.hidden % 64 != 0 || s.ffn % 64 != 0 ||
        (s.shared_experts > 0 && s.shared_ffn % 64 != 0)))
     return MOE_ERR_UNSUPPORTED;
-  if (s.weight_dtype == MOE_DTYPE_U4_AFFINE &&
-      (s.act != MOE_ACT_SWIGLU || s.hidden > 2048 || s.ffn > 2048 ||
-       (s.hidden & (s.hidden - 1)) != 0 || (s.ffn & (s.ffn - 1)) != 0))
-    return MOE_ERR_UNSUPPORTED;
+  if (s.weight_dtype == MOE_DTYPE_U4_AFFINE) {
+    // the weight-stream kernels take SwiGLU with d, F powers of two up to
+    // 2048; the tiled kernels any d, F that are multiples of 128 (an even
+    // number of quantisation groups per row)
+    const bool pow2 = s.hidden <= 2048 && s.ffn <= 2048 &&
+                      (s.hidden & (s.hidden - 1)) == 0 && (s.ffn & (s.ffn - 1)) == 0;
+    const bool stream_ok = s.act == MOE_ACT_SWIGLU && pow2;
+    const bool tiled_ok = s.hidden % 128 == 0 && s.ffn % 128 == 0;
+    if (!stream_ok && !tiled_ok) return MOE_ERR_UNSUPPORTED;
+  }
   if (s.num_experts > 1024 || s.top_k > 64) return MOE_ERR_UNSUPPORTED;
   // the bf16 matrix-core kernels address activations, hidden rows and one
-  // expert's matrix with 32-bit byte offsets
-  if (s.act_dtype == MOE_DTYPE_BF16 && s.weight_dtype == MOE_DTYPE_BF16) {
+  // expert's matrix with 32-bit byte offsets (4-bit matrices are smaller)
+  if (s.act_dtype == MOE_DTYPE_BF16 && s.weight_dtype != MOE_DTYPE_F32) {
     const int64_t lim = INT64_C(1) << 32;
     const int64_t slots = T * s.top_k;
     if (T * s.hidden * 2 >= lim || slots * s.ffn * 2 >= lim ||
@@ -159,6 +165,7 @@ WsLayout layout_of(const Dims& D) {
   L.Y = take(S * D.d * 4);
   L.Ypart = take(down_splits(D) > 1 ? S * D.d * 4 : 0);
   L.Ys = take(static_cast<size_t>(D.S) * T * D.d * 4);
+  L.X16 = take(D.u4 && u4_tiled(D) ? T * D.d * 2 : 0);
   L.total = o;
   return L;
 }
@@ -240,15 +247,25 @@ moe_status do_ffn(const moe_spec& sp, const Dims& D, const WsLayout& L,
   hipEvent_t mid = ev ? static_cast<hipEvent_t>(ev[1]) : nullptr;
   hipError_t e = hipSuccess;
   if (!D.bf16 || D.u4) {
+    // (the 4-bit tiled kernels, like the bf16 ones, read the M-tile
+    // prefixes, which the fused layer's dispatch wrote)
     if (ev && (e = hipEventRecord(static_cast<hipEvent_t>(ev[0]), s)) != hipSuccess)
       return MOE_ERR_HIP;
     if (!D.bf16) {
       e = launch_ffn_f32(D, offsets, sorted_token, x, w, H, Hs, y_rows, y_shared, mid, s);
-    } else {
+    } else if (!u4_tiled(D)) {
       e = launch_ffn_u4(D, sp.quant_group, offsets, sorted_token, x, w, H, y_rows, err,
                         mid, s);
-      if (e == hipSuccess && D.S > 0) e = launch_shared_bf16(D, x, w, Hs, y_shared, err, s);
+    } else {
+      int32_t* t1 = at<int32_t>(ws, L.tiles1);
+      int32_t* t2 = at<int32_t>(ws, L.tiles2);
+      if (!fused) e = launch_tile_prefix(D, offsets, t1, t2, s);
+      if (e == hipSuccess)
+        e = launch_ffn_u4_tiled(D, offsets, t1, t2, sorted_token, x, at<void>(ws, L.X16), w, H,
+                                y_rows, err, mid, s);
     }
+    if (e == hipSuccess && D.bf16 && D.S > 0)
+      e = launch_shared_bf16(D, x, w, Hs, y_shared, err, s);
     if (e == hipSuccess && ev) e = hipEventRecord(static_cast<hipEvent_t>(ev[2]), s);
     return hip_status(e);
   }
@@ -309,7 +326,7 @@ moe_status layer_forward(const moe_spec* spec, int64_t T, const void* x,
   st = do_route(*spec, D, L, x, w_router, expert_bias, nullptr, nullptr, ids,
                 tw, o.logits, o.prob_sum, o.errors, ws, s);
   if (st != MOE_OK) return st;
-  const bool mfma_path = D.bf16 && !D.u4;
+  const bool mfma_path = D.bf16 && (!D.u4 || u4_tiled(D));
   hipError_t e = launch_dispatch(
       D, ids, tw, at<int32_t>(ws, L.hist), L.dispatch_blocks, counts, offsets,
       sorted_token, sorted_w, slot_row, dropped,

@@ -131,7 +131,7 @@ struct WsLayout {
   size_t logits, probpart, hist, tiles1, tiles2;  // logits: [S][T][E] partials
   size_t topk_ids, topk_w, counts, offsets, sorted_token, sorted_w, slot_row,
       dropped;
-  size_t H, Hs, Y, Ypart, Ys;
+  size_t H, Hs, Y, Ypart, Ys, X16;
   size_t total;
   int route_blocks;     // selection kernel grid (prob partial rows)
   int dispatch_blocks;  // count / scatter grid (histogram rows)
@@ -208,6 +208,17 @@ hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
                          const int32_t* sorted_token, const void* x,
                          const moe_expert_weights& w, void* H, void* Y,
                          int32_t* err, hipEvent_t mid, hipStream_t s);
+// gemm_bf16.hip: 4-bit routed weights on the tiled matrix-core kernel
+// (dequantised in the K loop), for groups of many rows; d and F multiples of
+// 128; tiles1 / tiles2 as for launch_ffn_bf16; X16: workspace [T][d] for
+// the fp16 copy of x both products are formed from
+hipError_t launch_ffn_u4_tiled(const Dims& D, const int32_t* offsets, const int32_t* tiles1,
+                               const int32_t* tiles2, const int32_t* sorted_token,
+                               const void* x, void* X16, const moe_expert_weights& w, void* H,
+                               void* Y, int32_t* err, hipEvent_t mid, hipStream_t s);
+// whether a 4-bit layer runs the tiled kernels (true) or the weight-stream
+// kernels of gemm_u4.hip (false); depends on the shapes only
+bool u4_tiled(const Dims& D);
 // shared experts with bf16 weights on the MFMA kernel (used by the u4 path)
 hipError_t launch_shared_bf16(const Dims& D, const void* x,
                               const moe_expert_weights& w, void* Hs, void* Ys,

@@ -2,7 +2,8 @@
 expert's gate and up rows from one fused tensor equals the layer over the
 separate tensors bit for bit (same kernels, same arithmetic, other
 addresses) and matches the oracle reading the fused tensor itself, for
-bf16 (routed + shared, split-K down projection), 4-bit and fp32 weights.
+bf16 (routed + shared, split-K down projection), 4-bit (weight-stream and
+tiled kernels) and fp32 weights.
 """
 import pytest
 import torch
@@ -16,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("name", ["sigmoid-group-shared", "swiglu-bf16-splitk",
                                   "swiglu-bf16-ragged", "u4-decode", "u4-small-k",
-                                  "f32-swiglu-shared"])
+                                  "u4-tiled-swiglu-shared", "f32-swiglu-shared"])
 def test_fused_gate_up_layer(name):
     cfg = MEDIUM[name]
     fcfg = cfg.replace(layout=synth.FUSED_GATE_UP)

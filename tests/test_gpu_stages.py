@@ -43,10 +43,11 @@ MEDIUM = {
     # 4-bit affine weights, decode-shaped; K % 128 == 0 and == 64 variants
     "u4-decode": C("u4-decode", 109, T=20, d=512, E=64, top_k=4, F=256, weight_dtype=synth.U4),
     "u4-small-k": C("u4-small-k", 110, T=37, d=256, E=16, top_k=2, F=64, weight_dtype=synth.U4),
-    # 4-bit weights with 64 rows per expert (16 four-row chunks each, weights
-    # streamed once per chunk) and the largest expert count (1024 experts,
-    # 64 of them touched at most)
-    "u4-many-rows": C("u4-many-rows", 116, T=256, d=256, E=8, top_k=2, F=128,
+    # 4-bit weights on the weight-stream kernels with about 30 rows per
+    # expert (8 four-row chunks each, weights streamed once per chunk; below
+    # the 32 rows per expert from which the tiled kernels take over) and
+    # the largest expert count (1024 experts, 64 of them touched at most)
+    "u4-many-rows": C("u4-many-rows", 116, T=120, d=256, E=8, top_k=2, F=128,
                       weight_dtype=synth.U4),
     "u4-1024-experts": C("u4-1024-experts", 117, T=8, d=64, E=1024, top_k=8, F=64,
                          weight_dtype=synth.U4),
@@ -56,6 +57,17 @@ MEDIUM = {
     "u4-k1024-f2048": C("u4-k1024-f2048", 118, T=24, d=1024, E=8, top_k=2, F=2048,
                         weight_dtype=synth.U4),
     "u4-k128-f1024": C("u4-k128-f1024", 119, T=40, d=128, E=16, top_k=3, F=1024,
+                       weight_dtype=synth.U4),
+    # 4-bit weights on the tiled matrix-core kernels (dequantised in the K
+    # loop): F not a power of two with a bf16 shared expert; ReLU with
+    # capacity drops (a shape only the tiled kernels take); a power-of-two
+    # shape with hundreds of rows per expert
+    "u4-tiled-swiglu-shared": C("u4-tiled-swiglu-shared", 132, T=1024, d=512, E=8, top_k=2,
+                                F=384, weight_dtype=synth.U4, shared_experts=1, shared_F=256),
+    "u4-tiled-relu-capacity": C("u4-tiled-relu-capacity", 133, T=600, d=256, E=8, top_k=2,
+                                F=256, act=synth.RELU, weight_dtype=synth.U4,
+                                capacity_factor=1.25),
+    "u4-tiled-pow2": C("u4-tiled-pow2", 134, T=2048, d=1024, E=16, top_k=4, F=512,
                        weight_dtype=synth.U4),
     # fp32 path, SwiGLU and a shared expert
     "f32-swiglu-shared": C("f32-swiglu-shared", 111, T=150, d=48, E=5, top_k=2, F=40,
@@ -366,6 +378,8 @@ def test_error_word_saturation_and_nonfinite():
     MOE_FLAG_NONFINITE_LOGIT.  The normal inputs set neither."""
     for cfg in (C("sat-bf16", 128, T=300, d=256, E=8, top_k=2, F=128),
                 C("sat-u4", 129, T=24, d=256, E=16, top_k=2, F=128,
+                  weight_dtype=synth.U4),
+                C("sat-u4-tiled", 136, T=600, d=256, E=8, top_k=2, F=256,
                   weight_dtype=synth.U4)):
         inp = gu.make_inputs(cfg)
         err = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -384,6 +398,16 @@ def test_error_word_saturation_and_nonfinite():
         torch.cuda.synchronize()
         assert int(err.item()) == moe.FLAG_H_SATURATED, f"{cfg.name}: {int(err.item())}"
         gu.log(f"  {cfg.name}: saturation flagged")
+        if cfg.name == "sat-u4-tiled":
+            # an activation beyond fp16's range: the tiled 4-bit products read
+            # an fp16 copy of x
+            x_wide = inp["x"].clone()
+            x_wide[5, 3] = 1.0e5
+            err.zero_()
+            moe.moe_layer_forward(spec, cfg.T, x_wide, inp["w_router"], None, inp, out,
+                                  stats=moe.layer_stats(errors=err), workspace=ws)
+            torch.cuda.synchronize()
+            assert int(err.item()) & moe.FLAG_X_SATURATED, f"{int(err.item())}"
     # a NaN token: its logits are NaN; the other tokens route as before
     cfg = C("nonfinite", 130, T=200, d=256, E=40, top_k=2, F=64)
     inp = gu.make_inputs(cfg)
@@ -425,3 +449,36 @@ def test_routing_health_counts_beyond_fp32_integers():
     assert np.array_equal(bias.cpu().numpy().astype(np.float64), ref)
     st = oracle.layer_stats(counts_h, counts_h, 0, None, cfg.T, 4, 4)
     assert abs(got["load_peak_over_mean"] - st["load_peak_over_mean"]) <= 1e-6
+
+
+U4_LARGE = {
+    # the DeepSeek-style expert shape in 4 bits (d = 7168, F = 2048) with
+    # about 256 rows per expert
+    "u4-deepseek-shape": C("u4-deepseek-shape", 135, T=2048, d=7168, E=16, top_k=2, F=2048,
+                           weight_dtype=synth.U4),
+    # a prefill batch over the decode-shaped layer's experts (4096 tokens,
+    # 256 experts, top-8: 128 rows per expert)
+    "u4-decode-experts-prefill": synth.CONFIGS[5].replace(name="u4-decode-experts-prefill",
+                                                          T=4096),
+}
+
+
+@pytest.mark.parametrize("name", list(U4_LARGE))
+def test_u4_tiled_large(name):
+    """The tiled 4-bit kernels at full-size expert shapes: routing and
+    dispatch in full, the output on 256 tokens (every expert's last M tile
+    first)."""
+    cfg = U4_LARGE[name]
+    gu.log(f"[u4 tiled] {name}: T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.top_k} F={cfg.F}")
+    inp = gu.make_inputs(cfg)
+    r = gu.run_layer(cfg, inp)
+
+    def choose(disp):
+        toks = set(gu.last_tile_tokens(disp, 1))
+        for t in np.random.default_rng(cfg.cfg_id).permutation(cfg.T):
+            if len(toks) >= 256:
+                break
+            toks.add(int(t))
+        return sorted(toks)
+
+    gu.full_check(cfg, inp, r, choose_tokens=choose)

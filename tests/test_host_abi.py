@@ -53,8 +53,12 @@ def base(**kw):
     ({"shared_experts": 1, "shared_F": 0}, 1),
     ({"weight_dtype": "u4", "quant_group": 32}, 1),
     ({"weight_dtype": "u4", "d": 96}, 1),
-    ({"weight_dtype": "u4", "d": 4096}, 7),      # 4-bit path: d, F <= 2048
-    ({"weight_dtype": "u4", "F": 192}, 7),       # ... powers of two
+    ({"weight_dtype": "u4", "d": 4096}, 0),      # tiled 4-bit kernels: multiples of 128
+    ({"weight_dtype": "u4", "d": 7168, "F": 2048}, 0),
+    ({"weight_dtype": "u4", "F": 192}, 7),       # neither a power of two nor 128k
+    ({"weight_dtype": "u4", "d": 192, "F": 128}, 7),
+    ({"weight_dtype": "u4", "act": "relu", "F": 128}, 0),  # ReLU: tiled only
+    ({"weight_dtype": "u4", "act": "relu", "F": 64}, 7),
     ({"weight_dtype": "f32"}, 1),                 # bf16 activations, f32 weights
     ({"act_dtype": "f32", "weight_dtype": "bf16"}, 7),
     ({"d": 100}, 7),
