@@ -119,3 +119,51 @@ def test_lane_sum_leaves_each_total_in_one_writer(K, pair):
                 key = (4 * ug + idx // M, lane & 3)
                 seen[key] = seen.get(key, 0) + 1
     assert seen == {(u, r): 1 for u in range(C["UPI"]) for r in range(4)}
+
+
+def load_rows_range(K, row0, rows, lane, sorted_token):
+    """(kept row, first element, end element) that `load_rows` of the 4-bit
+    stream kernel reads for lane `lane` of a chunk starting at kept row
+    row0 with `rows` rows, restated from the kernel: the lane's row i4 =
+    lane % 4 (a lane past the chunk reads the chunk's first row and discards
+    it), its K slice ks = (lane / 4) % NKS, and the 8-element words
+    8w .. 8w+7 of that slice for w < KB / 8 -- one contiguous range."""
+    C = kcfg(K)
+    i4 = lane & 3
+    ks = (lane >> 2) % C["NKS"]
+    live = i4 < rows
+    kr = row0 + (i4 if live else 0)
+    src = sorted_token[kr] if sorted_token is not None else kr
+    first = src * K + ks * C["KB"]
+    return kr, ks, first, first + 8 * (C["KB"] // 8)
+
+
+@pytest.mark.parametrize("K", KS)
+@pytest.mark.parametrize("gather", [True, False])
+def test_activation_rows_stay_in_their_buffer(K, gather):
+    """Over random dispatch outcomes (offsets, sorted tokens), every chunk
+    of every expert -- the chunks the kernel's items visit, row0 = offs[e] +
+    4k < offs[e+1] -- reads only kept rows and, through them, only elements
+    of x (T rows) or of H (the kept rows), and every K slice stays inside
+    its row."""
+    import random
+    rnd = random.Random(K * 2 + gather)
+    C = kcfg(K)
+    for _ in range(10):
+        E, T = rnd.randint(2, 40), rnd.randint(1, 300)
+        counts = [rnd.randint(0, 12) for _ in range(E)]
+        offs = [0]
+        for c in counts:
+            offs.append(offs[-1] + c)
+        kept = offs[-1]
+        st = [rnd.randrange(T) for _ in range(kept)] if gather else None
+        nrows = T if gather else kept
+        for e in range(E):
+            for row0 in range(offs[e], offs[e + 1], 4):
+                rows = min(4, offs[e + 1] - row0)
+                for lane in range(64):
+                    kr, ks, a, b = load_rows_range(K, row0, rows, lane, st)
+                    assert offs[e] <= kr < offs[e + 1]
+                    assert 0 <= a and b <= nrows * K
+                    assert a // K == (b - 1) // K  # inside one row
+                    assert a % K == ks * C["KB"] and b - a == C["KB"]
