@@ -320,7 +320,7 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
   if (D.slots <= kDispatchChunk) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, ids, w,
                        D.slots, D.k, D.E, D.cap, nbits, counts, offsets, dropped,
-                       tiles1, kGemm1BM, tiles2, kGemm2BM, sorted_token, sorted_w,
+                       tiles1, routed_bm(D), tiles2, routed_bm(D), sorted_token, sorted_w,
                        slot_row, err);
     return hipGetLastError();
   }
@@ -328,7 +328,7 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
                      D.slots, D.E, hist, err);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, hist,
                      nblocks, D.E, D.slots, D.cap, counts, offsets, dropped,
-                     tiles1, kGemm1BM, tiles2, kGemm2BM);
+                     tiles1, routed_bm(D), tiles2, routed_bm(D));
   hipLaunchKernelGGL(scatter_kernel, dim3(nblocks), dim3(256), 5 * hsz, s, ids,
                      w, D.slots, D.k, D.E, D.cap, nbits, hist, offsets,
                      sorted_token, sorted_w, slot_row);
@@ -338,7 +338,7 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
 hipError_t launch_tile_prefix(const Dims& D, const int32_t* offsets,
                               int32_t* tiles1, int32_t* tiles2, hipStream_t s) {
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, D.E,
-                     tiles1, kGemm1BM, tiles2, kGemm2BM);
+                     tiles1, routed_bm(D), tiles2, routed_bm(D));
   return hipGetLastError();
 }
 

@@ -19,18 +19,19 @@
 // (the conversion saturates at +-65504).
 //
 // Kernel shape (gfx950):
-//   * a 256 x 256 output tile per 512-thread workgroup, K steps of 64;
-//     each of the 8 waves (2 per SIMD, so one fills the other's issue gaps)
-//     owns a 128 x 64 sub-tile = 4 x 2 blocks of v_mfma_f32_32x32x16.  The
+//   * a BM x 256 output tile (BM = 256, or 128 for 4-bit layers with few
+//     rows per expert) per 512-thread workgroup, K steps of 64; each of the
+//     8 waves (2 per SIMD, so one fills the other's issue gaps) owns a
+//     BM/2 x 64 sub-tile = BM/64 x 2 blocks of v_mfma_f32_32x32x16.  The
 //     weight tile is the MFMA A operand (rows = output columns) and the
 //     activation tile the B operand, so a lane's accumulators hold 4
 //     consecutive output columns of one row;
 //   * both operands are K-contiguous in HBM (weights are [out, in]) and go
 //     straight from HBM to LDS (buffer_load_dwordx4 ... lds, no staging
-//     registers) into double-buffered tiles (2 x 64 KiB).  The loads of K
-//     step t+1 start right after the barrier that ends step t-1 (half
-//     there, half in step t's first sub-step), so the memory pipe is busy
-//     across the barrier.  The 16-byte chunks of each 128-byte LDS row are
+//     registers) into a ring of 2 or 3 stages (as many as fit 160 KiB).  The
+//     loads of a later step start right after the barrier that ends the
+//     step whose stage they reuse, so the memory pipe is busy across the
+//     barrier.  The 16-byte chunks of each 128-byte LDS row are
 //     XOR-swizzled (conflict-free for 8- and 16-lane LDS phases); the
 //     swizzle is applied on the global side, since a direct load writes LDS
 //     at lane*16;
@@ -62,17 +63,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = kGemm1BM, BN = 256, BK = 64;
+constexpr int BN = 256, BK = 64;
 constexpr int kRowBytes = BK * 2;            // 128
-constexpr int kTileBytesA = BM * kRowBytes;  // activation tile per stage
 constexpr int kTileBytesW = BN * kRowBytes;  // weight tile per stage (32 KiB)
 constexpr int kNG = 8;                      // N-tiles per scheduling column group
 constexpr int kWaves = 8;                   // 2 waves per SIMD
 constexpr int kThreads = kWaves * 64;
 constexpr int kWavesN = 4;                  // waves along N (2 along M)
-constexpr int MB = BM / 64, NB = 2;         // 32x32 blocks per wave: (BM/2) x 64
-constexpr int kLoadsA = kTileBytesA / 1024 / kWaves;  // 1 KiB direct loads per wave
-constexpr int kLoadsW = kTileBytesW / 1024 / kWaves;
+constexpr int NB = 2;                       // 32x32 weight blocks per wave (64 columns)
+constexpr int kLoadsW = kTileBytesW / 1024 / kWaves;  // 1 KiB direct loads per wave
 // 4-bit weights, per stage: the codes of the BN weight rows (32 B per row
 // per K step of 64), then one dword per row holding its scale, then one
 // holding its bias (the dword of the bf16 array that contains this K step's
@@ -81,8 +80,6 @@ constexpr int kQCodeBytes = BN * 32;
 constexpr int kTileBytesQ = kQCodeBytes + BN * 8;
 static_assert(kQCodeBytes == kWaves * 1024 && BN == 4 * 64, "one code load per wave, "
               "four 64-row dword loads each for scales and biases");
-static_assert(BM == kGemm2BM && BM % 64 == 0, "tile prefix BM mismatch");
-static_assert(kTileBytesA % (1024 * kWaves) == 0, "whole direct loads per wave");
 
 enum Mode { kSwiGLU = 0, kReLU = 1, kDown = 2 };
 
@@ -201,16 +198,39 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, float sc, float bi, uint32
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-template <int MODE, bool GATHER, bool U4>
+// Sizes of one kernel variant: BMT-row tiles, bf16 or 4-bit weights.  The
+// LDS ring has three stages where they fit the 160 KiB of LDS (128-row
+// tiles, 4-bit weights), so two K steps of loads are in flight during a
+// step's products; two for 256-row tiles of bf16 weights.
+// the largest per-variant counts, for array sizes: arrays sized by a
+// template-dependent count and captured by the kernel's lambdas lose the
+// kernel's host-side launch stub
+constexpr int kMaxMB = 4, kMaxLoadsA = 4;
+
+template <int BMT, bool U4>
+struct TileCfg {
+  static constexpr int BM = BMT;                          // tile rows (activation rows)
+  static constexpr int kTileBytesA = BM * kRowBytes;      // activation tile per stage
+  static constexpr int MB = BM / 64;                      // 32x32 blocks per wave along M
+  static constexpr int kLoadsA = kTileBytesA / 1024 / kWaves;  // 1 KiB direct loads per wave
+  static constexpr int kWBytes = U4 ? kTileBytesQ : kTileBytesW;  // weight stage
+  static constexpr int NST = (kTileBytesA + kWBytes) * 3 <= 160 * 1024 ? 3 : 2;
+  // direct loads per K step and wave (vmcnt counts them in issue order)
+  static constexpr int kStepLoads = kLoadsA + (U4 ? 2 : kLoadsW);
+  static_assert(BM % 128 == 0 && kTileBytesA % (1024 * kWaves) == 0, "whole direct loads");
+  static_assert(MB <= kMaxMB && kLoadsA <= kMaxLoadsA, "array bounds");
+};
+
+template <int MODE, bool GATHER, bool U4, int BMT>
 __global__ void __launch_bounds__(kThreads, 1)
 grouped_gemm_kernel(GemmArgs g) {
-  constexpr int kWBytes = U4 ? kTileBytesQ : kTileBytesW;  // weight stage
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (kTileBytesA + kWBytes)];
-  uint8_t* sA = smem;                    // [2][BM rows][128 B]
-  uint8_t* sW = smem + 2 * kTileBytesA;  // [2][BN rows][128 B] (4-bit: codes, scales, biases)
+  using TC = TileCfg<BMT, U4>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TC::NST * (TC::kTileBytesA + TC::kWBytes)];
+  uint8_t* sA = smem;                              // [NST][BM rows][128 B]
+  uint8_t* sW = smem + TC::NST * TC::kTileBytesA;  // [NST][BN rows][128 B]; 4-bit: codes, scales, biases
 
   // ---------------- tile scheduling
-  const int total_mt = g.tiles ? g.tiles[g.E] : (g.single_rows + BM - 1) / BM;
+  const int total_mt = g.tiles ? g.tiles[g.E] : (g.single_rows + TC::BM - 1) / TC::BM;
   const int real = total_mt * g.NT;
   const int share = (real * g.ksplit + 7) >> 3;
   const int bid = blockIdx.x;
@@ -253,7 +273,7 @@ grouped_gemm_kernel(GemmArgs g) {
       cnt = g.single_rows;
     }
   }
-  const int m0 = mt * BM;  // first row of this tile inside the group
+  const int m0 = mt * TC::BM;  // first row of this tile inside the group
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -278,9 +298,9 @@ grouped_gemm_kernel(GemmArgs g) {
       const_cast<uint16_t*>(wbase0), (short)0, -1, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsW1 = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(wbase1), (short)0, -1, 0x00020000);
-  uint32_t voffA[kLoadsA], voffW[kLoadsW];
+  uint32_t voffA[kMaxLoadsA], voffW[kLoadsW];  // the first TC::kLoadsA used
 #pragma unroll
-  for (int j = 0; j < kLoadsA; ++j) {
+  for (int j = 0; j < TC::kLoadsA; ++j) {
     const int r = (j * kWaves + wave) * 8 + (lane >> 3);  // tile row
     const int c = (lane & 7) ^ ((r ^ (r >> 3)) & 7);     // chunk at position lane%8
     const int m = m0 + r;
@@ -338,7 +358,7 @@ grouped_gemm_kernel(GemmArgs g) {
   // blocks); for SwiGLU those are 32 gate rows and the matching 32 up rows.
   const int fr = lane & 31;
   const int fh = lane >> 5;
-  int wrow[NB], arow_l[MB];
+  int wrow[NB], arow_l[kMaxMB];  // the first TC::MB used
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     if (MODE == kSwiGLU)
@@ -347,13 +367,13 @@ grouped_gemm_kernel(GemmArgs g) {
       wrow[nb] = wn * 64 + nb * 32 + fr;
   }
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) arow_l[mb] = wm * (MB * 32) + mb * 32 + fr;
+  for (int mb = 0; mb < TC::MB; ++mb) arow_l[mb] = wm * (TC::MB * 32) + mb * 32 + fr;
 
-  f32x16 acc[NB][MB];
+  f32x16 acc[NB][kMaxMB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int j = 0; j < MB; ++j)
+    for (int j = 0; j < TC::MB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -361,10 +381,10 @@ grouped_gemm_kernel(GemmArgs g) {
   const int kbase = split * KT;
   auto issue = [&](int kt, int buf) {
     const int soff = (kbase + kt) * kRowBytes;  // K advance in bytes
-    uint8_t* a = sA + buf * kTileBytesA;
-    uint8_t* w = sW + buf * kWBytes;
+    uint8_t* a = sA + buf * TC::kTileBytesA;
+    uint8_t* w = sW + buf * TC::kWBytes;
 #pragma unroll
-    for (int j = 0; j < kLoadsA; ++j)
+    for (int j = 0; j < TC::kLoadsA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsA, (__attribute__((address_space(3))) void*)(a + (j * kWaves + wave) * 1024), 16,
           voffA[j], soff, 0, 0);
@@ -399,7 +419,7 @@ grouped_gemm_kernel(GemmArgs g) {
   // it; dequantised weights then keep 11 bits instead of bf16's 8)
   constexpr bool kF16 = MODE == kDown || U4;
   using frag_t = typename std::conditional<kF16, half8, bf16x8>::type;
-  frag_t wf[2][NB], af[2][MB];
+  frag_t wf[2][NB], af[2][kMaxMB];
   bf16x8 wraw[2][NB];
   // 4-bit weights: a lane's codes for the whole K step (4 words: K chunks
   // 4*fh .. 4*fh+3 of its row), and the step's scale and bias of its rows.
@@ -409,16 +429,15 @@ grouped_gemm_kernel(GemmArgs g) {
   // unchanged, and each lane's codes are one 16-byte LDS read.
   uint4 qw[NB];
   float qs[NB], qb[NB];
-  auto read_frags = [&](int buf, int ks, int fb) {
-    const uint8_t* a = sA + buf * kTileBytesA;
-    const uint8_t* w = sW + buf * kWBytes;
+  auto read_frags = [&](int buf, int ks, int fb, int step) {
+    const uint8_t* a = sA + buf * TC::kTileBytesA;
+    const uint8_t* w = sW + buf * TC::kWBytes;
     const int ch = U4 ? fh * 4 + ks : ks * 2 + fh;
     if constexpr (U4) {
       if (ks == 0) {
-        // K step parity selects the bf16 half of the scale / bias dword
-        // (the down projection is never split, so the step index is the
-        // stage's parity)
-        const int hi = buf;
+        // the K step's parity selects the bf16 half of the scale / bias
+        // dword
+        const int hi = (kbase + step) & 1;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           qw[nb] = *reinterpret_cast<const uint4*>(w + wrow[nb] * 32 + fh * 16);
@@ -439,7 +458,7 @@ grouped_gemm_kernel(GemmArgs g) {
       }
     }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < TC::MB; ++mb)
       af[fb][mb] = *reinterpret_cast<const frag_t*>(a + swz(arow_l[mb], ch));
   };
   auto convert = [&](int fb, int ks) {
@@ -458,7 +477,7 @@ grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
+      for (int mb = 0; mb < TC::MB; ++mb) {
         if constexpr (kF16)
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
               wf[fb][nb], af[fb][mb], acc[nb][mb], 0, 0, 0);
@@ -481,20 +500,20 @@ grouped_gemm_kernel(GemmArgs g) {
   auto pace = [&]() {
     if constexpr (U4) {
 #pragma unroll
-      for (int i = 0; i < NB * MB; ++i) {
-        if (i < MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      for (int i = 0; i < NB * TC::MB; ++i) {
+        if (i < TC::MB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         __builtin_amdgcn_sched_group_barrier(0x002, kDeqValu, 0);      // VALU
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
       }
       return;
     }
 #pragma unroll
-    for (int i = 0; i < NB + MB; ++i) {
+    for (int i = 0; i < NB + TC::MB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
 #pragma unroll
-    for (int i = NB + MB; i < NB * MB; ++i) {
+    for (int i = NB + TC::MB; i < NB * TC::MB; ++i) {
       if (MODE == kDown) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
@@ -502,10 +521,10 @@ grouped_gemm_kernel(GemmArgs g) {
   // the sub-step that issues a K step's direct loads: fragment reads first,
   // then the loads spread evenly over its MFMAs
   auto pace_loads = [&]() {
-    constexpr int kV = kLoadsA + (U4 ? 2 : kLoadsW);  // direct loads in this sub-step
-    constexpr int NM = NB * MB;
+    constexpr int kV = TC::kLoadsA + (U4 ? 2 : kLoadsW);  // direct loads in this sub-step
+    constexpr int NM = NB * TC::MB;
     static_assert(kV <= 2 * NM, "load spread");
-    __builtin_amdgcn_sched_group_barrier(0x100, U4 ? MB + 3 * NB : NB + MB, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x100, U4 ? TC::MB + 3 * NB : NB + TC::MB, 0);  // DS read
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int n_here = ((i + 1) * kV) / NM - (i * kV) / NM;
@@ -516,39 +535,48 @@ grouped_gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
   };
-  // Load pipeline.  The loads of K tile t+1 go into the buffer that tile
-  // t-1 used: they are issued right after the barrier that ends tile t-1
-  // (that buffer is free from then on), during tile t-1's last MFMAs, so
-  // the memory pipe never idles across the barrier and tile t+1 has nearly
-  // a whole tile of MFMAs to arrive in.
+  // Load pipeline over TC::NST LDS stages; step t lives in stage t % TC::NST.  The
+  // loads of step t+TC::NST-1 go into the stage that step t-1 used: they are
+  // issued right after the barrier that ends step t-1 (that stage is free
+  // from then on), during step t-1's last MFMAs, so the memory pipe never
+  // idles across a barrier and TC::NST-1 steps of loads are in flight.  Before
+  // the barrier that publishes step t+1, a wave waits until only the loads
+  // issued after step t+1's (those of step t+2 when TC::NST = 3) are pending.
+  auto wait_publish = [&](bool later_in_flight) {
+    if (TC::NST > 2 && later_in_flight)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(TC::kStepLoads) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  };
   auto tile = [&](int kt, auto kind_tag) {
-    constexpr int kind = decltype(kind_tag)::value;  // 0 full, 1 no loads, 2 last
-    const int cur = kt & 1;
-    read_frags(cur, 1, 1);
+    constexpr int kind = decltype(kind_tag)::value;  // 0 issues loads, 1 none, 2 last
+    const int cur = kt % TC::NST;
+    const int nxt = (kt + 1) % TC::NST;
+    read_frags(cur, 1, 1, kt);
     mfmas(0);
     convert(1, 1);
     pace();
-    read_frags(cur, 2, 0);
+    read_frags(cur, 2, 0, kt);
     mfmas(1);
     convert(0, 2);
     pace();
-    read_frags(cur, 3, 1);
+    read_frags(cur, 3, 1, kt);
     mfmas(0);
     convert(1, 3);
     pace();
     if constexpr (kind != 2) {
-      // every read of this tile is issued: wait for them and for the next
-      // tile's loads, publish the next tile, read its first fragments ahead
-      // of this tile's last MFMAs, and start the loads of the tile after it
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      // every read of this step is issued: wait for them and for the next
+      // step's loads, publish the next step, read its first fragments ahead
+      // of this step's last MFMAs, and start the loads of a later step
+      wait_publish(kt + 2 < KT);
       __syncthreads();
       // down projection: the waves that leave the barrier first issue the
       // next loads and their last sub-step at raised priority (5% faster on
       // the Mixtral-shaped layer; the gate/up product is 1% slower with it)
       if constexpr (MODE == kDown) __builtin_amdgcn_s_setprio(1);
-      read_frags(cur ^ 1, 0, 0);
+      read_frags(nxt, 0, 0, kt + 1);
       if constexpr (kind == 0) {
-        issue(kt + 2, cur);
+        issue(kt + TC::NST, cur);
         mfmas(1);
         convert(0, 0);
         pace_loads();
@@ -566,12 +594,20 @@ grouped_gemm_kernel(GemmArgs g) {
 
   issue(0, 0);
   if (KT > 1) issue(1, 1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (TC::NST > 2 && KT > 2) issue(2, 2);
+  // step 0's loads: the later prologue steps' may stay in flight
+  if (TC::NST > 2 && KT > 2)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * TC::kStepLoads) : "memory");
+  else if (KT > 1)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(TC::kStepLoads) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  read_frags(0, 0, 0);
+  read_frags(0, 0, 0, 0);
   convert(0, 0);
-  for (int kt = 0; kt + 2 < KT; ++kt) tile(kt, std::integral_constant<int, 0>{});
-  if (KT > 1) tile(KT - 2, std::integral_constant<int, 1>{});
+  int kt = 0;
+  for (; kt + TC::NST < KT; ++kt) tile(kt, std::integral_constant<int, 0>{});
+  for (; kt + 1 < KT; ++kt) tile(kt, std::integral_constant<int, 1>{});
   tile(KT - 1, std::integral_constant<int, 2>{});
 
   // ---------------- epilogue
@@ -579,7 +615,7 @@ grouped_gemm_kernel(GemmArgs g) {
   //   colbase(nb) + 8*(v/4) + 4*(lane/32) + v%4, row arow_l[mb].
   bool sat = false;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
+  for (int mb = 0; mb < TC::MB; ++mb) {
     const int m = m0 + arow_l[mb];
     if (m >= cnt) continue;
     const int64_t orow_off = static_cast<int64_t>(row0 + m) * g.ldo;
@@ -663,46 +699,65 @@ int ntiles(int mode, int N) {
   return (N + cols - 1) / cols;
 }
 
-hipError_t launch_one(int mode, bool gather, const GemmArgs& g, int64_t mt_upper,
-                      hipStream_t s, bool u4 = false) {
-  int64_t n = mt_upper * g.NT * g.ksplit;
-  n = (n + 7) / 8 * 8;
-  if (n <= 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(n)), block(kThreads);
+template <int BMT>
+hipError_t launch_bm(int mode, bool gather, bool u4, const GemmArgs& g, dim3 grid,
+                     hipStream_t s) {
+  const dim3 block(kThreads);
   if (u4) {
     // routed experts only: the gate/up product gathers, the down one does not
     if (g.ksplit != 1) return hipErrorInvalidValue;
     if (mode == kSwiGLU && gather)
-      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, true, true>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, true, true, BMT>), grid, block, 0, s, g);
     else if (mode == kReLU && gather)
-      hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, true, true>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, true, true, BMT>), grid, block, 0, s, g);
     else if (mode == kDown && !gather)
-      hipLaunchKernelGGL((grouped_gemm_kernel<kDown, false, true>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((grouped_gemm_kernel<kDown, false, true, BMT>), grid, block, 0, s, g);
     else
       return hipErrorInvalidValue;
     return hipGetLastError();
   }
   if (mode == kSwiGLU && gather)
-    hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, true, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, true, false, BMT>), grid, block, 0, s, g);
   else if (mode == kSwiGLU)
-    hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, false, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<kSwiGLU, false, false, BMT>), grid, block, 0, s, g);
   else if (mode == kReLU && gather)
-    hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, true, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, true, false, BMT>), grid, block, 0, s, g);
   else if (mode == kReLU)
-    hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, false, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<kReLU, false, false, BMT>), grid, block, 0, s, g);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<kDown, false, false>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_kernel<kDown, false, false, BMT>), grid, block, 0, s, g);
   return hipGetLastError();
 }
 
+// rows_upper: an upper bound on the group's rows (single group) or on the
+// kept rows (grouped); the grid covers its M tiles plus one partial tile per
+// expert, rounded to whole XCD rounds
+hipError_t launch_one(int mode, bool gather, const GemmArgs& g, int64_t rows_upper, int bm,
+                      hipStream_t s, bool u4 = false) {
+  const int64_t mt_upper = g.tiles ? rows_upper / bm + g.E : (rows_upper + bm - 1) / bm;
+  int64_t n = mt_upper * g.NT * g.ksplit;
+  n = (n + 7) / 8 * 8;
+  if (n <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(n));
+  if (bm == 128) return launch_bm<128>(mode, gather, u4, g, grid, s);
+  if (bm == 256) return launch_bm<256>(mode, gather, u4, g, grid, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+int routed_bm(const Dims& D) {
+  if (!D.u4) return 256;
+  const int64_t nmax = std::min<int64_t>(D.slots, D.cap * D.E);
+  return nmax >= 64 * static_cast<int64_t>(D.E) ? 256 : 128;
+}
 
 int down_splits(const Dims& D) {
   if (!D.bf16 || D.u4) return 1;
   const int KT = D.F / BK;
   if (KT % 2 != 0 || KT < 16) return 1;
   const int64_t nmax = std::min<int64_t>(D.slots, D.cap * D.E);
-  const int64_t t = (nmax / BM + D.E) * ntiles(kDown, D.d);  // tile upper bound
+  const int64_t t = (nmax / routed_bm(D) + D.E) * ntiles(kDown, D.d);  // tile upper bound
   constexpr int64_t kCUs = 256;
   const int64_t half_rounds1 = (t + kCUs - 1) / kCUs * 2;
   const int64_t half_rounds2 = (2 * t + kCUs - 1) / kCUs;
@@ -713,7 +768,6 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
                               const moe_expert_weights& w, void* Hs, void* Ys,
                               int32_t* err, hipStream_t s) {
   const int up_mode = D.swiglu ? kSwiGLU : kReLU;
-  const int64_t mt = (D.T + BM - 1) / BM;
   const int64_t mat = static_cast<int64_t>(D.Fs) * D.d;  // one [Fs][d] matrix
   for (int sh = 0; sh < D.S; ++sh) {
     const int64_t wo = static_cast<int64_t>(sh) * mat;
@@ -737,7 +791,7 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
     g.NT = ntiles(up_mode, D.Fs);
     g.ksplit = 1;
     g.err = err;
-    hipError_t e = launch_one(up_mode, false, g, mt, s);
+    hipError_t e = launch_one(up_mode, false, g, D.T, 256, s);
     if (e != hipSuccess) return e;
     GemmArgs h{};
     h.a = static_cast<const uint16_t*>(Hs);
@@ -752,7 +806,7 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
     h.ldo = D.d;
     h.NT = ntiles(kDown, D.d);
     h.ksplit = 1;
-    e = launch_one(kDown, false, h, mt, s);
+    e = launch_one(kDown, false, h, D.T, 256, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -791,7 +845,7 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
     g.NT = ntiles(up_mode, D.F);
     g.ksplit = 1;
     g.err = err;
-    hipError_t e = launch_one(up_mode, true, g, nmax / BM + D.E, s);
+    hipError_t e = launch_one(up_mode, true, g, nmax, routed_bm(D), s);
     if (e != hipSuccess) return e;
     if (mid != nullptr && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
   }
@@ -812,7 +866,7 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
     g.ksplit = down_splits(D);
     g.part = Ypart;
     if (g.ksplit > 1 && Ypart == nullptr) return hipErrorInvalidValue;
-    hipError_t e = launch_one(kDown, false, g, nmax / BM + D.E, s);
+    hipError_t e = launch_one(kDown, false, g, nmax, routed_bm(D), s);
     if (e != hipSuccess) return e;
   }
   if (D.S > 0) return launch_shared_bf16(D, x, w, Hs, Ys, err, s);
@@ -865,7 +919,7 @@ hipError_t launch_ffn_u4_tiled(const Dims& D, const int32_t* offsets, const int3
     g.NT = ntiles(up_mode, D.F);
     g.ksplit = 1;
     g.err = err;
-    hipError_t e = launch_one(up_mode, true, g, nmax / BM + D.E, s, true);
+    hipError_t e = launch_one(up_mode, true, g, nmax, routed_bm(D), s, true);
     if (e != hipSuccess) return e;
     if (mid != nullptr && (e = hipEventRecord(mid, s)) != hipSuccess) return e;
   }
@@ -886,7 +940,7 @@ hipError_t launch_ffn_u4_tiled(const Dims& D, const int32_t* offsets, const int3
   g.ldo = D.d;
   g.NT = ntiles(kDown, D.d);
   g.ksplit = 1;
-  return launch_one(kDown, false, g, nmax / BM + D.E, s, true);
+  return launch_one(kDown, false, g, nmax, routed_bm(D), s, true);
 }
 
 }  // namespace moe

@@ -140,10 +140,14 @@ struct WsLayout {
 constexpr int kDispatchChunk = 2048;  // slots per dispatch block
 constexpr int kSelectWaves = 4;       // tokens in flight per select block
 
-// GEMM tile rows (M) of the bf16 grouped kernels; the dispatch scan writes
-// the per-expert M-tile prefix for them.
-constexpr int kGemm1BM = 256;
-constexpr int kGemm2BM = 256;
+// Tile rows (M) of the routed grouped GEMMs (gemm_bf16.hip), 128 or 256,
+// from the shapes only.  bf16 weights: 256 (measured: 128-row tiles with
+// three LDS stages stream each weight panel for twice as many row blocks and
+// were 15% slower on the DeepSeek-style down projection, no faster
+// elsewhere).  4-bit weights: 128-row tiles below 64 kept rows per expert on
+// average (less padding; 20% faster at 8-32 rows per expert), 256 above.
+// The dispatch scan writes the per-expert M-tile prefix for this size.
+int routed_bm(const Dims& D);
 
 // K splits of the grouped down projection (1 or 2).  Too few output tiles
 // for the chip leave its last round of workgroups mostly idle; splitting

@@ -69,6 +69,13 @@ MEDIUM = {
                                 capacity_factor=1.25),
     "u4-tiled-pow2": C("u4-tiled-pow2", 134, T=2048, d=1024, E=16, top_k=4, F=512,
                        weight_dtype=synth.U4),
+    # 128-row 4-bit tiles (under 64 rows per expert): 50 rows per expert on
+    # a power-of-two shape, and 8 rows per expert where the stream kernels
+    # cannot take the shape (d = 384)
+    "u4-tiled-128-rows": C("u4-tiled-128-rows", 137, T=400, d=512, E=32, top_k=4, F=256,
+                           weight_dtype=synth.U4),
+    "u4-tiled-few-rows": C("u4-tiled-few-rows", 138, T=64, d=384, E=16, top_k=2, F=256,
+                           weight_dtype=synth.U4),
     # fp32 path, SwiGLU and a shared expert
     "f32-swiglu-shared": C("f32-swiglu-shared", 111, T=150, d=48, E=5, top_k=2, F=40,
                            act_dtype=synth.F32, weight_dtype=synth.F32, shared_experts=2,
