@@ -138,7 +138,8 @@ class HipEvents:
         self.ev = []
 
 
-def time_layer(torch, moe, cfg, steps: int, warmup: int, n_rep: int):
+def time_layer(torch, moe, cfg, steps: int, warmup: int, n_rep: int, graph: bool = False,
+               split: bool = True):
     """Warm-up, then two timed passes of `steps` moe_layer_forward calls of
     workload `cfg`, rotating through `n_rep` independently drawn input
     copies: the first, plain, gives the per-step layer time (torch events
@@ -158,8 +159,11 @@ def time_layer(torch, moe, cfg, steps: int, warmup: int, n_rep: int):
     offs = [torch.empty(cfg.E + 1, dtype=torch.int32, device="cuda") for _ in reps]
     ev = HipEvents(3 * steps)
     plain = [moe.layer_stats(offsets=o) for o in offs]
+    # split=False: no event between the two expert kernels (for layers of a
+    # few tens of µs, where recording one costs a visible share)
     timed = [moe.layer_stats(offsets=offs[i % n_rep],
-                             ffn_events=ev.ev[3 * i:3 * i + 3]) for i in range(steps)]
+                             ffn_events=[ev.ev[3 * i], ev.ev[3 * i + 1] if split else 0,
+                                         ev.ev[3 * i + 2]]) for i in range(steps)]
 
     def step(i, st):
         r = i % n_rep
@@ -181,13 +185,46 @@ def time_layer(torch, moe, cfg, steps: int, warmup: int, n_rep: int):
         step(i, plain[i % n_rep])
     ms_step, wall = timed_pass(lambda i: plain[i % n_rep])
     ms_step_ev, _ = timed_pass(lambda i: timed[i])
-    up = [ev.ms(3 * i, 3 * i + 1) for i in range(steps)]
-    down = [ev.ms(3 * i + 1, 3 * i + 2) for i in range(steps)]
+    ms_graph = None
+    if graph:
+        # one HIP graph per input copy, captured from the same C-ABI call
+        # (kernels only: no memset, allocation or host synchronisation)
+        graphs = []
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            for r in range(n_rep):
+                step(r, plain[r])
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        for r in range(n_rep):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step(r, plain[r])
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        for i in range(max(warmup, n_rep)):
+            graphs[i % n_rep].replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for i in range(steps):
+            graphs[i % n_rep].replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_graph = g0.elapsed_time(g1) / steps
+    if split:
+        up = [ev.ms(3 * i, 3 * i + 1) for i in range(steps)]
+        down = [ev.ms(3 * i + 1, 3 * i + 2) for i in range(steps)]
+    else:  # the whole expert FFN as "up", nothing as "down"
+        up = [ev.ms(3 * i, 3 * i + 2) for i in range(steps)]
+        down = [0.0] * steps
     ev.close()
     kept = [int(o[-1].item()) for o in offs]
     touched = [int((o[1:] - o[:-1] > 0).sum().item()) for o in offs]
-    return {"ms_step": ms_step, "ms_step_events": ms_step_ev, "wall": wall, "up": up,
-            "down": down, "kept": kept, "touched": touched, "inp": reps[0]}
+    return {"ms_step": ms_step, "ms_step_events": ms_step_ev, "ms_step_graph": ms_graph,
+            "wall": wall, "up": up, "down": down, "kept": kept, "touched": touched,
+            "inp": reps[0]}
 
 
 def decode_leg(torch, moe, steps: int, warmup: int):
@@ -195,12 +232,14 @@ def decode_leg(torch, moe, steps: int, warmup: int):
     SwiGLU 512), timed like the headline workload over three rotated input
     copies (its ~290 MB of touched weights would otherwise sit in the
     256 MB last-level cache between steps); HBM roofline of the layer and of
-    its two 4-bit expert kernels."""
+    its two 4-bit expert kernels (timed together, between two events the
+    layer records before the first and after the second); the layer also
+    replayed from HIP graphs."""
     import synth
     cfg = synth.CONFIGS[5]
     n_rep = 3
-    r = time_layer(torch, moe, cfg, steps, warmup, n_rep)
-    ffn = [a + b for a, b in zip(r["up"], r["down"])]
+    r = time_layer(torch, moe, cfg, steps, warmup, n_rep, graph=True, split=False)
+    ffn = r["up"]
 
     def ffn_bytes(j):
         return (r["touched"][j] * u4_expert_bytes(cfg) + cfg.T * cfg.d * 2
@@ -213,8 +252,9 @@ def decode_leg(torch, moe, steps: int, warmup: int):
             "input_copies_rotated": n_rep,
             "layer_us": r["ms_step"] * 1e3, "tokens_per_s": cfg.T / (r["ms_step"] / 1e3),
             "layer_us_with_events": r["ms_step_events"] * 1e3,
-            "ffn_us": ffn_ms * 1e3, "ffn_up_us": sum(r["up"]) / steps * 1e3,
-            "ffn_down_us": sum(r["down"]) / steps * 1e3,
+            "layer_us_graph_replay": r["ms_step_graph"] * 1e3,
+            "tokens_per_s_graph_replay": cfg.T / (r["ms_step_graph"] / 1e3),
+            "ffn_us": ffn_ms * 1e3,
             "touched_experts": r["touched"],
             "ffn_bytes_per_call": byts,
             "ffn_hbm_gbs": byts / (ffn_ms / 1e3) / 1e9,
