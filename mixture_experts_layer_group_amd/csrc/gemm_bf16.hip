@@ -202,6 +202,54 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, float sc, float bi, uint32
 // LDS ring has three stages where they fit the 160 KiB of LDS (128-row
 // tiles, 4-bit weights), so two K steps of loads are in flight during a
 // step's products; two for 256-row tiles of bf16 weights.
+// Which tile a workgroup computes.  The grid is an upper bound on the tile
+// count (ragged groups, no host sync): a workgroup reads the per-expert
+// M-tile prefix that the dispatch wrote and returns false if surplus.
+// Workgroup ids are remapped so each of the 8 XCDs (hardware dispatch is
+// round-robin over XCDs) gets a contiguous range of tiles, in expert-major
+// order: per expert, groups of kNG N-tiles; inside a group the expert's
+// M-tiles run fastest, so the workgroups that run together on one XCD share
+// each weight tile and the expert's activation rows.
+struct TileSched {
+  int e, row0, cnt, mt, nt, split;
+};
+
+__device__ __forceinline__ bool schedule_tile(const GemmArgs& g, int bm, TileSched& t) {
+  const int total_mt = g.tiles ? g.tiles[g.E] : (g.single_rows + bm - 1) / bm;
+  const int real = total_mt * g.NT;
+  const int share = (real * g.ksplit + 7) >> 3;
+  const int bid = blockIdx.x;
+  const int local = bid >> 3;
+  if (local >= share) return false;
+  int L = (bid & 7) * share + local;
+  if (L >= real * g.ksplit) return false;
+  t.split = L / real;  // K split (slowest, so each split's tiles keep their order)
+  L -= t.split * real;
+  t.e = 0;
+  const int32_t* tp = g.tiles;
+  int t0 = 0, t1 = total_mt;
+  if (tp) {
+    t.e = largest_le(tp, g.E, L / g.NT);
+    t0 = tp[t.e];
+    t1 = tp[t.e + 1];
+  }
+  const int mte = t1 - t0;
+  const int rem = L - t0 * g.NT;
+  const int full = g.NT / kNG;
+  const int grp = rem / (mte * kNG);
+  const int r2 = rem - (grp < full ? grp : full) * mte * kNG;
+  t.nt = (grp < full ? grp : full) * kNG + r2 / mte;
+  t.mt = r2 % mte;
+  if (tp) {
+    t.row0 = g.offsets[t.e];
+    t.cnt = g.offsets[t.e + 1] - t.row0;
+  } else {
+    t.row0 = 0;
+    t.cnt = g.single_rows;
+  }
+  return true;
+}
+
 // the largest per-variant counts, for array sizes: arrays sized by a
 // template-dependent count and captured by the kernel's lambdas lose the
 // kernel's host-side launch stub
@@ -230,49 +278,9 @@ grouped_gemm_kernel(GemmArgs g) {
   uint8_t* sW = smem + TC::NST * TC::kTileBytesA;  // [NST][BN rows][128 B]; 4-bit: codes, scales, biases
 
   // ---------------- tile scheduling
-  const int total_mt = g.tiles ? g.tiles[g.E] : (g.single_rows + TC::BM - 1) / TC::BM;
-  const int real = total_mt * g.NT;
-  const int share = (real * g.ksplit + 7) >> 3;
-  const int bid = blockIdx.x;
-  const int local = bid >> 3;
-  if (local >= share) return;
-  int L = (bid & 7) * share + local;
-  if (L >= real * g.ksplit) return;
-  const int split = L / real;  // K split (slowest, so each split's tiles keep their order)
-  L -= split * real;
-  int e = 0, row0, cnt, mt, nt;
-  {
-    // expert-major order: per expert, groups of kNG N-tiles; inside a group
-    // the expert's M-tiles run fastest, so the workgroups that run together
-    // on one XCD share each weight tile and the expert's activation rows
-    const int32_t* tp = g.tiles;
-    int t0 = 0, t1 = total_mt;
-    if (tp) {
-      e = largest_le(tp, g.E, L / g.NT);
-      t0 = tp[e];
-      t1 = tp[e + 1];
-    }
-    const int mte = t1 - t0;
-    const int rem = L - t0 * g.NT;
-    const int full = g.NT / kNG;
-    const int grp = rem / (mte * kNG);
-    if (grp < full) {
-      const int r2 = rem - grp * mte * kNG;
-      nt = grp * kNG + r2 / mte;
-      mt = r2 % mte;
-    } else {
-      const int r2 = rem - full * mte * kNG;
-      nt = full * kNG + r2 / mte;
-      mt = r2 % mte;
-    }
-    if (tp) {
-      row0 = g.offsets[e];
-      cnt = g.offsets[e + 1] - row0;
-    } else {
-      row0 = 0;
-      cnt = g.single_rows;
-    }
-  }
+  TileSched ts;
+  if (!schedule_tile(g, TC::BM, ts)) return;
+  const int e = ts.e, row0 = ts.row0, cnt = ts.cnt, mt = ts.mt, nt = ts.nt, split = ts.split;
   const int m0 = mt * TC::BM;  // first row of this tile inside the group
 
   const int tid = threadIdx.x;
@@ -429,7 +437,17 @@ grouped_gemm_kernel(GemmArgs g) {
   // unchanged, and each lane's codes are one 16-byte LDS read.
   uint4 qw[NB];
   float qs[NB], qb[NB];
+  // A wave's K loop is specialised to MBA, the number of its activation
+  // blocks that hold rows of the group (the wave's share of the tile's
+  // rows, in 32-row blocks): in a ragged last tile the empty blocks get no
+  // fragment reads and no products, so their SIMD's matrix core takes the
+  // other wave's products sooner.  Every wave still issues its share of the
+  // direct loads and meets every barrier.
+  auto run = [&](auto mba_tag) {
+  constexpr int MBA = decltype(mba_tag)::value;
+  constexpr bool kFull = MBA == TC::MB;
   auto read_frags = [&](int buf, int ks, int fb, int step) {
+    if constexpr (MBA == 0) return;
     const uint8_t* a = sA + buf * TC::kTileBytesA;
     const uint8_t* w = sW + buf * TC::kWBytes;
     const int ch = U4 ? fh * 4 + ks : ks * 2 + fh;
@@ -458,10 +476,11 @@ grouped_gemm_kernel(GemmArgs g) {
       }
     }
 #pragma unroll
-    for (int mb = 0; mb < TC::MB; ++mb)
+    for (int mb = 0; mb < MBA; ++mb)
       af[fb][mb] = *reinterpret_cast<const frag_t*>(a + swz(arow_l[mb], ch));
   };
   auto convert = [&](int fb, int ks) {
+    if constexpr (MBA == 0) return;
     if constexpr (U4) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -477,7 +496,7 @@ grouped_gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < TC::MB; ++mb) {
+      for (int mb = 0; mb < MBA; ++mb) {
         if constexpr (kF16)
           acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
               wf[fb][nb], af[fb][mb], acc[nb][mb], 0, 0, 0);
@@ -496,8 +515,11 @@ grouped_gemm_kernel(GemmArgs g) {
   // conversions (about 12 VALU ops per fragment) in the second half.
   // 4-bit weights: the dequantisation (about 23 VALU ops per fragment, 2
   // fragments per sub-step) is spread evenly over the sub-step's MFMAs.
+  // A wave with empty blocks (MBA < MB) runs short of products to pace
+  // against and is left to the compiler's schedule.
   constexpr int kDeqValu = 6;
   auto pace = [&]() {
+    if constexpr (!kFull) return;
     if constexpr (U4) {
 #pragma unroll
       for (int i = 0; i < NB * TC::MB; ++i) {
@@ -521,6 +543,7 @@ grouped_gemm_kernel(GemmArgs g) {
   // the sub-step that issues a K step's direct loads: fragment reads first,
   // then the loads spread evenly over its MFMAs
   auto pace_loads = [&]() {
+    if constexpr (!kFull) return;
     constexpr int kV = TC::kLoadsA + (U4 ? 2 : kLoadsW);  // direct loads in this sub-step
     constexpr int NM = NB * TC::MB;
     static_assert(kV <= 2 * NM, "load spread");
@@ -609,6 +632,26 @@ grouped_gemm_kernel(GemmArgs g) {
   for (; kt + TC::NST < KT; ++kt) tile(kt, std::integral_constant<int, 0>{});
   for (; kt + 1 < KT; ++kt) tile(kt, std::integral_constant<int, 1>{});
   tile(KT - 1, std::integral_constant<int, 2>{});
+
+  };
+  // this wave's rows of the tile, in 32-row blocks
+  const int wave_rows = cnt - m0 - wm * (TC::MB * 32);
+  const int mba = wave_rows <= 0 ? 0 : (wave_rows + 31) / 32;
+  if (mba >= TC::MB) {
+    run(std::integral_constant<int, TC::MB>{});
+  } else if (mba == 0) {
+    run(std::integral_constant<int, 0>{});
+  } else if constexpr (TC::MB == 4) {
+    if (mba == 1)
+      run(std::integral_constant<int, 1>{});
+    else if (mba == 2)
+      run(std::integral_constant<int, 2>{});
+    else
+      run(std::integral_constant<int, 3>{});
+  } else {
+    static_assert(TC::MB == 2, "tile rows");
+    run(std::integral_constant<int, 1>{});
+  }
 
   // ---------------- epilogue
   // lane holds, for block (nb, mb) and item v: output column

@@ -18,6 +18,11 @@ C = synth.LayerConfig
 MEDIUM = {
     # several M tiles per expert with a ragged tail; N tails in both GEMMs
     "swiglu-bf16-ragged": C("swiglu-bf16-ragged", 101, T=2000, d=576, E=4, top_k=2, F=704),
+    # about 250 rows per expert in one ragged M tile: each of the tile's two
+    # 128-row halves holds 0 to 4 non-empty 32-row blocks, so the K loop's
+    # specialisations by block count all run, on both GEMMs
+    "swiglu-bf16-partial-blocks": C("swiglu-bf16-partial-blocks", 139, T=1000, d=320, E=8,
+                                    top_k=2, F=320),
     # Zipf-skewed popularity with capacity: heavy drops
     "swiglu-bf16-zipf-capacity": C("swiglu-bf16-zipf-capacity", 102, T=1500, d=512, E=8,
                                    top_k=2, F=512, capacity_factor=1.0, zipf_s=1.1),
