@@ -263,8 +263,17 @@ struct TileCfg {
   static constexpr int kLoadsA = kTileBytesA / 1024 / kWaves;  // 1 KiB direct loads per wave
   static constexpr int kWBytes = U4 ? kTileBytesQ : kTileBytesW;  // weight stage
   static constexpr int NST = (kTileBytesA + kWBytes) * 3 <= 160 * 1024 ? 3 : 2;
+  // LDS stages of the activation and of the weight tiles: NST each, except
+  // where three stages of both do not fit and a third weight stage does
+  // (256-row bf16 tiles: 2 x 32 KiB + 3 x 32 KiB = 160 KiB), which puts the
+  // weights -- streamed from HBM -- two steps ahead and the activations,
+  // mostly served by the caches, one
+  static constexpr int NSA = NST;
+  static constexpr int NSW =
+      NST == 2 && 2 * kTileBytesA + 3 * kWBytes <= 160 * 1024 ? 3 : NST;
+  static constexpr int kLoadsWStep = U4 ? 2 : kLoadsW;
   // direct loads per K step and wave (vmcnt counts them in issue order)
-  static constexpr int kStepLoads = kLoadsA + (U4 ? 2 : kLoadsW);
+  static constexpr int kStepLoads = kLoadsA + kLoadsWStep;
   static_assert(BM % 128 == 0 && kTileBytesA % (1024 * kWaves) == 0, "whole direct loads");
   static_assert(MB <= kMaxMB && kLoadsA <= kMaxLoadsA, "array bounds");
 };
@@ -273,9 +282,9 @@ template <int MODE, bool GATHER, bool U4, int BMT>
 __global__ void __launch_bounds__(kThreads, 1)
 grouped_gemm_kernel(GemmArgs g) {
   using TC = TileCfg<BMT, U4>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[TC::NST * (TC::kTileBytesA + TC::kWBytes)];
-  uint8_t* sA = smem;                              // [NST][BM rows][128 B]
-  uint8_t* sW = smem + TC::NST * TC::kTileBytesA;  // [NST][BN rows][128 B]; 4-bit: codes, scales, biases
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TC::NSA * TC::kTileBytesA + TC::NSW * TC::kWBytes];
+  uint8_t* sA = smem;                              // [NSA][BM rows][128 B]
+  uint8_t* sW = smem + TC::NSA * TC::kTileBytesA;  // [NSW][BN rows][128 B]; 4-bit: codes, scales, biases
 
   // ---------------- tile scheduling
   TileSched ts;
@@ -285,7 +294,9 @@ grouped_gemm_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform to the compiler: descriptors and LDS addresses derived
+  // from it stay in scalar registers (no per-lane waterfall loops)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / kWavesN, wn = wave % kWavesN;
 
   // ---------------- direct-to-LDS load descriptors
@@ -344,13 +355,13 @@ grouped_gemm_kernel(GemmArgs g) {
   if constexpr (U4) {
     const int64_t erow = static_cast<int64_t>(e) * g.qstride;  // expert's first row
     const int rq = wave * 32 + (lane >> 1);
-    const bool up_q = MODE == kSwiGLU && rq >= 128;
+    const bool up_q = MODE == kSwiGLU && wave >= 4;  // rq >= 128
     qptr = (up_q ? g.q1 : g.q0) + erow * (K / 2);
     qbytes = static_cast<int>(static_cast<int64_t>(g.N) * (K / 2));
     voffQ = static_cast<uint32_t>(static_cast<int64_t>(tile_row_n(rq)) * (K / 2) +
                                   (lane & 1) * 16);
     const int rs = (wave & 3) * 64 + lane;
-    const bool up_s = MODE == kSwiGLU && rs >= 128;
+    const bool up_s = MODE == kSwiGLU && (wave & 3) >= 2;  // rs >= 128
     sbptr = (wave < 4 ? (up_s ? g.s1 : g.s0) : (up_s ? g.b1 : g.b0)) + erow * G;
     sbbytes = static_cast<int>(static_cast<int64_t>(g.N) * G * 2);
     voffSB = static_cast<uint32_t>(static_cast<int64_t>(tile_row_n(rs)) * G * 2);
@@ -387,15 +398,20 @@ grouped_gemm_kernel(GemmArgs g) {
 
   const int KT = g.K / BK / g.ksplit;  // K steps of this split
   const int kbase = split * KT;
-  auto issue = [&](int kt, int buf) {
+  // the direct loads of K step kt: activations into stage kt % NSA,
+  // weights into stage kt % NSW
+  auto issue_a = [&](int kt) {
     const int soff = (kbase + kt) * kRowBytes;  // K advance in bytes
-    uint8_t* a = sA + buf * TC::kTileBytesA;
-    uint8_t* w = sW + buf * TC::kWBytes;
+    uint8_t* a = sA + (kt % TC::NSA) * TC::kTileBytesA;
 #pragma unroll
     for (int j = 0; j < TC::kLoadsA; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsA, (__attribute__((address_space(3))) void*)(a + (j * kWaves + wave) * 1024), 16,
           voffA[j], soff, 0, 0);
+  };
+  auto issue_w = [&](int kt) {
+    const int soff = (kbase + kt) * kRowBytes;  // K advance in bytes
+    uint8_t* w = sW + (kt % TC::NSW) * TC::kWBytes;
     if constexpr (U4) {
       const int step = kbase + kt;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -446,10 +462,11 @@ grouped_gemm_kernel(GemmArgs g) {
   auto run = [&](auto mba_tag) {
   constexpr int MBA = decltype(mba_tag)::value;
   constexpr bool kFull = MBA == TC::MB;
-  auto read_frags = [&](int buf, int ks, int fb, int step) {
+  // K step `step` (activations in stage sa, weights in stage sw)
+  auto read_frags = [&](int sa, int sw, int step, int ks, int fb) {
     if constexpr (MBA == 0) return;
-    const uint8_t* a = sA + buf * TC::kTileBytesA;
-    const uint8_t* w = sW + buf * TC::kWBytes;
+    const uint8_t* a = sA + sa * TC::kTileBytesA;
+    const uint8_t* w = sW + sw * TC::kWBytes;
     const int ch = U4 ? fh * 4 + ks : ks * 2 + fh;
     if constexpr (U4) {
       if (ks == 0) {
@@ -558,78 +575,94 @@ grouped_gemm_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     }
   };
-  // Load pipeline over TC::NST LDS stages; step t lives in stage t % TC::NST.  The
-  // loads of step t+TC::NST-1 go into the stage that step t-1 used: they are
-  // issued right after the barrier that ends step t-1 (that stage is free
-  // from then on), during step t-1's last MFMAs, so the memory pipe never
-  // idles across a barrier and TC::NST-1 steps of loads are in flight.  Before
-  // the barrier that publishes step t+1, a wave waits until only the loads
-  // issued after step t+1's (those of step t+2 when TC::NST = 3) are pending.
+  // Load pipeline: K step t's activations live in stage t % NSA, its
+  // weights in stage t % NSW (NSA <= NSW).  Right after the barrier that
+  // ends step t-1 (from then on both of its stages are free) a wave issues
+  // the activations of step t-1+NSA, then the weights of step t-1+NSW,
+  // during step t-1's last MFMAs, so the memory pipe never idles across a
+  // barrier.  The prologue issues steps 0.. in the same order (activations
+  // before weights within a step).  Before the barrier that publishes step
+  // t+1, a wave waits until only the loads issued after step t+1's are
+  // pending: those of step t+2 (NSA = NSW = 3), or the weights of step t+2
+  // (NSA = 2, NSW = 3); vector-memory loads retire in issue order.
+  constexpr int kLaterLoads = TC::NSW == 3 ? (TC::NSA == 3 ? TC::kStepLoads : TC::kLoadsWStep) : 0;
   auto wait_publish = [&](bool later_in_flight) {
-    if (TC::NST > 2 && later_in_flight)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(TC::kStepLoads) : "memory");
+    if (kLaterLoads > 0 && later_in_flight)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kLaterLoads) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   };
   auto tile = [&](int kt, auto kind_tag) {
-    constexpr int kind = decltype(kind_tag)::value;  // 0 issues loads, 1 none, 2 last
-    const int cur = kt % TC::NST;
-    const int nxt = (kt + 1) % TC::NST;
-    read_frags(cur, 1, 1, kt);
+    // 0 issues both operands' loads, 3 the activations' only, 1 none, 2 last
+    constexpr int kind = decltype(kind_tag)::value;
+    const int ca = kt % TC::NSA, cw = TC::NSA == TC::NSW ? ca : kt % TC::NSW;
+    read_frags(ca, cw, kt, 1, 1);
     mfmas(0);
     convert(1, 1);
     pace();
-    read_frags(cur, 2, 0, kt);
+    read_frags(ca, cw, kt, 2, 0);
     mfmas(1);
     convert(0, 2);
     pace();
-    read_frags(cur, 3, 1, kt);
+    read_frags(ca, cw, kt, 3, 1);
     mfmas(0);
     convert(1, 3);
     pace();
     if constexpr (kind != 2) {
       // every read of this step is issued: wait for them and for the next
       // step's loads, publish the next step, read its first fragments ahead
-      // of this step's last MFMAs, and start the loads of a later step
+      // of this step's last MFMAs, and start the loads of later steps
       wait_publish(kt + 2 < KT);
       __syncthreads();
       // down projection: the waves that leave the barrier first issue the
       // next loads and their last sub-step at raised priority (5% faster on
       // the Mixtral-shaped layer; the gate/up product is 1% slower with it)
       if constexpr (MODE == kDown) __builtin_amdgcn_s_setprio(1);
-      read_frags(nxt, 0, 0, kt + 1);
+      const int na = (kt + 1) % TC::NSA;
+      read_frags(na, TC::NSA == TC::NSW ? na : (kt + 1) % TC::NSW, kt + 1, 0, 0);
       if constexpr (kind == 0) {
-        issue(kt + TC::NST, cur);
+        issue_a(kt + TC::NSA);
+        issue_w(kt + TC::NSW);
         mfmas(1);
         convert(0, 0);
         pace_loads();
-        if constexpr (MODE == kDown) __builtin_amdgcn_s_setprio(0);
       } else {
+        if constexpr (kind == 3) issue_a(kt + TC::NSA);
         mfmas(1);
         convert(0, 0);
         pace();
-        if constexpr (MODE == kDown) __builtin_amdgcn_s_setprio(0);
       }
+      if constexpr (MODE == kDown) __builtin_amdgcn_s_setprio(0);
     } else {
       mfmas(1);
     }
   };
 
-  issue(0, 0);
-  if (KT > 1) issue(1, 1);
-  if (TC::NST > 2 && KT > 2) issue(2, 2);
+  issue_a(0);
+  issue_w(0);
+  if (KT > 1) {
+    issue_a(1);
+    issue_w(1);
+  }
+  if (KT > 2) {
+    if constexpr (TC::NSA > 2) issue_a(2);
+    if constexpr (TC::NSW > 2) issue_w(2);
+  }
   // step 0's loads: the later prologue steps' may stay in flight
-  if (TC::NST > 2 && KT > 2)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * TC::kStepLoads) : "memory");
+  constexpr int kPro2 = (TC::NSA > 2 ? TC::kLoadsA : 0) + (TC::NSW > 2 ? TC::kLoadsWStep : 0);
+  if (kPro2 > 0 && KT > 2)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(TC::kStepLoads + kPro2) : "memory");
   else if (KT > 1)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(TC::kStepLoads) : "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  read_frags(0, 0, 0, 0);
+  read_frags(0, 0, 0, 0, 0);
   convert(0, 0);
   int kt = 0;
-  for (; kt + TC::NST < KT; ++kt) tile(kt, std::integral_constant<int, 0>{});
+  for (; kt + TC::NSW < KT; ++kt) tile(kt, std::integral_constant<int, 0>{});
+  if constexpr (TC::NSA < TC::NSW)
+    for (; kt + TC::NSA < KT; ++kt) tile(kt, std::integral_constant<int, 3>{});
   for (; kt + 1 < KT; ++kt) tile(kt, std::integral_constant<int, 1>{});
   tile(KT - 1, std::integral_constant<int, 2>{});
 
