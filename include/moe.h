@@ -299,7 +299,8 @@ moe_status moe_dispatch(const moe_spec* spec, int64_t T,
  * bf16 activations use matrix cores with fp32 accumulation: bf16 x bf16
  * for the gate/up product, whose hidden activation is rounded to fp16
  * (saturating at +-65504), then fp16 x fp16 for the down product (the bf16
- * weights are converted exactly in registers); expert outputs stay fp32.
+ * weights are rounded to the nearest fp16 in registers: exact for
+ * magnitudes from 2^-17 to 65504); expert outputs stay fp32.
  * 4-bit weights (Edge0 page, QuantSpec): decode-sized groups (under 32 kept
  * rows per expert on average) stream each expert's codes once per 4 rows
  * with the affine term factored per group; larger groups run 256 x 256

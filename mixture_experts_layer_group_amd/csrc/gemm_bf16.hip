@@ -153,17 +153,21 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b, bool& sat) {
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hb)) << 16);
 }
 
-// 8 bf16 weights -> 8 fp16 (exact for normal fp16 values; v_cvt_pkrtz
-// saturates instead of overflowing)
+// 8 bf16 weights -> 8 fp16, rounded to nearest (v_cvt_pk_f16_f32, one
+// instruction per pair): exact for magnitudes from 2^-17 (where fp16's
+// subnormal grid still holds bf16's 8 significant bits) up to 65504; smaller
+// ones land on the nearest multiple of 2^-24, larger ones become +-inf
 __device__ __forceinline__ half8 bf16x8_to_f16x8(bf16x8 v) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const uint4 u = __builtin_bit_cast(uint4, v);
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
   uint32_t o[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    o[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
-                                            __uint_as_float(w[j] << 16),
-                                            __uint_as_float(w[j] & 0xffff0000u)));
+  for (int j = 0; j < 4; ++j) {
+    const f2 f = {__uint_as_float(w[j] << 16), __uint_as_float(w[j] & 0xffff0000u)};
+    o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, h2));
+  }
   return __builtin_bit_cast(half8, make_uint4(o[0], o[1], o[2], o[3]));
 }
 

@@ -245,10 +245,8 @@ def check_output(cfg, inp, r, ids_g, w_o, disp, tokens: Optional[Sequence[int]] 
                                  spec_dict(cfg), toks)
     got = r["out"].float().cpu().numpy().astype(np.float64)[toks]
     rms = math.sqrt(float(np.mean(ref ** 2)))
+    # bf16 output: the same bar, the final rounding to bf16 included
     absdiff = np.abs(got - ref)
-    if cfg.out_dtype == synth.BF16:
-        # the final rounding of the output to bf16 adds at most half an ulp
-        absdiff = np.maximum(absdiff - 2.0 ** -8 * np.abs(ref), 0.0)
     err = float(absdiff.max())
     log(f"  output: {len(toks)} tokens, max|err| {err:.3e}, RMS(ref) {rms:.3e}, "
         f"ratio {err / max(rms, 1e-300):.2e} (bar {tol}), oracle {time.time() - t0:.1f}s")
