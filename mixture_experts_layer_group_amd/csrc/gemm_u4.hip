@@ -203,7 +203,15 @@ __device__ __forceinline__ void dma4(rsrc_t rs, uint32_t lds, uint32_t voff) {
                : "memory");
 }
 
-// wait until at most N vector-memory operations of this wave are pending
+// wait until at most N vector-memory operations of this wave are pending.
+// The counted waits of the ring rest on two facts: every load of an item is
+// issued by the wave (the loads are asm statements, which the compiler can
+// neither drop nor merge; the one lane-dependent condition, on the scale and
+// bias loads when K = 64, holds for lanes 0-31 of every wave), and
+// vector-memory operations retire in issue order.  Any other vector-memory operation the
+// compiler places between an item's loads and its wait only makes the count
+// more conservative: whether it is older or younger than the awaited item,
+// "at most N pending" still implies that the item's loads have retired.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
