@@ -34,10 +34,12 @@ __device__ __forceinline__ void store8(float* p, const float* v) {
 
 constexpr int kMaxSlots = 64;
 
-// One block per token; expert outputs are fp32, the result is written in
-// the output type.
+// One block per token of d/8 threads (up to 1024, whole waves): each thread
+// owns 8 consecutive columns, so a row is one pass; the token's kept rows
+// are loaded in groups of 4 before they are added (in slot order).  Expert
+// outputs are fp32, the result is written in the output type.
 template <typename OutT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(1024)
 combine_kernel(const float* __restrict__ y, const float* __restrict__ ypart,
                const int32_t* __restrict__ slot_row,
                const float* __restrict__ topk_w, const float* __restrict__ ysh,
@@ -52,20 +54,28 @@ combine_kernel(const float* __restrict__ y, const float* __restrict__ ypart,
   __syncthreads();
   for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < k; ++i) {
-      const int32_t r = rows[i];
-      if (r < 0) continue;
-      float v[8];
-      load8(y + static_cast<int64_t>(r) * d + c, v);
-      if (ypart) {
-        float u[8];
-        load8(ypart + static_cast<int64_t>(r) * d + c, u);
+    for (int i0 = 0; i0 < k; i0 += 4) {
+      float v[4][8], u[4][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] += u[j];
+      for (int jj = 0; jj < 4; ++jj) {
+        const int i = i0 + jj;
+        const int32_t r = i < k ? rows[i] : -1;
+        if (r < 0) continue;
+        load8(y + static_cast<int64_t>(r) * d + c, v[jj]);
+        if (ypart) load8(ypart + static_cast<int64_t>(r) * d + c, u[jj]);
       }
-      const float wi = wts[i];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] = fmaf(wi, v[j], acc[j]);
+      for (int jj = 0; jj < 4; ++jj) {
+        const int i = i0 + jj;
+        if (i >= k || rows[i] < 0) continue;
+        if (ypart) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[jj][j] += u[jj][j];
+        }
+        const float wi = wts[i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(wi, v[jj][j], acc[j]);
+      }
     }
     for (int s = 0; s < S; ++s) {
       float v[8];
@@ -109,15 +119,16 @@ hipError_t launch_combine(const Dims& D, const void* y_rows, const float* y_part
                           const void* y_shared, void* out, hipStream_t s) {
   if (D.k > kMaxSlots) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(D.T));
+  const int threads = std::min(1024, (D.d / 8 + 63) / 64 * 64);  // >= 64 >= k
   const int S = y_shared ? D.S : 0;
   const float* y = static_cast<const float*>(y_rows);
   const float* ys = static_cast<const float*>(y_shared);
   if (D.out_bf16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, s, y, y_part,
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(threads), 0, s, y, y_part,
                        slot_row, topk_w, ys, static_cast<uint16_t*>(out), D.T,
                        D.k, S, D.d);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, s, y, y_part, slot_row,
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(threads), 0, s, y, y_part, slot_row,
                        topk_w, ys, static_cast<float*>(out), D.T, D.k, S, D.d);
   return hipGetLastError();
 }

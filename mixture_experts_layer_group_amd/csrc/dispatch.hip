@@ -29,8 +29,18 @@ count_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
   const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
   const int64_t s1 = min(S, s0 + kDispatchChunk);
   bool bad = false;  // an id outside [0,E): its slot is dropped
-  for (int64_t s = s0 + threadIdx.x; s < s1; s += blockDim.x) {
-    const int e = ids[s];
+  // the chunk's ids are all loaded before they are counted
+  constexpr int kRounds = kDispatchChunk / 256;
+  int idv[kRounds];
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    const int64_t s = s0 + q * 256 + threadIdx.x;
+    idv[q] = s < s1 ? ids[s] : 0;
+  }
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    if (s0 + q * 256 + threadIdx.x >= s1) break;
+    const int e = idv[q];
     if (e >= 0 && e < E) atomicAdd(&h[e], 1);
     else bad = true;
   }
@@ -113,11 +123,19 @@ scan_kernel(int32_t* __restrict__ hist, int nb, int E, int64_t S, int64_t cap,
   const int e = threadIdx.x;
   int32_t run = 0;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) {
-      const int64_t i = static_cast<int64_t>(b) * E + e;
-      const int32_t c = hist[i];
-      hist[i] = run;
-      run += c;
+    // blocks in groups of kG: the group's counts are all loaded before any
+    // is replaced by its base (one memory round trip per group, not per block)
+    constexpr int kG = 32;
+    for (int b0 = 0; b0 < nb; b0 += kG) {
+      int32_t c[kG];
+#pragma unroll
+      for (int j = 0; j < kG; ++j)
+        c[j] = b0 + j < nb ? hist[static_cast<int64_t>(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kG; ++j) {
+        if (b0 + j < nb) hist[static_cast<int64_t>(b0 + j) * E + e] = run;
+        run += c[j];
+      }
     }
   }
   expert_prefixes(e, E, run, S, cap, counts, offsets, dropped, tiles1, bm1,
@@ -134,22 +152,38 @@ scatter_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
   extern __shared__ int32_t sm[];
   int32_t* run = sm;            // [E] running rank per expert
   int32_t* wcnt = sm + E;       // [4][E] per-wave counts of this round
+  int32_t* offs = sm + 5 * E;   // [E] the experts' first rows
   const int lane = threadIdx.x % kWave;
   const int wv = threadIdx.x / kWave;
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
+  const int64_t s1 = min(S, s0 + kDispatchChunk);
+  // every round's ids and weights are loaded up front (one memory round
+  // trip for the chunk instead of one per round)
+  constexpr int kRounds = kDispatchChunk / 256;
+  int idv[kRounds];
+  float wvv[kRounds];
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    const int64_t s = s0 + q * 256 + threadIdx.x;
+    idv[q] = s < s1 ? ids[s] : -1;
+    wvv[q] = s < s1 ? w[s] : 0.f;
+  }
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     run[e] = base[static_cast<int64_t>(blockIdx.x) * E + e];
+    offs[e] = offsets[e];
 #pragma unroll
     for (int q = 0; q < 4; ++q) wcnt[q * E + e] = 0;
   }
   __syncthreads();
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kDispatchChunk;
-  const int64_t s1 = min(S, s0 + kDispatchChunk);
-  for (int64_t r0 = s0; r0 < s1; r0 += blockDim.x) {
+#pragma unroll
+  for (int q = 0; q < kRounds; ++q) {
+    const int64_t r0 = s0 + q * 256;
+    if (r0 >= s1) break;
     const int64_t s = r0 + threadIdx.x;
     int e = -1;
     if (s < s1) {
-      const int v = ids[s];
+      const int v = idv[q];
       if (v >= 0 && v < E) e = v;
     }
     const bool valid = e >= 0;
@@ -180,9 +214,9 @@ scatter_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
     if (s < s1) {
       int32_t row = -1;
       if (valid && static_cast<int64_t>(rank) < cap) {
-        row = offsets[e] + rank;
+        row = offs[e] + rank;
         sorted_token[row] = static_cast<int32_t>(s / k);
-        sorted_w[row] = w[s];
+        sorted_w[row] = wvv[q];
       }
       slot_row[s] = row;
     }
@@ -329,7 +363,7 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, hist,
                      nblocks, D.E, D.slots, D.cap, counts, offsets, dropped,
                      tiles1, routed_bm(D), tiles2, routed_bm(D));
-  hipLaunchKernelGGL(scatter_kernel, dim3(nblocks), dim3(256), 5 * hsz, s, ids,
+  hipLaunchKernelGGL(scatter_kernel, dim3(nblocks), dim3(256), 6 * hsz, s, ids,
                      w, D.slots, D.k, D.E, D.cap, nbits, hist, offsets,
                      sorted_token, sorted_w, slot_row);
   return hipGetLastError();

@@ -136,7 +136,9 @@ WsLayout layout_of(const Dims& D) {
   WsLayout L{};
   const size_t es = D.bf16 ? 2 : 4;
   const size_t T = static_cast<size_t>(D.T), E = D.E, S = D.slots;
-  L.route_blocks = static_cast<int>(std::min<int64_t>((D.T + kSelectWaves - 1) / kSelectWaves, 1024));
+  // one wave per token in flight: a token's selection is a chain of dependent
+  // wave reductions, so throughput comes from many tokens at once
+  L.route_blocks = static_cast<int>(std::min<int64_t>((D.T + kSelectWaves - 1) / kSelectWaves, 8192));
   if (L.route_blocks < 1) L.route_blocks = 1;
   L.dispatch_blocks = static_cast<int>((D.slots + kDispatchChunk - 1) / kDispatchChunk);
   if (L.dispatch_blocks < 1) L.dispatch_blocks = 1;

@@ -525,8 +525,17 @@ __global__ void prob_finalize_kernel(const float* __restrict__ part, int nb,
                                      int E, float* __restrict__ out) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= E) return;
+  // rows added in row order; each group of 16 loaded before it is added
   float s = 0.f;
-  for (int b = 0; b < nb; ++b) s += part[static_cast<int64_t>(b) * E + e];
+  for (int b0 = 0; b0 < nb; b0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      v[j] = b0 + j < nb ? part[static_cast<int64_t>(b0 + j) * E + e] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (b0 + j < nb) s += v[j];
+  }
   out[e] = s;
 }
 
