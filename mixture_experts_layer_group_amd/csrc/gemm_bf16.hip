@@ -28,16 +28,19 @@
 //     consecutive output columns of one row;
 //   * both operands are K-contiguous in HBM (weights are [out, in]) and go
 //     straight from HBM to LDS (buffer_load_dwordx4 ... lds, no staging
-//     registers) into a ring of 2 or 3 stages (as many as fit 160 KiB).  The
-//     loads of a later step start right after the barrier that ends the
-//     step whose stage they reuse, so the memory pipe is busy across the
-//     barrier.  The 16-byte chunks of each 128-byte LDS row are
+//     registers) into LDS stages: three of each operand where they fit
+//     160 KiB, else (256-row bf16 tiles) two activation and three weight
+//     stages, so the weights run two K steps ahead.  The loads of a later
+//     step start right after the barrier that ends the step whose stage
+//     they reuse, so the memory pipe is busy across the barrier.  The 16-byte chunks of each 128-byte LDS row are
 //     XOR-swizzled (conflict-free for 8- and 16-lane LDS phases); the
 //     swizzle is applied on the global side, since a direct load writes LDS
 //     at lane*16;
 //   * activation rows are gathered on load through sorted_token (no
 //     permuted copy of x); rows past the end of a group are given an
-//     out-of-range offset, so a ragged tile fetches only its real rows;
+//     out-of-range offset, so a ragged tile fetches only its real rows,
+//     and a wave's K loop is compiled per number of its 32-row blocks
+//     that hold rows (empty blocks get no fragment reads and no products);
 //   * SwiGLU: a tile's 256 weight rows are 128 gate rows then the same 128
 //     up rows; each wave holds gate and up accumulators of the same
 //     (row, column) in the same lanes, so the epilogue fuses silu(g) * u;
@@ -202,10 +205,6 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, float sc, float bi, uint32
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-// Sizes of one kernel variant: BMT-row tiles, bf16 or 4-bit weights.  The
-// LDS ring has three stages where they fit the 160 KiB of LDS (128-row
-// tiles, 4-bit weights), so two K steps of loads are in flight during a
-// step's products; two for 256-row tiles of bf16 weights.
 // Which tile a workgroup computes.  The grid is an upper bound on the tile
 // count (ragged groups, no host sync): a workgroup reads the per-expert
 // M-tile prefix that the dispatch wrote and returns false if surplus.
@@ -259,6 +258,8 @@ __device__ __forceinline__ bool schedule_tile(const GemmArgs& g, int bm, TileSch
 // kernel's host-side launch stub
 constexpr int kMaxMB = 4, kMaxLoadsA = 4;
 
+// Sizes of one kernel variant: BMT-row tiles, bf16 or 4-bit weights, and
+// its LDS stages.
 template <int BMT, bool U4>
 struct TileCfg {
   static constexpr int BM = BMT;                          // tile rows (activation rows)
