@@ -69,6 +69,16 @@ TRAFFIC_SOURCES = {"bf16": ("csrc/gemm_bf16.hip",), "u4": ("csrc/gemm_u4.hip",)}
 COPY_BYTES = 1 << 30  # calibration kernel: reads and writes 1 GiB
 # counters are collected for the calibration copy and the expert kernels only
 TRAFFIC_REGEX = "neg_kernel|grouped_gemm|u4s_kernel"
+# the router, dispatch and combine kernels (their HBM traffic, summarised
+# with --side)
+SIDE_KERNELS = ("logits_", "select_kernel", "count_kernel", "scan_kernel", "scatter_kernel",
+                "dispatch_small_kernel", "combine_kernel")
+SIDE_REGEX = "neg_kernel|" + "|".join(SIDE_KERNELS)
+SIDE_SOURCES = ("csrc/router.hip", "csrc/dispatch.hip", "csrc/combine.hip")
+# matrix-core counters of the bf16 expert GEMMs (one rocprofv3 pass)
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                 "SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE")
+SIMDS = 4 * 256  # MI355X: 256 CUs of 4 SIMDs
 
 
 def sources_digest(weight_dtype: str = "bf16") -> str:
@@ -79,8 +89,18 @@ def sources_digest(weight_dtype: str = "bf16") -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_summary_path(workload: str) -> str:
+def traffic_summary_path(workload: str, side: bool = False) -> str:
+    if side:
+        return os.path.join(ROOT, "profiles", f"side_kernels_{workload}_hbm_traffic.md")
     return os.path.join(ROOT, "profiles", f"expert_gemms_{workload}_hbm_traffic.md")
+
+
+def side_sources_digest() -> str:
+    h = hashlib.sha256()
+    for rel in SIDE_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_layer_group_amd", rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, kernel: str):
@@ -341,9 +361,16 @@ def main() -> int:
                     help="run a 1 GiB copy and three layer calls, for rocprofv3 --pmc")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two --pmc runs of --traffic-probe into the profiles/ summary")
+    ap.add_argument("--side", action="store_true",
+                    help="with --summarize-traffic: the router, dispatch and combine kernels")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="turn a --pmc run of --traffic-probe with the matrix-core counters "
+                         "into the profiles/ summary")
     args = ap.parse_args()
     if args.summarize_traffic:
         return summarize_traffic(args)
+    if args.summarize_mfma:
+        return summarize_mfma(args)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
@@ -490,6 +517,8 @@ def summarize_traffic(args) -> int:
     it."""
     import synth
     cfg = synth.CONFIGS[args.config]
+    kernels_of_interest = SIDE_KERNELS if args.side else FFN_KERNELS
+    regex = SIDE_REGEX if args.side else TRAFFIC_REGEX
     res = {}
     for counter, d in (("FETCH_SIZE", args.summarize_traffic[0]),
                        ("WRITE_SIZE", args.summarize_traffic[1])):
@@ -504,32 +533,34 @@ def summarize_traffic(args) -> int:
             if last_copy is None or int(r["Dispatch_Id"]) <= last_copy:
                 continue
             name = r["Kernel_Name"]
-            for k in FFN_KERNELS:
+            for k in kernels_of_interest:
                 if k in name:
                     key = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
                     ffn.setdefault(key, []).append(float(r["Counter_Value"]))
         if not copy_kib or not ffn:
-            print(f"no calibration or expert-kernel dispatches for {counter} in {d}",
+            print(f"no calibration or kernel dispatches for {counter} in {d}",
                   file=sys.stderr)
             return 1
         factor = COPY_BYTES / (sum(copy_kib) / len(copy_kib) * 1024.0)
         # per layer call: every kernel's dispatches over the 3 calls
         per_kernel = {k: sum(vs) / 3 * 1024.0 * factor for k, vs in ffn.items()}
         res[counter] = {"factor": factor, "copy_kib": copy_kib, "per_kernel": per_kernel}
-    path = traffic_summary_path(cfg.name)
+    path = traffic_summary_path(cfg.name, args.side)
     rel = os.path.relpath(path, ROOT)
     kernels = sorted(set(res["FETCH_SIZE"]["per_kernel"]) | set(res["WRITE_SIZE"]["per_kernel"]))
     with open(path, "w") as f:
-        f.write(f"# HBM traffic of the expert kernels per layer call, {cfg.name}\n\n")
+        what = "router, dispatch and combine kernels" if args.side else "expert kernels"
+        f.write(f"# HBM traffic of the {what} per layer call, {cfg.name}\n\n")
         f.write("Commands (repository root, one MI355X; the probe runs a 1 GiB elementwise "
                 "negation for calibration, then three layer calls):\n\n```\n")
         f.write("cd /tmp && export TMPDIR=/tmp\n")
         for c, dd in (("FETCH_SIZE", "pmc_fetch"), ("WRITE_SIZE", "pmc_write")):
-            f.write(f"timeout -s KILL 120 rocprofv3 --kernel-include-regex '{TRAFFIC_REGEX}' "
+            f.write(f"timeout -s KILL 120 rocprofv3 --kernel-include-regex '{regex}' "
                     f"--pmc {c} --output-format csv -d $REPO/gpurun_out/{dd} "
                     f"-o p -- python3 $REPO/bench.py --config {cfg.cfg_id} --traffic-probe\n")
         f.write(f"python3 $REPO/bench.py --config {cfg.cfg_id} --summarize-traffic "
-                "$REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write\n```\n\n")
+                f"$REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write"
+                f"{' --side' if args.side else ''}\n```\n\n")
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             r = res[c]
             f.write(f"{c}: calibration read {sum(r['copy_kib']) / len(r['copy_kib']):.0f} KiB "
@@ -543,10 +574,66 @@ def summarize_traffic(args) -> int:
             tot = res["FETCH_SIZE"]["per_kernel"].get(k, 0.0) + \
                 res["WRITE_SIZE"]["per_kernel"].get(k, 0.0)
             f.write(f"- per_call[{k}]: {tot:.6g}\n")
-        f.write(f"- sources_sha256: {sources_digest(cfg.weight_dtype)}\n")
+        f.write(f"- sources_sha256: "
+                f"{side_sources_digest() if args.side else sources_digest(cfg.weight_dtype)}\n")
     total = sum(res["FETCH_SIZE"]["per_kernel"].values()) + \
         sum(res["WRITE_SIZE"]["per_kernel"].values())
     print(f"wrote {rel}: {total / 1e9:.3f} GB per layer call", flush=True)
+    return 0
+
+
+def summarize_mfma(args) -> int:
+    """profiles/ summary of the bf16 expert GEMMs' matrix-core counters per
+    layer call: MFMA busy cycles over the GPU's busy cycles and SIMDs (the
+    definition of rocprofv3's MfmaUtil, with the XCDs' mean busy cycles),
+    the MFMA operations counted (bf16 and fp16, 512 per unit), and the
+    shader clock the busy-cycle count implies over the dispatch's
+    duration."""
+    import synth
+    cfg = synth.CONFIGS[args.config]
+    rows = _counter_rows(args.summarize_mfma)
+    copies = [r for r in rows if "neg_kernel" in r["Kernel_Name"]]
+    last_copy = max((int(r["Dispatch_Id"]) for r in copies), default=-1)
+    per = {}  # kernel -> dispatch -> {counter: value, "ns": duration}
+    for r in rows:
+        if int(r["Dispatch_Id"]) <= last_copy or "grouped_gemm" not in r["Kernel_Name"]:
+            continue
+        key = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        dd = per.setdefault(key, {}).setdefault(int(r["Dispatch_Id"]), {})
+        dd[r["Counter_Name"]] = float(r["Counter_Value"])
+        dd["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    if not per:
+        print(f"no grouped-GEMM dispatches in {args.summarize_mfma}", file=sys.stderr)
+        return 1
+    path = os.path.join(ROOT, "profiles", f"expert_gemms_{cfg.name}_mfma_counters.md")
+    with open(path, "w") as f:
+        f.write(f"# Matrix-core counters of the bf16 expert GEMMs, {cfg.name}\n\n")
+        f.write("Commands (repository root, one MI355X; three layer calls after a calibration "
+                "copy):\n\n```\ncd /tmp && export TMPDIR=/tmp\n")
+        f.write(f"timeout -s KILL 120 rocprofv3 --kernel-trace --kernel-include-regex "
+                f"'neg_kernel|grouped_gemm' --pmc {MFMA_COUNTERS} --output-format csv "
+                f"-d $REPO/gpurun_out/pmc_mfma -o p -- python3 $REPO/bench.py --config "
+                f"{cfg.cfg_id} --traffic-probe\n")
+        f.write(f"python3 $REPO/bench.py --config {cfg.cfg_id} --summarize-mfma "
+                "$REPO/gpurun_out/pmc_mfma\n```\n\n")
+        f.write("MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+                "MFMA FLOPs = 512 x SQ_INSTS_VALU_MFMA_MOPS_*; the clock is GRBM_GUI_ACTIVE "
+                "summed over the 8 XCDs, / 8, over the dispatch's duration (under counter "
+                "collection).\n\n")
+        f.write("| kernel | dispatches | µs per dispatch | MFMA busy | MFMA TFLOP per dispatch "
+                "(bf16 / fp16) | TFLOP/s by counters | implied clock (GHz) |\n|---|---|---|---|---|---|---|\n")
+        for k in sorted(per):
+            ds = list(per[k].values())
+            ns = sum(d["ns"] for d in ds) / len(ds)
+            util = sum(100.0 * d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) /
+                       max(1.0, d.get("GRBM_GUI_ACTIVE", 0.0) / 8 * SIMDS) for d in ds) / len(ds)
+            fb = sum(d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for d in ds) / len(ds) * 512
+            fh = sum(d.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) for d in ds) / len(ds) * 512
+            gui = sum(d.get("GRBM_GUI_ACTIVE", 0.0) for d in ds) / len(ds)
+            f.write(f"| `{k}` | {len(ds)} | {ns / 1e3:.1f} | {util:.1f}% | {fb / 1e12:.3f} / "
+                    f"{fh / 1e12:.3f} | {(fb + fh) / ns / 1e3:.0f} | {gui / 8 / ns:.2f} |\n")
+        f.write(f"\n- sources_sha256: {sources_digest('bf16')}\n")
+    print(f"wrote {os.path.relpath(path, ROOT)}", flush=True)
     return 0
 
 
