@@ -75,6 +75,11 @@ SIDE_KERNELS = ("logits_", "select_kernel", "count_kernel", "scan_kernel", "scat
                 "dispatch_small_kernel", "combine_kernel")
 SIDE_REGEX = "neg_kernel|" + "|".join(SIDE_KERNELS)
 SIDE_SOURCES = ("csrc/router.hip", "csrc/dispatch.hip", "csrc/combine.hip")
+# kernel-name fragments of the dominant kernels in the profiler's summaries:
+# the routed bf16 gate/up GEMM (SwiGLU mode, gathered rows; any tile size)
+# and the 4-bit weight-stream kernels
+GATE_UP_KEY = "grouped_gemm_kernel<0, true,"
+U4_STREAM_KEY = "u4s_kernel"
 # matrix-core counters of the bf16 expert GEMMs (one rocprofv3 pass)
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
                  "SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE")
@@ -451,7 +456,7 @@ def main() -> int:
                      "frac": up_tflops / PEAK_BF16_TFLOPS,
                      "flops_per_launch": up_flops, "avg_launch_ms": up_ms,
                      "median_launch_ms": _median(r["up"]), "min_launch_ms": min(r["up"]),
-                     "traffic": measured_traffic(cfg.name, "grouped_gemm_kernel<0, true>")},
+                     "traffic": measured_traffic(cfg.name, GATE_UP_KEY)},
     }
     if u4:
         def ffn_bytes(j):
@@ -465,7 +470,7 @@ def main() -> int:
                            "frac": gbs / PEAK_HBM_GBS, "bytes_per_launch": byts,
                            "avg_launch_ms": ffn_ms, "median_launch_ms": _median(ffn_times),
                            "min_launch_ms": min(ffn_times),
-                           "traffic": measured_traffic(cfg.name, "u4s_kernel")}
+                           "traffic": measured_traffic(cfg.name, U4_STREAM_KEY)}
         res["touched_experts"] = r["touched"]
         res["input_copies_rotated"] = n_rep
     elif not args.no_decode:
