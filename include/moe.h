@@ -292,7 +292,10 @@ moe_status moe_dispatch(const moe_spec* spec, int64_t T,
 /* Grouped expert FFN over the ragged expert groups (dockyard page,
  * "The pipeline", grouped GEMM; blog page third program's moe_forward):
  * for every expert e and every kept row r in [offsets[e], offsets[e+1]),
- *   y_rows[r] = FFN_e(x[sorted_token[r]])   (unweighted)
+ *   y_rows[r] = FFN_e(x[sorted_token[r]])                (sorted_w NULL)
+ *   y_rows[r] = sorted_w[r] * FFN_e(x[sorted_token[r]])  (otherwise: the
+ *     routing weight applied in the down product's epilogue, after its fp32
+ *     accumulation, instead of in the combine)
  * and for every shared expert s and token t
  *   y_shared[s*T + t] = FFN_shared_s(x[t]).
  * SwiGLU: W_down (silu(W_gate x) * (W_up x)); ReLU: W_down relu(W_gate x).
@@ -309,13 +312,15 @@ moe_status moe_dispatch(const moe_spec* spec, int64_t T,
  *  offsets, sorted_token  device, as produced by moe_dispatch
  *  x         device [T,d] act dtype
  *  weights   host struct of device pointers
+ *  sorted_w  device [T*k] fp32 (moe_dispatch's sorted_w), or NULL
  *  y_rows    device out [T*k, d] fp32 (rows >= offsets[E] untouched)
  *  y_shared  device out [S*T, d] fp32, or NULL when S = 0
  *  errors    device [1] int32 or NULL: MOE_FLAG_H_SATURATED is OR-ed in */
 moe_status moe_grouped_ffn(const moe_spec* spec, int64_t T,
                            const int32_t* offsets, const int32_t* sorted_token,
                            const void* x, const moe_expert_weights* weights,
-                           void* y_rows, void* y_shared, int32_t* errors,
+                           const float* sorted_w, void* y_rows, void* y_shared,
+                           int32_t* errors,
                            void* workspace, size_t ws_bytes,
                            moe_stream_t stream);
 
@@ -326,8 +331,10 @@ moe_status moe_grouped_ffn(const moe_spec* spec, int64_t T,
  *            + sum_s y_shared[s*T + t]
  * accumulated in fp32 in the fixed order i = 0..k-1 then s (no atomics);
  * dropped slots add nothing and the kept weights are not renormalised.
+ * With topk_w NULL each kept row is added unscaled: the rows already carry
+ * their weights (moe_grouped_ffn with sorted_w).
  *  y_rows device [T*k, d] fp32, y_shared device [S*T, d] fp32 or NULL
- *  slot_row device [T,k] int32, topk_w device [T,k] fp32
+ *  slot_row device [T,k] int32, topk_w device [T,k] fp32 or NULL
  *  out device out [T,d] out dtype */
 moe_status moe_combine(const moe_spec* spec, int64_t T, const void* y_rows,
                        const int32_t* slot_row, const float* topk_w,

@@ -107,7 +107,7 @@ def library() -> ctypes.CDLL:
                                      vp, vp, sz, vp]
         lib.moe_grouped_ffn.argtypes = [sp, i64, vp, vp, vp,
                                         ctypes.POINTER(MoEExpertWeights), vp, vp, vp, vp,
-                                        sz, vp]
+                                        vp, sz, vp]
         lib.moe_combine.argtypes = [sp, i64, vp, vp, vp, vp, vp, vp]
         lib.moe_layer_forward.argtypes = [sp, i64, vp, vp, vp,
                                           ctypes.POINTER(MoEExpertWeights), vp,
@@ -266,12 +266,15 @@ def moe_dispatch(spec, T, topk_ids, topk_w, counts_pre, offsets, sorted_token,
 
 def moe_grouped_ffn(spec, T, offsets, sorted_token, x, weights, y_rows,
                     y_shared=None, workspace=None, ws_bytes=None, stream=None,
-                    errors=None) -> None:
+                    errors=None, sorted_w=None) -> None:
+    """sorted_w (moe_dispatch's [T*k] fp32, or None): when given, each routed
+    row comes out multiplied by its routing weight (then combine with
+    topk_w=None)."""
     w = weights if isinstance(weights, MoEExpertWeights) else expert_weights(weights)
     ws_bytes = ws_bytes if ws_bytes is not None else (workspace.numel() if workspace is not None else 0)
     _check(library().moe_grouped_ffn(ctypes.byref(spec), T, _ptr(offsets),
                                      _ptr(sorted_token), _ptr(x), ctypes.byref(w),
-                                     _ptr(y_rows), _ptr(y_shared), _ptr(errors),
+                                     _ptr(sorted_w), _ptr(y_rows), _ptr(y_shared), _ptr(errors),
                                      _ptr(workspace), ws_bytes, _stream(stream)),
            "moe_grouped_ffn")
 

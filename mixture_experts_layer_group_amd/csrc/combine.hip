@@ -1,5 +1,6 @@
 // Combine: the routed expert outputs go back to token order, each scaled by
-// its routing weight, summed with the always-on shared experts (dockyard_rl
+// its routing weight (unless the expert rows already carry it), summed with
+// the always-on shared experts (dockyard_rl
 // "Mixture-of-Experts" page, "The pipeline", combine; "Mixture of Experts"
 // blog page, the third program's scatter-add, where a token routed to k
 // experts collects k contributions; "Mixture-of-Experts Documentation",
@@ -49,7 +50,8 @@ combine_kernel(const float* __restrict__ y, const float* __restrict__ ypart,
   const int64_t t = blockIdx.x;
   if (threadIdx.x < k) {
     rows[threadIdx.x] = slot_row[t * k + threadIdx.x];
-    wts[threadIdx.x] = topk_w[t * k + threadIdx.x];
+    // no weights: the rows already carry them (moe_grouped_ffn with sorted_w)
+    wts[threadIdx.x] = topk_w != nullptr ? topk_w[t * k + threadIdx.x] : 1.f;
   }
   __syncthreads();
   for (int c = threadIdx.x * 8; c < d; c += blockDim.x * 8) {

@@ -106,6 +106,7 @@ struct GemmArgs {
   int ldo;                      // output row length (F or d)
   int NT;                       // N tiles
   int32_t* err;                 // MOE_FLAG_H_SATURATED is OR-ed in (or nullptr)
+  const float* row_scale;       // down: factor of each output row (nullptr: 1)
   // 4-bit affine weights (U4 kernels): packed codes [N][K/8] uint32 and bf16
   // scales / biases [N][K/64] of expert 0 (gate / in / down, and up)
   const uint8_t* q0;
@@ -702,6 +703,9 @@ grouped_gemm_kernel(GemmArgs g) {
     const int64_t orow_off = static_cast<int64_t>(row0 + m) * g.ldo;
     uint16_t* orow = static_cast<uint16_t*>(g.out) + orow_off;
     float* orow_f = (split ? g.part : static_cast<float*>(g.out)) + orow_off;
+    // the routing weight of the row, when the caller asks for weighted rows
+    // (each K split is scaled; the splits add up to the scaled row)
+    const float rsc = MODE == kDown && g.row_scale != nullptr ? g.row_scale[row0 + m] : 1.f;
     if (MODE == kSwiGLU) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -724,9 +728,15 @@ grouped_gemm_kernel(GemmArgs g) {
           const int col = nt * BN + wn * 64 + nb * 32 + 8 * q + 4 * fh;
           if (col >= g.N) continue;
           if (MODE == kDown) {
-            *reinterpret_cast<float4*>(orow_f + col) =
-                make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
-                            acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
+            float4 o = make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
+                                   acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
+            if (g.row_scale != nullptr) {
+              o.x *= rsc;
+              o.y *= rsc;
+              o.z *= rsc;
+              o.w *= rsc;
+            }
+            *reinterpret_cast<float4*>(orow_f + col) = o;
           } else {
             float h[4];
 #pragma unroll
@@ -896,8 +906,8 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
 hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
                            const int32_t* tiles1, const int32_t* tiles2,
                            const int32_t* sorted_token, const void* x,
-                           const moe_expert_weights& w, void* H, void* Hs,
-                           void* Y, float* Ypart, void* Ys, int32_t* err,
+                           const moe_expert_weights& w, const float* row_scale, void* H,
+                           void* Hs, void* Y, float* Ypart, void* Ys, int32_t* err,
                            hipEvent_t mid, hipStream_t s) {
   const int up_mode = D.swiglu ? kSwiGLU : kReLU;
   // kept rows are at most min(T*k, E*capacity); cap is already <= T*k
@@ -946,6 +956,7 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
     g.NT = ntiles(kDown, D.d);
     g.ksplit = down_splits(D);
     g.part = Ypart;
+    g.row_scale = row_scale;
     if (g.ksplit > 1 && Ypart == nullptr) return hipErrorInvalidValue;
     hipError_t e = launch_one(kDown, false, g, nmax, routed_bm(D), s);
     if (e != hipSuccess) return e;
@@ -956,8 +967,9 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
 
 hipError_t launch_ffn_u4_tiled(const Dims& D, const int32_t* offsets, const int32_t* tiles1,
                                const int32_t* tiles2, const int32_t* sorted_token,
-                               const void* x, void* X16, const moe_expert_weights& w, void* H,
-                               void* Y, int32_t* err, hipEvent_t mid, hipStream_t s) {
+                               const void* x, void* X16, const moe_expert_weights& w,
+                               const float* row_scale, void* H, void* Y, int32_t* err,
+                               hipEvent_t mid, hipStream_t s) {
   const int up_mode = D.swiglu ? kSwiGLU : kReLU;
   const int64_t nmax = std::min<int64_t>(D.slots, D.cap * D.E);
   // one (scale, bias) per 64 weights of a row, an even number per row
@@ -1018,6 +1030,7 @@ hipError_t launch_ffn_u4_tiled(const Dims& D, const int32_t* offsets, const int3
   g.N = D.d;
   g.K = D.F;
   g.out = Y;
+  g.row_scale = row_scale;
   g.ldo = D.d;
   g.NT = ntiles(kDown, D.d);
   g.ksplit = 1;

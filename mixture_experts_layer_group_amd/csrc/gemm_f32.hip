@@ -57,27 +57,28 @@ f32_up_kernel(const int32_t* __restrict__ offsets, int E,
   H[r * F + n] = h;
 }
 
-// Y[r, m] = H[r] . Wd[e][m]
+// Y[r, m] = H[r] . Wd[e][m]  (times row_scale[r] when it is given)
 __global__ void __launch_bounds__(256)
 f32_down_kernel(const int32_t* __restrict__ offsets, int E,
                 const float* __restrict__ H, const float* __restrict__ wd,
-                float* __restrict__ Y, int64_t rows_max, int d, int F,
-                int identity) {
+                const float* __restrict__ row_scale, float* __restrict__ Y,
+                int64_t rows_max, int d, int F, int identity) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t total = identity ? rows_max : offsets[E];
   if (idx >= total * d) return;
   const int64_t r = idx / d;
   const int m = static_cast<int>(idx % d);
   const int e = identity ? 0 : find_group(offsets, E, static_cast<int32_t>(r));
-  Y[r * d + m] = dot(H + r * F, wd + (static_cast<int64_t>(e) * d + m) * F, F);
+  const float y = dot(H + r * F, wd + (static_cast<int64_t>(e) * d + m) * F, F);
+  Y[r * d + m] = row_scale != nullptr ? y * row_scale[r] : y;
 }
 
 }  // namespace
 
 hipError_t launch_ffn_f32(const Dims& D, const int32_t* offsets,
                           const int32_t* sorted_token, const void* x,
-                          const moe_expert_weights& w, void* H, void* Hs,
-                          void* Y, void* Ys, hipEvent_t mid, hipStream_t s) {
+                          const moe_expert_weights& w, const float* row_scale, void* H,
+                          void* Hs, void* Y, void* Ys, hipEvent_t mid, hipStream_t s) {
   const float* xf = static_cast<const float*>(x);
   // FUSED_GATE_UP: each expert's [F][d] gate rows, then its up rows
   const int64_t mat = static_cast<int64_t>(D.F) * D.d;
@@ -96,7 +97,7 @@ hipError_t launch_ffn_f32(const Dims& D, const int32_t* offsets,
     const int64_t m = D.slots * D.d;
     hipLaunchKernelGGL(f32_down_kernel, dim3(static_cast<unsigned>((m + 255) / 256)),
                        dim3(256), 0, s, offsets, D.E, static_cast<const float*>(H),
-                       static_cast<const float*>(w.down), static_cast<float*>(Y),
+                       static_cast<const float*>(w.down), row_scale, static_cast<float*>(Y),
                        D.slots, D.d, D.F, 0);
   }
   for (int sh = 0; sh < D.S; ++sh) {
@@ -114,7 +115,7 @@ hipError_t launch_ffn_f32(const Dims& D, const int32_t* offsets,
     const int64_t m = D.T * D.d;
     hipLaunchKernelGGL(f32_down_kernel, dim3(static_cast<unsigned>((m + 255) / 256)),
                        dim3(256), 0, s, offsets, 1, static_cast<const float*>(Hs),
-                       static_cast<const float*>(w.shared_down) + so,
+                       static_cast<const float*>(w.shared_down) + so, nullptr,
                        static_cast<float*>(Ys) + static_cast<int64_t>(sh) * D.T * D.d,
                        D.T, D.d, D.Fs, 1);
   }

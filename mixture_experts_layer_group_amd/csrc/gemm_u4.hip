@@ -295,6 +295,7 @@ struct U4Args {
   int N;                        // units (output columns) per expert
   int rstride;                  // rows from one expert's matrix to the next
   int32_t* err;                 // MOE_FLAG_H_SATURATED is OR-ed in (or nullptr)
+  const float* row_scale;       // down: factor of each output row (nullptr: 1)
 };
 
 // exclusive prefix over the lanes of a wave, and the wave total: an
@@ -317,7 +318,9 @@ __device__ __forceinline__ int wave_prefix(int v, int lane, int& total) {
   return inc - v;
 }
 
-template <bool PAIR, int K>
+// WEIGHTED (down product only): each output row is multiplied by
+// g.row_scale[row]
+template <bool PAIR, int K, bool WEIGHTED>
 __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
   using SL = SCfg<PAIR, K>;
   using KC = KCfg<K>;
@@ -517,6 +520,7 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
   const uint32_t m_lo = opaque_vgpr(0x000F000Fu), m_hi = opaque_vgpr(0x00F000F0u);
   half4_t xa[KC::WPL], xb[KC::WPL];
   float xs[KC::GPL], xc[KC::GPL];
+  float row_f = 1.f;  // the factor of this lane's output row (down product)
   auto load_rows = [&](int row0, int rows) {
     // a lane past the chunk's rows reads the chunk's first row and keeps
     // zeros, so no branch divides the wave here
@@ -525,6 +529,7 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
     const int64_t src = g.sorted_token ? static_cast<int64_t>(g.sorted_token[kr])
                                        : static_cast<int64_t>(kr);
     const uint16_t* p = g.a + src * K + ks * KC::KB;
+    if constexpr (WEIGHTED) row_f = g.row_scale[kr];
     const half4_t zero = half4_t{0, 0, 0, 0};
 #pragma unroll
     for (int gg = 0; gg < KC::GPL; ++gg) {
@@ -654,7 +659,7 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
         h = fminf(fmaxf(h, -65504.f), 65504.f);
         static_cast<_Float16*>(g.out)[o] = static_cast<_Float16>(h);
       } else {  // expert output, fp32
-        static_cast<float*>(g.out)[o] = gv;
+        static_cast<float*>(g.out)[o] = WEIGHTED ? gv * row_f : gv;
       }
     }
   };
@@ -704,7 +709,14 @@ __device__ __forceinline__ void u4_stream(const U4Args& g, uint8_t* smem) {
   __global__ void __launch_bounds__((SCfg<P, K>::kThreads))                   \
       u4s_kernel_##P##_##K(U4Args g) {                                        \
     __shared__ __attribute__((aligned(16))) uint8_t smem[SCfg<P, K>::kLds];   \
-    u4_stream<P, K>(g, smem);                                                 \
+    u4_stream<P, K, false>(g, smem);                                          \
+  }
+// the down product with weighted rows
+#define MOE_U4W_KERNEL(K)                                                       \
+  __global__ void __launch_bounds__((SCfg<false, K>::kThreads))               \
+      u4s_kernel_weighted_##K(U4Args g) {                                     \
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SCfg<false, K>::kLds]; \
+    u4_stream<false, K, true>(g, smem);                                       \
   }
 MOE_U4S_KERNEL(true, 2048)
 MOE_U4S_KERNEL(true, 1024)
@@ -718,6 +730,13 @@ MOE_U4S_KERNEL(false, 512)
 MOE_U4S_KERNEL(false, 256)
 MOE_U4S_KERNEL(false, 128)
 MOE_U4S_KERNEL(false, 64)
+MOE_U4W_KERNEL(2048)
+MOE_U4W_KERNEL(1024)
+MOE_U4W_KERNEL(512)
+MOE_U4W_KERNEL(256)
+MOE_U4W_KERNEL(128)
+MOE_U4W_KERNEL(64)
+#undef MOE_U4W_KERNEL
 #undef MOE_U4S_KERNEL
 
 int stream_grid() {
@@ -737,8 +756,9 @@ hipError_t launch_stream(int K, const U4Args& g, hipStream_t s) {
   const dim3 grid(stream_grid()), block(SCfg<PAIR, 64>::kThreads);
 #define MOE_U4S(KK)                                                                    \
   case KK:                                                                             \
-    hipLaunchKernelGGL(PAIR ? u4s_kernel_true_##KK : u4s_kernel_false_##KK, grid, block, \
-                       0, s, g);                                                       \
+    hipLaunchKernelGGL(PAIR ? u4s_kernel_true_##KK                                     \
+                            : (g.row_scale ? u4s_kernel_weighted_##KK : u4s_kernel_false_##KK), \
+                       grid, block, 0, s, g);                                          \
     break;
   switch (K) {
     MOE_U4S(2048)
@@ -772,8 +792,8 @@ bool u4_tiled(const Dims& D) {
 
 hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
                          const int32_t* sorted_token, const void* x,
-                         const moe_expert_weights& w, void* H, void* Y,
-                         int32_t* err, hipEvent_t mid, hipStream_t s) {
+                         const moe_expert_weights& w, const float* row_scale, void* H,
+                         void* Y, int32_t* err, hipEvent_t mid, hipStream_t s) {
   if (!supported_k(D.d) || !supported_k(D.F) || !D.swiglu || group != 64 ||
       D.E > kMaxExperts)
     return hipErrorInvalidValue;
@@ -819,6 +839,7 @@ hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
   h.E = D.E;
   h.N = D.d;
   h.rstride = D.d;
+  h.row_scale = row_scale;
   return launch_stream<false>(D.F, h, s);
 }
 

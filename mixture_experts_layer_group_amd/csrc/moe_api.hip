@@ -241,7 +241,8 @@ moe_status do_route(const moe_spec& sp, const Dims& D, const WsLayout& L,
 // between the routed gate/up and down kernels, and after the last one
 moe_status do_ffn(const moe_spec& sp, const Dims& D, const WsLayout& L,
                   const int32_t* offsets, const int32_t* sorted_token,
-                  const void* x, const moe_expert_weights& w, void* y_rows,
+                  const void* x, const moe_expert_weights& w, const float* row_scale,
+                  void* y_rows,
                   void* y_shared, int32_t* err, void* const* ev, void* ws,
                   bool fused, hipStream_t s) {
   void* H = at<void>(ws, L.H);
@@ -254,16 +255,18 @@ moe_status do_ffn(const moe_spec& sp, const Dims& D, const WsLayout& L,
     if (ev && (e = hipEventRecord(static_cast<hipEvent_t>(ev[0]), s)) != hipSuccess)
       return MOE_ERR_HIP;
     if (!D.bf16) {
-      e = launch_ffn_f32(D, offsets, sorted_token, x, w, H, Hs, y_rows, y_shared, mid, s);
+      e = launch_ffn_f32(D, offsets, sorted_token, x, w, row_scale, H, Hs, y_rows, y_shared,
+                         mid, s);
     } else if (!u4_tiled(D)) {
-      e = launch_ffn_u4(D, sp.quant_group, offsets, sorted_token, x, w, H, y_rows, err,
+      e = launch_ffn_u4(D, sp.quant_group, offsets, sorted_token, x, w, row_scale, H, y_rows, err,
                         mid, s);
     } else {
       int32_t* t1 = at<int32_t>(ws, L.tiles1);
       int32_t* t2 = at<int32_t>(ws, L.tiles2);
       if (!fused) e = launch_tile_prefix(D, offsets, t1, t2, s);
       if (e == hipSuccess)
-        e = launch_ffn_u4_tiled(D, offsets, t1, t2, sorted_token, x, at<void>(ws, L.X16), w, H,
+        e = launch_ffn_u4_tiled(D, offsets, t1, t2, sorted_token, x, at<void>(ws, L.X16), w,
+                                row_scale, H,
                                 y_rows, err, mid, s);
     }
     if (e == hipSuccess && D.bf16 && D.S > 0)
@@ -280,7 +283,7 @@ moe_status do_ffn(const moe_spec& sp, const Dims& D, const WsLayout& L,
   if (ev && (e = hipEventRecord(static_cast<hipEvent_t>(ev[0]), s)) != hipSuccess)
     return MOE_ERR_HIP;
   float* part = down_splits(D) > 1 ? at<float>(ws, L.Ypart) : nullptr;
-  e = launch_ffn_bf16(D, offsets, t1, t2, sorted_token, x, w, H, Hs, y_rows, part,
+  e = launch_ffn_bf16(D, offsets, t1, t2, sorted_token, x, w, row_scale, H, Hs, y_rows, part,
                       y_shared, err, mid, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (ev && (e = hipEventRecord(static_cast<hipEvent_t>(ev[2]), s)) != hipSuccess)
@@ -337,7 +340,7 @@ moe_status layer_forward(const moe_spec* spec, int64_t T, const void* x,
   if (e != hipSuccess) return MOE_ERR_HIP;
   void* Y = at<void>(ws, L.Y);
   void* Ys = at<void>(ws, L.Ys);
-  st = do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, Y, Ys, o.errors,
+  st = do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, nullptr, Y, Ys, o.errors,
               o.ffn_events, ws, mfma_path, s);
   if (st != MOE_OK) return st;
   const float* part = (mfma_path && down_splits(D) > 1) ? at<float>(ws, L.Ypart) : nullptr;
@@ -471,7 +474,7 @@ moe_status moe_dispatch(const moe_spec* spec, int64_t T,
 moe_status moe_grouped_ffn(const moe_spec* spec, int64_t T,
                            const int32_t* offsets, const int32_t* sorted_token,
                            const void* x, const moe_expert_weights* weights,
-                           void* y_rows, void* y_shared, int32_t* errors,
+                           const float* sorted_w, void* y_rows, void* y_shared, int32_t* errors,
                            void* workspace, size_t ws_bytes,
                            moe_stream_t stream) {
   moe_status st = validate(spec, T);
@@ -486,7 +489,7 @@ moe_status moe_grouped_ffn(const moe_spec* spec, int64_t T,
   const Dims D = dims_of(*spec, T);
   const WsLayout L = layout_of(D);
   if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  return do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, y_rows,
+  return do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, sorted_w, y_rows,
                 y_shared, errors, nullptr, workspace, false,
                 static_cast<hipStream_t>(stream));
 }
@@ -497,7 +500,7 @@ moe_status moe_combine(const moe_spec* spec, int64_t T, const void* y_rows,
   moe_status st = validate(spec, T);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
-  if (!y_rows || !slot_row || !topk_w || !out || !aligned16(y_rows) || !aligned16(out))
+  if (!y_rows || !slot_row || !out || !aligned16(y_rows) || !aligned16(out))
     return MOE_ERR_SHAPE;
   if (spec->shared_experts > 0 && (!y_shared || !aligned16(y_shared)))
     return MOE_ERR_SHAPE;

@@ -191,12 +191,15 @@ hipError_t launch_gather_rows(const Dims& D, const int32_t* offsets,
 hipError_t launch_tile_prefix(const Dims& D, const int32_t* offsets,
                               int32_t* tiles1, int32_t* tiles2, hipStream_t s);
 
+// Expert FFN launchers.  row_scale (device [T*k] fp32, or nullptr): each
+// routed expert row r of Y is multiplied by row_scale[r] (its routing
+// weight) as it is written; shared-expert rows never are.
 // gemm_bf16.hip (bf16 activations, bf16 weights, MFMA)
 hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
                            const int32_t* tiles1, const int32_t* tiles2,
                            const int32_t* sorted_token, const void* x,
-                           const moe_expert_weights& w, void* H, void* Hs,
-                           void* Y, float* Ypart, void* Ys, int32_t* err,
+                           const moe_expert_weights& w, const float* row_scale, void* H,
+                           void* Hs, void* Y, float* Ypart, void* Ys, int32_t* err,
                            hipEvent_t mid, hipStream_t s);
 // Y[r] += Ypart[r] for the kept rows (r < offsets[E]): folds the second K
 // split into the expert outputs with the combine's own fp32 addition
@@ -205,21 +208,22 @@ hipError_t launch_fold_split(const Dims& D, const int32_t* offsets, float* Y,
 // gemm_f32.hip (fp32 activations and weights, VALU)
 hipError_t launch_ffn_f32(const Dims& D, const int32_t* offsets,
                           const int32_t* sorted_token, const void* x,
-                          const moe_expert_weights& w, void* H, void* Hs,
-                          void* Y, void* Ys, hipEvent_t mid, hipStream_t s);
+                          const moe_expert_weights& w, const float* row_scale, void* H,
+                          void* Hs, void* Y, void* Ys, hipEvent_t mid, hipStream_t s);
 // gemm_u4.hip (bf16 activations, 4-bit affine routed weights, VALU)
 hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
                          const int32_t* sorted_token, const void* x,
-                         const moe_expert_weights& w, void* H, void* Y,
-                         int32_t* err, hipEvent_t mid, hipStream_t s);
+                         const moe_expert_weights& w, const float* row_scale, void* H,
+                         void* Y, int32_t* err, hipEvent_t mid, hipStream_t s);
 // gemm_bf16.hip: 4-bit routed weights on the tiled matrix-core kernel
 // (dequantised in the K loop), for groups of many rows; d and F multiples of
 // 128; tiles1 / tiles2 as for launch_ffn_bf16; X16: workspace [T][d] for
 // the fp16 copy of x both products are formed from
 hipError_t launch_ffn_u4_tiled(const Dims& D, const int32_t* offsets, const int32_t* tiles1,
                                const int32_t* tiles2, const int32_t* sorted_token,
-                               const void* x, void* X16, const moe_expert_weights& w, void* H,
-                               void* Y, int32_t* err, hipEvent_t mid, hipStream_t s);
+                               const void* x, void* X16, const moe_expert_weights& w,
+                               const float* row_scale, void* H, void* Y, int32_t* err,
+                               hipEvent_t mid, hipStream_t s);
 // whether a 4-bit layer runs the tiled kernels (true) or the weight-stream
 // kernels of gemm_u4.hip (false); depends on the shapes only
 bool u4_tiled(const Dims& D);

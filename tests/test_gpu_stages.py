@@ -209,6 +209,63 @@ def test_stagewise_api_matches_layer(name):
     assert torch.equal(sw[:n].cpu(), tw.reshape(-1)[torch.as_tensor(disp["sorted_slot"])].cpu())
 
 
+@pytest.mark.parametrize("name", ["swiglu-bf16-splitk", "sigmoid-group-shared",
+                                  "f32-swiglu-shared", "u4-decode", "u4-tiled-swiglu-shared"])
+def test_routing_weights_applied_in_the_ffn(name):
+    """moe_grouped_ffn with sorted_w writes each routed row times its routing
+    weight (the down product's epilogue scales the fp32 accumulation; shared
+    rows stay unweighted), and moe_combine with topk_w=NULL adds the rows
+    unscaled: the same layer output up to rounding order, within the oracle's
+    bar.  Covers the bf16 MFMA path (split and unsplit down product), the
+    fp32 path, the 4-bit stream and the 4-bit tiled kernels."""
+    import mixture_experts_layer_group_amd as moe
+    cfg = MEDIUM[name]
+    gu.log(f"[weighted rows] {name}: T={cfg.T} d={cfg.d} E={cfg.E} k={cfg.top_k} F={cfg.F}")
+    inp = gu.make_inputs(cfg)
+    spec = moe.spec_from_config(cfg)
+    T, k, E, d = cfg.T, cfg.top_k, cfg.E, cfg.d
+    dev = "cuda"
+    ws = moe.workspace(spec, T)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    moe.moe_route(spec, T, inp["x"], inp["w_router"], inp["expert_bias"], ids, tw,
+                  None, None, ws)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    st = torch.empty(T * k, dtype=torch.int32, device=dev)
+    sw = torch.empty(T * k, dtype=torch.float32, device=dev)
+    sr = torch.empty((T, k), dtype=torch.int32, device=dev)
+    dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    moe.moe_dispatch(spec, T, ids, tw, counts, offsets, st, sw, sr, dropped, None, None, ws)
+    S = cfg.shared_experts
+    y_u = torch.zeros((T * k, d), dtype=torch.float32, device=dev)
+    y_w = torch.zeros((T * k, d), dtype=torch.float32, device=dev)
+    ysh_u = torch.zeros((max(S, 1) * T, d), dtype=torch.float32, device=dev)
+    ysh_w = torch.zeros((max(S, 1) * T, d), dtype=torch.float32, device=dev)
+    moe.moe_grouped_ffn(spec, T, offsets, st, inp["x"], inp, y_u, ysh_u if S else None, ws)
+    moe.moe_grouped_ffn(spec, T, offsets, st, inp["x"], inp, y_w, ysh_w if S else None, ws,
+                        sorted_w=sw)
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    moe.moe_combine(spec, T, y_w, sr, None, ysh_w if S else None, out)
+    torch.cuda.synchronize()
+    n = int(offsets[-1].item())
+    # the scaled rows: one fp32 rounding of the product (a few when the down
+    # product's K halves are scaled before they are added)
+    ref = y_u[:n] * sw[:n, None]
+    err = (y_w[:n] - ref).abs().max().item()
+    assert err <= 1e-6 * max(ref.abs().max().item(), 1e-30), err
+    if S:
+        assert torch.equal(ysh_w, ysh_u)
+    r = gu.run_layer(cfg, inp)
+    diff = (out - r["out"]).abs().max().item()
+    rms = r["out"].float().pow(2).mean().sqrt().item()
+    gu.log(f"  {n} rows; max|out - layer out| = {diff:.3e} (RMS {rms:.3e})")
+    assert diff <= 1e-5 * rms
+    r2 = dict(r)
+    r2["out"] = out
+    gu.full_check(cfg, inp, r2)
+
+
 def test_determinism_bitwise():
     cfg = MEDIUM["swiglu-bf16-zipf-capacity"]
     inp = gu.make_inputs(cfg)
