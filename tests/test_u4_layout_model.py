@@ -167,3 +167,65 @@ def test_activation_rows_stay_in_their_buffer(K, gather):
                     assert 0 <= a and b <= nrows * K
                     assert a // K == (b - 1) // K  # inside one row
                     assert a % K == ks * C["KB"] and b - a == C["KB"]
+
+
+def stream_split(counts, NBW, W, item_cost=12, rows_max=4):
+    """The 4-bit stream kernel's split of its items over W waves, restated
+    from the kernel: the active experts (count > 0) in expert order with
+    their first chunk p[a] and cost prefix c[a] (NBW * (chunks * item_cost +
+    rows) per expert), and each wave's first item -- the first item whose
+    cost prefix reaches wv * TC / W.  Returns the start items of waves
+    0..W, and for every expert start_item lands in, the row count read from
+    the offsets against the one its cost implies."""
+    act = [(e, c) for e, c in enumerate(counts) if c > 0]
+    p, cst = [0], [0]
+    for _, c in act:
+        ch = -(-c // rows_max)
+        p.append(p[-1] + ch)
+        cst.append(cst[-1] + NBW * (ch * item_cost + c))
+    A, C, TC = len(act), p[-1], cst[-1]
+    derived = {}
+
+    def start(wv):
+        x = wv * TC // W
+        if x >= TC:
+            return C * NBW
+        lo, hi = 0, A - 1
+        while lo < hi:
+            mid = (lo + hi + 1) >> 1
+            if cst[mid] <= x:
+                lo = mid
+            else:
+                hi = mid - 1
+        ch = p[lo + 1] - p[lo]
+        cnt = act[lo][1]  # offsets[e + 1] - offsets[e]
+        derived[lo] = (cst[lo + 1] - cst[lo]) // NBW - ch * item_cost
+        full = NBW * (item_cost + rows_max)
+        y = x - cst[lo]
+        k = min(y // full, ch - 1)
+        rows = min(rows_max, cnt - k * rows_max)
+        rem = y - k * full
+        b = (rem + item_cost + rows - 1) // (item_cost + rows)
+        return (p[lo] + k) * NBW + b
+
+    return [start(w) for w in range(W + 1)], derived, act, C
+
+
+@pytest.mark.parametrize("NBW", [1, 4, 128])
+def test_stream_split_partitions_the_items(NBW):
+    """Over random routing outcomes, the waves' ranges are consecutive and
+    cover every item (chunk, unit block) exactly once, and an expert's cost
+    prefix difference is NBW * (chunks * item_cost + rows)."""
+    import random
+    rnd = random.Random(NBW)
+    for _ in range(40):
+        E = rnd.randint(1, 300)
+        counts = [rnd.choice([0, 0, 1, 1, 2, 3, 4, 5, 9, 30]) for _ in range(E)]
+        if sum(counts) == 0:
+            counts[0] = 1
+        W = rnd.choice([8, 64, 2048])
+        starts, derived, act, C = stream_split(counts, NBW, W)
+        assert starts[0] == 0 and starts[-1] == C * NBW
+        assert all(a <= b for a, b in zip(starts, starts[1:]))
+        for a, cnt in derived.items():
+            assert cnt == act[a][1]
