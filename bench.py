@@ -368,6 +368,9 @@ def main() -> int:
                     help="turn two --pmc runs of --traffic-probe into the profiles/ summary")
     ap.add_argument("--side", action="store_true",
                     help="with --summarize-traffic: the router, dispatch and combine kernels")
+    ap.add_argument("--vendor-compare", action="store_true",
+                    help="time torch.matmul per expert on the workload's kept-row counts "
+                         "against this library's expert kernels; writes profiles/")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
                     help="turn a --pmc run of --traffic-probe with the matrix-core counters "
                          "into the profiles/ summary")
@@ -390,6 +393,8 @@ def main() -> int:
     u4 = cfg.weight_dtype == "u4"
     if args.traffic_probe:
         return traffic_probe(torch, moe, cfg)
+    if args.vendor_compare:
+        return vendor_compare(torch, moe, cfg, args.steps, args.warmup)
     # the 4-bit decode layer touches ~290 MB of weights, about the size of
     # the 256 MB last-level cache: its timed steps rotate through three
     # independently drawn copies of the inputs (1.4 GB) so no step finds the
@@ -479,6 +484,119 @@ def main() -> int:
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
     print(json.dumps(res), flush=True)
+    return 0
+
+
+def vendor_compare(torch, moe, cfg, steps: int, warmup: int) -> int:
+    """The vendor library on the layer's own expert products: torch.matmul
+    (hipBLASLt) once per expert, with the kept-row counts this library's
+    routing gives the workload, on contiguous bf16 rows (no gather, no
+    SwiGLU, no weighting), against this library's routed gate/up and down
+    kernels timed between the layer's events.  Writes
+    profiles/vendor_gemm_<workload>.md.  bf16 weights only."""
+    import synth
+    if cfg.weight_dtype != "bf16" or cfg.act_dtype != "bf16":
+        print("--vendor-compare needs a bf16 workload", file=sys.stderr)
+        return 2
+    r = time_layer(torch, moe, cfg, steps, warmup, 1)
+    # per-expert kept rows of the same inputs
+    spec = moe.spec_from_config(cfg)
+    inp = r["inp"]
+    offs = torch.empty(cfg.E + 1, dtype=torch.int32, device="cuda")
+    out = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    moe.moe_layer_forward(spec, cfg.T, inp["x"], inp["w_router"], inp["expert_bias"], inp,
+                          out, stats=moe.layer_stats(offsets=offs),
+                          workspace=moe.workspace(spec, cfg.T))
+    torch.cuda.synchronize()
+    o = offs.cpu().tolist()
+    cnt = [o[e + 1] - o[e] for e in range(cfg.E)]
+    del inp, out
+    r["inp"] = None
+    torch.cuda.empty_cache()
+    d, F = cfg.d, cfg.F
+    nup = 2 * F if cfg.act == "swiglu" else F
+    g = torch.Generator(device="cuda").manual_seed(7)
+    X = [torch.randn(c, d, device="cuda", dtype=torch.bfloat16, generator=g) for c in cnt if c]
+    H = [torch.randn(c, F, device="cuda", dtype=torch.bfloat16, generator=g) for c in cnt if c]
+    # [N][K] row-major weights as the layer stores them, passed transposed
+    # (a 2-D product: K-contiguous B, no batch)
+    W1 = [torch.randn(nup, d, device="cuda", dtype=torch.bfloat16, generator=g) * 0.02
+          for c in cnt if c]
+    W2 = [torch.randn(d, F, device="cuda", dtype=torch.bfloat16, generator=g) * 0.02
+          for c in cnt if c]
+    rows = sum(cnt)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def up():
+        for x, w in zip(X, W1):
+            torch.matmul(x, w.t())
+
+    def down():
+        for h, w in zip(H, W2):
+            torch.matmul(h, w.t())
+
+    def graphed(fn):
+        # the same per-expert loop captured once and replayed: the GPU time
+        # without the host's per-call launch cost
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            fn()
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            fn()
+        return timed(gr.replay)
+
+    v_up, v_down = timed(up), timed(down)
+    g_up, g_down = graphed(up), graphed(down)
+    ours_up = sum(r["up"]) / len(r["up"])
+    ours_down = sum(r["down"]) / len(r["down"])
+    f_up, f_down = 2.0 * rows * nup * d, 2.0 * rows * d * F
+    lines = [f"# Vendor GEMM against this library's expert kernels, {cfg.name}", "",
+             "Command (repository root, one MI355X):", "", "```",
+             f"python3 bench.py --config {cfg.cfg_id} --vendor-compare --steps {steps} "
+             f"--warmup {warmup}",
+             "```", "",
+             f"Kept rows per expert (this library's routing of the seeded inputs): "
+             f"{min(cnt)}-{max(cnt)}, {rows} in total over {sum(1 for c in cnt if c)} experts.", "",
+             "Vendor: one torch.matmul (hipBLASLt) per expert on contiguous bf16 rows with "
+             "random data of the same shapes, no gather, no activation; this library: the "
+             "routed kernels between the layer's HIP events (gate/up with the gathered rows "
+             "and the SwiGLU / ReLU epilogue; down" +
+             (" plus the shared experts' products" if cfg.shared_experts else "") + ").", "",
+             "The vendor loop is timed as issued from the host and as one captured HIP "
+             "graph (its GPU time without the per-call launch cost).", "",
+             "| product | this library (µs) | TFLOP/s | vendor loop (µs) | TFLOP/s "
+             "| vendor loop in a graph (µs) | TFLOP/s |",
+             "|---|---|---|---|---|---|---|",
+             f"| gate/up | {ours_up * 1e3:.1f} | {f_up / ours_up / 1e9:.0f} | "
+             f"{v_up * 1e3:.1f} | {f_up / v_up / 1e9:.0f} | "
+             f"{g_up * 1e3:.1f} | {f_up / g_up / 1e9:.0f} |",
+             f"| down | {ours_down * 1e3:.1f} | "
+             f"{'-' if cfg.shared_experts else f'{f_down / ours_down / 1e9:.0f}'} | "
+             f"{v_down * 1e3:.1f} | {f_down / v_down / 1e9:.0f} | "
+             f"{g_down * 1e3:.1f} | {f_down / g_down / 1e9:.0f} |", ""]
+    path = os.path.join(ROOT, "profiles", f"vendor_gemm_{cfg.name}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps({"workload": cfg.name, "ours_up_us": ours_up * 1e3,
+                      "vendor_up_us": v_up * 1e3, "vendor_graph_up_us": g_up * 1e3,
+                      "ours_down_us": ours_down * 1e3, "vendor_down_us": v_down * 1e3,
+                      "vendor_graph_down_us": g_down * 1e3}))
+    print(f"wrote {os.path.relpath(path, ROOT)}")
     return 0
 
 
