@@ -38,6 +38,15 @@ MEDIUM = {
     "top1": C("top1", 105, T=333, d=128, E=16, top_k=1, F=128),
     # k = E: every expert on every token
     "k-equals-E": C("k-equals-E", 106, T=100, d=64, E=4, top_k=4, F=64),
+    # the spec's limits: 1024 experts with k = 64 (bf16 and 4-bit weights),
+    # and sigmoid-group routing over 64 groups
+    "limits-e1024-k64": C("limits-e1024-k64", 140, T=33, d=64, E=1024, top_k=64, F=64),
+    "limits-u4-e1024-k64": C("limits-u4-e1024-k64", 141, T=17, d=128, E=1024, top_k=64, F=128,
+                             weight_dtype=synth.U4),
+    "limits-sigmoid-64-groups": C("limits-sigmoid-64-groups", 142, T=50, d=128, E=1024,
+                                  top_k=16, F=64, router=synth.SIGMOID_GROUP,
+                                  routed_scaling=2.5, n_group=64, topk_group=8,
+                                  bias_range=0.05),
     # softmax without renormalisation
     "no-norm": C("no-norm", 107, T=257, d=192, E=8, top_k=2, F=192, norm_topk_prob=False),
     # sigmoid group with every group kept and norm off
