@@ -43,6 +43,8 @@ MEDIUM = {
     "limits-e1024-k64": C("limits-e1024-k64", 140, T=33, d=64, E=1024, top_k=64, F=64),
     "limits-u4-e1024-k64": C("limits-u4-e1024-k64", 141, T=17, d=128, E=1024, top_k=64, F=128,
                              weight_dtype=synth.U4),
+    # capacity max(1, int(3 * 2 / 8 * 1.0)) = 1: one kept row per expert
+    "capacity-one": C("capacity-one", 143, T=3, d=64, E=8, top_k=2, F=64, capacity_factor=1.0),
     "limits-sigmoid-64-groups": C("limits-sigmoid-64-groups", 142, T=50, d=128, E=1024,
                                   top_k=16, F=64, router=synth.SIGMOID_GROUP,
                                   routed_scaling=2.5, n_group=64, topk_group=8,
