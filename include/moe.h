@@ -74,12 +74,18 @@ enum { MOE_LAYOUT_SEPARATE = 0, MOE_LAYOUT_FUSED_GATE_UP = 1 };
  *                            token is then undefined)
  *   MOE_FLAG_X_SATURATED     a 4-bit layer on the tiled kernels met an
  *                            activation outside the fp16 range (or NaN);
- *                            its fp16 copy was stored as +-65504 */
+ *                            its fp16 copy was stored as +-65504
+ *   MOE_FLAG_Y_SATURATED     moe_layer_forward on the matrix-core kernels
+ *                            (bf16 layers, 4-bit layers on the tiled
+ *                            kernels) keeps the expert rows in fp16: an
+ *                            expert output outside the fp16 range (or NaN)
+ *                            was stored as +-65504 */
 enum {
   MOE_FLAG_BAD_EXPERT_ID = 1,
   MOE_FLAG_H_SATURATED = 2,
   MOE_FLAG_NONFINITE_LOGIT = 4,
-  MOE_FLAG_X_SATURATED = 8
+  MOE_FLAG_X_SATURATED = 8,
+  MOE_FLAG_Y_SATURATED = 16
 };
 
 /* Everything the math depends on; the subset of the Edge0 page's MoESpec
@@ -342,7 +348,11 @@ moe_status moe_combine(const moe_spec* spec, int64_t T, const void* y_rows,
 
 /* The whole layer forward (dockyard page, "The pipeline"): moe_route ->
  * moe_dispatch -> moe_grouped_ffn -> moe_combine on one stream, with
- * ragged sizes kept on the device.  Returns the MoE branch only (the
+ * ragged sizes kept on the device.  On the matrix-core kernels (bf16
+ * layers, 4-bit layers on the tiled kernels) the expert rows pass from the
+ * down product to the combine in fp16 (each part of a row rounded once,
+ * saturating at +-65504 with MOE_FLAG_Y_SATURATED); the combine sums in
+ * fp32.  Returns the MoE branch only (the
  * residual add belongs to the caller): a token whose slots were all
  * dropped and which has no shared expert gets exactly 0.
  *  x, w_router, expert_bias  as moe_route

@@ -25,6 +25,7 @@ FLAG_BAD_EXPERT_ID = 1
 FLAG_H_SATURATED = 2
 FLAG_NONFINITE_LOGIT = 4
 FLAG_X_SATURATED = 8
+FLAG_Y_SATURATED = 16
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_INVALID_TOPK",
                 3: "MOE_ERR_CAPACITY_TOO_TIGHT", 4: "MOE_ERR_SHAPE",
                 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_HIP", 7: "MOE_ERR_UNSUPPORTED"}

@@ -20,6 +20,13 @@ __device__ __forceinline__ void load8(const float* p, float* v) {
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
+// 8 fp16 values (one 16-byte load), exactly widened to fp32
+__device__ __forceinline__ void load8(const _Float16* p, float* v) {
+  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+  const h8 a = *reinterpret_cast<const h8*>(p);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = static_cast<float>(a[j]);
+}
 __device__ __forceinline__ void store8(uint16_t* p, const float* v) {
   uint4 a;
   a.x = pack_bf16x2(v[0], v[1]);
@@ -38,10 +45,11 @@ constexpr int kMaxSlots = 64;
 // One block per token of d/8 threads (up to 1024, whole waves): each thread
 // owns 8 consecutive columns, so a row is one pass; the token's kept rows
 // are loaded in groups of 4 before they are added (in slot order).  Expert
-// outputs are fp32, the result is written in the output type.
-template <typename OutT>
+// rows are fp32 or fp16 (YT), the sum is fp32, the result is written in the
+// output type.
+template <typename OutT, typename YT>
 __global__ void __launch_bounds__(1024)
-combine_kernel(const float* __restrict__ y, const float* __restrict__ ypart,
+combine_kernel(const YT* __restrict__ y, const YT* __restrict__ ypart,
                const int32_t* __restrict__ slot_row,
                const float* __restrict__ topk_w, const float* __restrict__ ysh,
                OutT* __restrict__ out, int64_t Tn, int k, int S, int d) {
@@ -116,22 +124,33 @@ hipError_t launch_fold_split(const Dims& D, const int32_t* offsets, float* Y,
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const Dims& D, const void* y_rows, const float* y_part,
+hipError_t launch_combine(const Dims& D, const void* y_rows, const void* y_part, bool y16,
                           const int32_t* slot_row, const float* topk_w,
                           const void* y_shared, void* out, hipStream_t s) {
   if (D.k > kMaxSlots) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(D.T));
   const int threads = std::min(1024, (D.d / 8 + 63) / 64 * 64);  // >= 64 >= k
   const int S = y_shared ? D.S : 0;
-  const float* y = static_cast<const float*>(y_rows);
   const float* ys = static_cast<const float*>(y_shared);
-  if (D.out_bf16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(threads), 0, s, y, y_part,
-                       slot_row, topk_w, ys, static_cast<uint16_t*>(out), D.T,
-                       D.k, S, D.d);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(threads), 0, s, y, y_part, slot_row,
-                       topk_w, ys, static_cast<float*>(out), D.T, D.k, S, D.d);
+  if (y16) {
+    const _Float16* y = static_cast<const _Float16*>(y_rows);
+    const _Float16* yp = static_cast<const _Float16*>(y_part);
+    if (D.out_bf16)
+      hipLaunchKernelGGL((combine_kernel<uint16_t, _Float16>), grid, dim3(threads), 0, s, y, yp,
+                         slot_row, topk_w, ys, static_cast<uint16_t*>(out), D.T, D.k, S, D.d);
+    else
+      hipLaunchKernelGGL((combine_kernel<float, _Float16>), grid, dim3(threads), 0, s, y, yp,
+                         slot_row, topk_w, ys, static_cast<float*>(out), D.T, D.k, S, D.d);
+  } else {
+    const float* y = static_cast<const float*>(y_rows);
+    const float* yp = static_cast<const float*>(y_part);
+    if (D.out_bf16)
+      hipLaunchKernelGGL((combine_kernel<uint16_t, float>), grid, dim3(threads), 0, s, y, yp,
+                         slot_row, topk_w, ys, static_cast<uint16_t*>(out), D.T, D.k, S, D.d);
+    else
+      hipLaunchKernelGGL((combine_kernel<float, float>), grid, dim3(threads), 0, s, y, yp,
+                         slot_row, topk_w, ys, static_cast<float*>(out), D.T, D.k, S, D.d);
+  }
   return hipGetLastError();
 }
 

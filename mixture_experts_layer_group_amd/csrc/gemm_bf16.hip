@@ -107,6 +107,7 @@ struct GemmArgs {
   int NT;                       // N tiles
   int32_t* err;                 // MOE_FLAG_H_SATURATED is OR-ed in (or nullptr)
   const float* row_scale;       // down: factor of each output row (nullptr: 1)
+  bool y16;                     // down: rows (and K-split parts) stored as fp16
   // 4-bit affine weights (U4 kernels): packed codes [N][K/8] uint32 and bf16
   // scales / biases [N][K/64] of expert 0 (gate / in / down, and up)
   const uint8_t* q0;
@@ -736,7 +737,17 @@ grouped_gemm_kernel(GemmArgs g) {
               o.z *= rsc;
               o.w *= rsc;
             }
-            *reinterpret_cast<float4*>(orow_f + col) = o;
+            if (g.y16) {  // fp16 rows inside the layer (saturating, reported)
+              uint16_t* orow_h =
+                  reinterpret_cast<uint16_t*>(split ? static_cast<void*>(g.part) : g.out) +
+                  orow_off;
+              uint2 pk;
+              pk.x = pack_h2(o.x, o.y, sat);
+              pk.y = pack_h2(o.z, o.w, sat);
+              *reinterpret_cast<uint2*>(orow_h + col) = pk;
+            } else {
+              *reinterpret_cast<float4*>(orow_f + col) = o;
+            }
           } else {
             float h[4];
 #pragma unroll
@@ -753,8 +764,8 @@ grouped_gemm_kernel(GemmArgs g) {
       }
     }
   }
-  if (MODE != kDown && g.err != nullptr && __ballot(sat) != 0 && lane == 0)
-    atomicOr(g.err, MOE_FLAG_H_SATURATED);
+  if (g.err != nullptr && __ballot(sat) != 0 && lane == 0)
+    atomicOr(g.err, MODE == kDown ? MOE_FLAG_Y_SATURATED : MOE_FLAG_H_SATURATED);
 }
 
 // bf16 activations -> fp16 for the 4-bit products, 8 per thread: exact
@@ -906,8 +917,8 @@ hipError_t launch_shared_bf16(const Dims& D, const void* x,
 hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
                            const int32_t* tiles1, const int32_t* tiles2,
                            const int32_t* sorted_token, const void* x,
-                           const moe_expert_weights& w, const float* row_scale, void* H,
-                           void* Hs, void* Y, float* Ypart, void* Ys, int32_t* err,
+                           const moe_expert_weights& w, const float* row_scale, bool y16,
+                           void* H, void* Hs, void* Y, float* Ypart, void* Ys, int32_t* err,
                            hipEvent_t mid, hipStream_t s) {
   const int up_mode = D.swiglu ? kSwiGLU : kReLU;
   // kept rows are at most min(T*k, E*capacity); cap is already <= T*k
@@ -957,6 +968,8 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
     g.ksplit = down_splits(D);
     g.part = Ypart;
     g.row_scale = row_scale;
+    g.y16 = y16;
+    g.err = err;
     if (g.ksplit > 1 && Ypart == nullptr) return hipErrorInvalidValue;
     hipError_t e = launch_one(kDown, false, g, nmax, routed_bm(D), s);
     if (e != hipSuccess) return e;
@@ -968,8 +981,8 @@ hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
 hipError_t launch_ffn_u4_tiled(const Dims& D, const int32_t* offsets, const int32_t* tiles1,
                                const int32_t* tiles2, const int32_t* sorted_token,
                                const void* x, void* X16, const moe_expert_weights& w,
-                               const float* row_scale, void* H, void* Y, int32_t* err,
-                               hipEvent_t mid, hipStream_t s) {
+                               const float* row_scale, bool y16, void* H, void* Y,
+                               int32_t* err, hipEvent_t mid, hipStream_t s) {
   const int up_mode = D.swiglu ? kSwiGLU : kReLU;
   const int64_t nmax = std::min<int64_t>(D.slots, D.cap * D.E);
   // one (scale, bias) per 64 weights of a row, an even number per row
@@ -1031,6 +1044,8 @@ hipError_t launch_ffn_u4_tiled(const Dims& D, const int32_t* offsets, const int3
   g.K = D.F;
   g.out = Y;
   g.row_scale = row_scale;
+  g.y16 = y16;
+  g.err = err;
   g.ldo = D.d;
   g.NT = ntiles(kDown, D.d);
   g.ksplit = 1;

@@ -238,13 +238,17 @@ moe_status do_route(const moe_spec& sp, const Dims& D, const WsLayout& L,
 }
 
 // ev (may be null): three events recorded before the first expert kernel,
-// between the routed gate/up and down kernels, and after the last one
+// between the routed gate/up and down kernels, and after the last one.
+// fused: the layer's dispatch wrote the M-tile prefixes; layer: called by
+// the layer, whose combine reads the matrix-core kernels' expert rows in
+// fp16 and adds the down projection's second K split itself (the stage API
+// returns whole fp32 rows)
 moe_status do_ffn(const moe_spec& sp, const Dims& D, const WsLayout& L,
                   const int32_t* offsets, const int32_t* sorted_token,
                   const void* x, const moe_expert_weights& w, const float* row_scale,
                   void* y_rows,
                   void* y_shared, int32_t* err, void* const* ev, void* ws,
-                  bool fused, hipStream_t s) {
+                  bool fused, bool layer, hipStream_t s) {
   void* H = at<void>(ws, L.H);
   void* Hs = at<void>(ws, L.Hs);
   hipEvent_t mid = ev ? static_cast<hipEvent_t>(ev[1]) : nullptr;
@@ -266,7 +270,7 @@ moe_status do_ffn(const moe_spec& sp, const Dims& D, const WsLayout& L,
       if (!fused) e = launch_tile_prefix(D, offsets, t1, t2, s);
       if (e == hipSuccess)
         e = launch_ffn_u4_tiled(D, offsets, t1, t2, sorted_token, x, at<void>(ws, L.X16), w,
-                                row_scale, H,
+                                row_scale, layer, H,
                                 y_rows, err, mid, s);
     }
     if (e == hipSuccess && D.bf16 && D.S > 0)
@@ -283,14 +287,16 @@ moe_status do_ffn(const moe_spec& sp, const Dims& D, const WsLayout& L,
   if (ev && (e = hipEventRecord(static_cast<hipEvent_t>(ev[0]), s)) != hipSuccess)
     return MOE_ERR_HIP;
   float* part = down_splits(D) > 1 ? at<float>(ws, L.Ypart) : nullptr;
-  e = launch_ffn_bf16(D, offsets, t1, t2, sorted_token, x, w, row_scale, H, Hs, y_rows, part,
+  // inside the layer the expert rows go to the combine in fp16
+  e = launch_ffn_bf16(D, offsets, t1, t2, sorted_token, x, w, row_scale, layer, H, Hs, y_rows,
+                      part,
                       y_shared, err, mid, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (ev && (e = hipEventRecord(static_cast<hipEvent_t>(ev[2]), s)) != hipSuccess)
     return MOE_ERR_HIP;
-  // the stage API returns whole expert rows; the fused layer lets the
-  // combine add the second split instead
-  if (part && !fused)
+  // the stage API returns whole expert rows; the layer lets the combine add
+  // the second split instead
+  if (part && !layer)
     return hip_status(launch_fold_split(D, offsets, static_cast<float*>(y_rows), part, s));
   return MOE_OK;
 }
@@ -341,11 +347,12 @@ moe_status layer_forward(const moe_spec* spec, int64_t T, const void* x,
   void* Y = at<void>(ws, L.Y);
   void* Ys = at<void>(ws, L.Ys);
   st = do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, nullptr, Y, Ys, o.errors,
-              o.ffn_events, ws, mfma_path, s);
+              o.ffn_events, ws, mfma_path, true, s);
   if (st != MOE_OK) return st;
-  const float* part = (mfma_path && down_splits(D) > 1) ? at<float>(ws, L.Ypart) : nullptr;
-  return hip_status(launch_combine(D, Y, part, slot_row, tw, D.S > 0 ? Ys : nullptr,
-                                   out, s));
+  const void* part = (mfma_path && down_splits(D) > 1) ? at<void>(ws, L.Ypart) : nullptr;
+  // the matrix-core kernels hand the layer's combine fp16 expert rows
+  return hip_status(launch_combine(D, Y, part, mfma_path, slot_row, tw,
+                                   D.S > 0 ? Ys : nullptr, out, s));
 }
 
 // Scratch of the no-allocation entry point: a file-scope device array, so
@@ -490,7 +497,7 @@ moe_status moe_grouped_ffn(const moe_spec* spec, int64_t T,
   const WsLayout L = layout_of(D);
   if (!workspace || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   return do_ffn(*spec, D, L, offsets, sorted_token, x, *weights, sorted_w, y_rows,
-                y_shared, errors, nullptr, workspace, false,
+                y_shared, errors, nullptr, workspace, false, false,
                 static_cast<hipStream_t>(stream));
 }
 
@@ -505,7 +512,7 @@ moe_status moe_combine(const moe_spec* spec, int64_t T, const void* y_rows,
   if (spec->shared_experts > 0 && (!y_shared || !aligned16(y_shared)))
     return MOE_ERR_SHAPE;
   const Dims D = dims_of(*spec, T);
-  return hip_status(launch_combine(D, y_rows, nullptr, slot_row, topk_w,
+  return hip_status(launch_combine(D, y_rows, nullptr, false, slot_row, topk_w,
                                    spec->shared_experts > 0 ? y_shared : nullptr,
                                    out, static_cast<hipStream_t>(stream)));
 }

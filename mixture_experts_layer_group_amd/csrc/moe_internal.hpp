@@ -193,13 +193,15 @@ hipError_t launch_tile_prefix(const Dims& D, const int32_t* offsets,
 
 // Expert FFN launchers.  row_scale (device [T*k] fp32, or nullptr): each
 // routed expert row r of Y is multiplied by row_scale[r] (its routing
-// weight) as it is written; shared-expert rows never are.
+// weight) as it is written; shared-expert rows never are.  y16: the routed
+// rows (and the down projection's second K split) are written as fp16
+// (saturating at +-65504, MOE_FLAG_Y_SATURATED), for the layer's combine.
 // gemm_bf16.hip (bf16 activations, bf16 weights, MFMA)
 hipError_t launch_ffn_bf16(const Dims& D, const int32_t* offsets,
                            const int32_t* tiles1, const int32_t* tiles2,
                            const int32_t* sorted_token, const void* x,
-                           const moe_expert_weights& w, const float* row_scale, void* H,
-                           void* Hs, void* Y, float* Ypart, void* Ys, int32_t* err,
+                           const moe_expert_weights& w, const float* row_scale, bool y16,
+                           void* H, void* Hs, void* Y, float* Ypart, void* Ys, int32_t* err,
                            hipEvent_t mid, hipStream_t s);
 // Y[r] += Ypart[r] for the kept rows (r < offsets[E]): folds the second K
 // split into the expert outputs with the combine's own fp32 addition
@@ -222,8 +224,8 @@ hipError_t launch_ffn_u4(const Dims& D, int group, const int32_t* offsets,
 hipError_t launch_ffn_u4_tiled(const Dims& D, const int32_t* offsets, const int32_t* tiles1,
                                const int32_t* tiles2, const int32_t* sorted_token,
                                const void* x, void* X16, const moe_expert_weights& w,
-                               const float* row_scale, void* H, void* Y, int32_t* err,
-                               hipEvent_t mid, hipStream_t s);
+                               const float* row_scale, bool y16, void* H, void* Y,
+                               int32_t* err, hipEvent_t mid, hipStream_t s);
 // whether a 4-bit layer runs the tiled kernels (true) or the weight-stream
 // kernels of gemm_u4.hip (false); depends on the shapes only
 bool u4_tiled(const Dims& D);
@@ -240,7 +242,8 @@ hipError_t launch_routing_health(const Dims& D, const int32_t* counts,
 
 // combine.hip (expert outputs are fp32)
 // y_part (may be null): second K split of the expert rows, added to y_rows
-hipError_t launch_combine(const Dims& D, const void* y_rows, const float* y_part,
+// y16: y_rows and y_part hold fp16 rows
+hipError_t launch_combine(const Dims& D, const void* y_rows, const void* y_part, bool y16,
                           const int32_t* slot_row, const float* topk_w,
                           const void* y_shared, void* out, hipStream_t s);
 

@@ -151,6 +151,25 @@ def bank_for(cfg, inp, experts: Optional[Sequence[int]] = None,
                              fused=cfg.layout == synth.FUSED_GATE_UP)
 
 
+def fp16_rows_bound(y_rows, slot_row, topk_w, parts: int = 1):
+    """Elementwise bound on what keeping the expert rows in fp16 (as the
+    layer does on the matrix-core path) changes in the combined output:
+    each of a row's `parts` fp16 parts is off by at most 2^-11 of its
+    magnitude, taken here as the whole row's with headroom for parts that
+    partly cancel (4x when the down projection's K halves are stored apart),
+    weighted by |w| and summed over the token's kept slots."""
+    import torch
+    f = 2.0 ** -11 * (1.0 if parts == 1 else 4.0)
+    T, k = slot_row.shape
+    bound = torch.zeros((T, y_rows.shape[1]), dtype=torch.float32, device=y_rows.device)
+    for i in range(k):
+        r = slot_row[:, i].long()
+        kept = (r >= 0)
+        rows = y_rows[r.clamp(min=0)].abs() * topk_w[:, i:i + 1].abs()
+        bound += torch.where(kept[:, None], rows, torch.zeros_like(rows))
+    return bound * f
+
+
 def last_tile_tokens(disp, per_expert: int = 1, bm: int = 256):
     """Tokens whose rows lie in the last M tile of each expert's group (the
     ragged tail the grouped GEMM handles specially), up to ``per_expert``
