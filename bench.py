@@ -25,6 +25,8 @@ import glob
 import hashlib
 import json
 import os
+import re
+import subprocess
 import sys
 import time
 
@@ -84,6 +86,33 @@ U4_STREAM_KEY = "u4s_kernel"
 MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
                  "SQ_INSTS_VALU_MFMA_MOPS_F16 GRBM_GUI_ACTIVE")
 SIMDS = 4 * 256  # MI355X: 256 CUs of 4 SIMDs
+
+
+def kernel_label(name: str) -> str:
+    """A profiler's kernel name as a readable template id without the
+    argument list.  rocprofv3 leaves a name mangled when it holds the
+    _Float16 builtin type (Itanium code DF16_), which c++filt cannot read;
+    that code is demangled here as the half type (Dh) and printed back as
+    _Float16."""
+    if name.startswith("_Z"):
+        try:
+            r = subprocess.run(["c++filt", name.replace("DF16_", "Dh")],
+                               capture_output=True, text=True, timeout=30)
+            if r.returncode == 0 and not r.stdout.startswith("_Z"):
+                name = re.sub(r"\bhalf\b", "_Float16", r.stdout.strip())
+        except (OSError, subprocess.SubprocessError):
+            pass
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[len("void "):]
+    depth, out = 0, ""
+    for ch in name:
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out += ch
+    return out
 
 
 def sources_digest(weight_dtype: str = "bf16") -> str:
@@ -371,6 +400,9 @@ def main() -> int:
     ap.add_argument("--vendor-compare", action="store_true",
                     help="time torch.matmul per expert on the workload's kept-row counts "
                          "against this library's expert kernels; writes profiles/")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_DIR", "BENCH_LOG"),
+                    help="turn a rocprofv3 --kernel-trace --stats run of bench.py and that "
+                         "run's output into the profiles/ kernel-time summary")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
                     help="turn a --pmc run of --traffic-probe with the matrix-core counters "
                          "into the profiles/ summary")
@@ -379,6 +411,8 @@ def main() -> int:
         return summarize_traffic(args)
     if args.summarize_mfma:
         return summarize_mfma(args)
+    if args.summarize_stats:
+        return summarize_stats(args)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr)
@@ -658,7 +692,7 @@ def summarize_traffic(args) -> int:
             name = r["Kernel_Name"]
             for k in kernels_of_interest:
                 if k in name:
-                    key = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+                    key = kernel_label(name)
                     ffn.setdefault(key, []).append(float(r["Counter_Value"]))
         if not copy_kib or not ffn:
             print(f"no calibration or kernel dispatches for {counter} in {d}",
@@ -705,6 +739,82 @@ def summarize_traffic(args) -> int:
     return 0
 
 
+STATS_WORKLOADS = {
+    2: "the Mixtral-shaped layer forward (T=4096, d=4096, E=8, top-2, SwiGLU F=14336, bf16)",
+    3: "the DeepSeek-style layer forward (T=8192, d=7168, E=256 in 8 groups, top-4 groups, "
+       "top-8, sigmoid router with selection bias, routed scaling 2.5, one shared expert, "
+       "SwiGLU F=2048, bf16)",
+    4: "the Qwen-style layer forward (T=16384, d=2048, E=128, top-8, Zipf-skewed router "
+       "s=1.1, capacity factor 1.0, SwiGLU F=768, bf16)",
+    5: "the decode layer forward with 4-bit experts (T=32, d=2048, E=256, top-8, SwiGLU "
+       "F=512; timed steps rotate three input copies)",
+}
+
+
+def summarize_stats(args) -> int:
+    """profiles/<workload>_layer_kernel_stats.md: the library's kernels from
+    a rocprofv3 kernel_stats.csv (calls, average, min, max, share of all GPU
+    time) and the bench.py line of the same run."""
+    import synth
+    cfg = synth.CONFIGS[args.config]
+    d, log = args.summarize_stats
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if len(files) != 1:
+        print(f"expected one kernel_stats.csv under {d}, found {len(files)}", file=sys.stderr)
+        return 1
+    with open(files[0]) as fh:
+        rows = list(csv.DictReader(fh))
+    labels = {r["Name"]: kernel_label(r["Name"]) for r in rows}
+    ours = [r for r in rows if labels[r["Name"]].startswith("moe::")]
+    others = [r for r in rows if not labels[r["Name"]].startswith("moe::")]
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    with open(log) as fh:
+        lines = [ln for ln in fh if ln.startswith("{")]
+    if not lines or not ours:
+        print(f"no bench.py line in {log} or no library kernels in {files[0]}", file=sys.stderr)
+        return 1
+    res = json.loads(lines[-1])
+    c = cfg.cfg_id
+    out = [f"# Kernel time of {STATS_WORKLOADS.get(c, cfg.name)}", "",
+           "Commands (repository root, one MI355X):", "", "```",
+           f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format "
+           f"csv -d $REPO/gpurun_out/prof_c{c} -o bench -- python3 $REPO/bench.py --config {c} "
+           f"--steps 20 --warmup 2 --no-cpu-baseline > $REPO/gpurun_out/prof_c{c}.log",
+           f"python3 $REPO/bench.py --config {c} --summarize-stats $REPO/gpurun_out/prof_c{c} "
+           f"$REPO/gpurun_out/prof_c{c}.log",
+           "```", "",
+           "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |",
+           "|---|---|---|---|---|---|"]
+    for r in sorted(ours, key=lambda r: -float(r["TotalDurationNs"])):
+        out.append(f"| `{labels[r['Name']]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{100 * float(r['TotalDurationNs']) / total:.2f}% |")
+    out += ["", f"{len(others)} kernels of torch that draw the seeded synthetic inputs before "
+            "the timed steps (random number generation, scaling, casts, copies) are omitted "
+            "from the table (they are in the share's denominator)."]
+    if "decode" in res and cfg.weight_dtype != "u4":
+        out += ["", "The run includes bench.py's decode leg (the 4-bit decode layer, T=32): the "
+                "`u4s_kernel_*`, `logits_rowdot_kernel`, `select_kernel<4, 0, false>` and "
+                "`dispatch_small_kernel` calls and the `combine_kernel<float, float>` calls are "
+                "that leg's."]
+    rf = res["roofline"]
+    s = (f"The same run's bench.py line: {res['ms_per_step']:.3f} ms per layer step, "
+         f"{res['value']:.4g} tokens/s; roofline kernel ({rf['kernel']}) averaged "
+         f"{rf['avg_launch_ms'] * 1e3:.1f} us per launch between HIP events recorded by the "
+         f"layer on its stream, {rf['achieved']:.4g} {rf['unit']} = {100 * rf['frac']:.1f}% of "
+         f"{rf['peak']:.4g} {rf['unit']}.")
+    if "decode" in res:
+        dd = res["decode"]
+        s += (f" Decode leg: {dd.get('layer_us', float('nan')):.1f} us per layer, expert FFN "
+              f"{dd.get('ffn_us', float('nan')):.1f} us.")
+    out += ["", s]
+    path = os.path.join(ROOT, "profiles", f"{cfg.name}_layer_kernel_stats.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(out) + "\n")
+    print(f"wrote {os.path.relpath(path, ROOT)}", flush=True)
+    return 0
+
+
 def summarize_mfma(args) -> int:
     """profiles/ summary of the bf16 expert GEMMs' matrix-core counters per
     layer call: MFMA busy cycles over the GPU's busy cycles and SIMDs (the
@@ -721,7 +831,7 @@ def summarize_mfma(args) -> int:
     for r in rows:
         if int(r["Dispatch_Id"]) <= last_copy or "grouped_gemm" not in r["Kernel_Name"]:
             continue
-        key = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+        key = kernel_label(r["Kernel_Name"])
         dd = per.setdefault(key, {}).setdefault(int(r["Dispatch_Id"]), {})
         dd[r["Counter_Name"]] = float(r["Counter_Value"])
         dd["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])

@@ -51,3 +51,16 @@ def test_kernel_stats_name_the_dominant_kernels():
     for p in glob.glob(os.path.join(ROOT, "profiles", "*_layer_kernel_stats.md")):
         text = open(p).read()
         assert bench.GATE_UP_KEY in text or bench.U4_STREAM_KEY in text, p
+
+
+def test_kernel_labels_are_readable():
+    """rocprofv3 leaves names holding _Float16 mangled; the summaries print
+    them as template ids, like the names it demangles itself."""
+    assert bench.kernel_label(
+        "_ZN3moe12_GLOBAL__N_114combine_kernelIfDF16_EEvPKT0_S4_PKiPKfS8_PT_liii"
+    ) == "moe::combine_kernel<float, _Float16>"
+    assert bench.kernel_label(
+        "void moe::(anonymous namespace)::grouped_gemm_kernel<0, true, false, 256>"
+        "(moe::(anonymous namespace)::GemmArgs)") == "moe::grouped_gemm_kernel<0, true, false, 256>"
+    for p in glob.glob(os.path.join(ROOT, "profiles", "*.md")):
+        assert "_ZN3moe" not in open(p).read(), p
