@@ -51,23 +51,24 @@ count_kernel(const int32_t* __restrict__ ids, int64_t S, int E,
     hist[static_cast<int64_t>(blockIdx.x) * E + e] = h[e];
 }
 
-// Exclusive prefix sum of one int per thread over the block (blockDim a
-// multiple of 64, at most 1024).  `wsum` is LDS scratch of 16 ints.
+// Exclusive prefix sum of one value per thread over the block (blockDim a
+// multiple of 64, at most 1024).  `wsum` is LDS scratch of 16 values.
 // Returns the exclusive prefix; *total receives the block sum.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
+template <typename V>
+__device__ __forceinline__ V block_exclusive_scan(V v, V* wsum, V* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
-  int x = v;
+  V x = v;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
+    const V y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
   if (lane == 63) wsum[wv] = x;
   __syncthreads();
-  int base = 0, tot = 0;
+  V base = 0, tot = 0;
   for (int w = 0; w < nw; ++w) {
-    const int s = wsum[w];
+    const V s = wsum[w];
     if (w < wv) base += s;
     tot += s;
   }
@@ -76,15 +77,77 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   return base + x - v;
 }
 
+// The XCD ranges of one routed GEMM (XcdPlan): thread e holds expert e's
+// kept rows `kp`, its first M tile `mt_off` and the M-tile total.  An
+// expert's N-tile columns are contiguous in the tile list (each holds the
+// expert's M tiles) and cost the same, w per column, so the tile where the
+// running cost reaches x/8 of the total is found by the thread of the expert
+// it falls in, rounded to the nearest column.  Thread 0 then clamps each
+// boundary so that no range exceeds cap tiles and the later XCDs can still
+// hold the rest, and writes the kXcds + 1 boundaries (the last one is the
+// tile count); threads 0-7 zero the claim counters.
+__device__ void xcd_bounds(int E, int32_t kp, int bm, int mt_off, int mt_total,
+                           const XcdPlan& p, int32_t* __restrict__ bounds,
+                           long long* wsum64, int* sh) {
+  // the run-time claim counters of the ranges' last quarters start at zero
+  if (threadIdx.x < kXcds)
+    *reinterpret_cast<unsigned long long*>(bounds - (E + 1) + tile_claims_at(E) +
+                                           kClaimStride * threadIdx.x) = 0;
+  const int mte = threadIdx.x < E ? (kp + bm - 1) / bm : 0;
+  long long w = 0;
+  if (mte > 0) {
+    const int last = kp - (mte - 1) * bm;
+    const long long blocks = static_cast<long long>(mte - 1) * (bm / 32) + (last + 31) / 32;
+    w = p.kt * blocks + static_cast<long long>(p.c) * mte;
+  }
+  long long wt;
+  const long long P = block_exclusive_scan<long long>(w, wsum64, &wt);
+  const long long split_cost = wt * p.nt;
+  const long long total = split_cost * p.ksplit;
+  const long long split_tiles = static_cast<long long>(mt_total) * p.nt;
+  const long long all_tiles = split_tiles * p.ksplit;
+  if (w > 0) {
+    const long long lo = P * p.nt, hi = (P + w) * p.nt;
+    for (int x = 1; x < kXcds; ++x) {
+      const long long target = total * x / kXcds;
+      const long long sp = target / split_cost;
+      const long long r = target - sp * split_cost;
+      if (r >= lo && r < hi) {
+        const long long col = (r - lo + w / 2) / w;
+        sh[x] = static_cast<int>(sp * split_tiles + static_cast<long long>(mt_off) * p.nt +
+                                 col * mte);
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    long long prev = 0;
+    bounds[0] = 0;
+    for (int x = 1; x < kXcds; ++x) {
+      long long v = total > 0 ? sh[x] : 0;
+      const long long lo = max(prev, all_tiles - static_cast<long long>(kXcds - x) * p.cap);
+      v = min(max(v, lo), prev + p.cap);
+      bounds[x] = static_cast<int32_t>(v);
+      prev = v;
+    }
+    bounds[kXcds] = static_cast<int32_t>(all_tiles);
+  }
+  __syncthreads();
+}
+
 // Kept count, per-expert capacity and M-tile counts of one expert, written
-// as exclusive prefixes over experts (thread e handles expert e; E <= 1024).
+// as exclusive prefixes over experts (thread e handles expert e; E <= 1024),
+// then each routed GEMM's XCD ranges after its M-tile prefix.
 __device__ __forceinline__ int expert_prefixes(int e, int E, int32_t cnt, int64_t S,
                                                 int64_t cap, int32_t* __restrict__ counts,
                                                 int32_t* __restrict__ offsets,
                                                 int32_t* __restrict__ dropped,
                                                 int32_t* __restrict__ tiles1, int bm1,
                                                 int32_t* __restrict__ tiles2, int bm2,
+                                                const XcdPlan& p1, const XcdPlan& p2,
                                                 int* wsum) {
+  __shared__ long long wsum64[16];
+  __shared__ int sh[kXcds];
   const bool on = e < E;
   const int32_t kp = on ? (static_cast<int64_t>(cnt) < cap ? cnt : static_cast<int32_t>(cap)) : 0;
   int tot;
@@ -102,12 +165,14 @@ __device__ __forceinline__ int expert_prefixes(int e, int E, int32_t cnt, int64_
     const int o1 = block_exclusive_scan(on ? (kp + bm1 - 1) / bm1 : 0, wsum, &t);
     if (on) tiles1[e] = o1;
     if (threadIdx.x == 0) tiles1[E] = t;
+    if (p1.nt > 0) xcd_bounds(E, kp, bm1, o1, t, p1, tiles1 + E + 1, wsum64, sh);
   }
   if (tiles2) {
     int t;
     const int o2 = block_exclusive_scan(on ? (kp + bm2 - 1) / bm2 : 0, wsum, &t);
     if (on) tiles2[e] = o2;
     if (threadIdx.x == 0) tiles2[E] = t;
+    if (p2.nt > 0) xcd_bounds(E, kp, bm2, o2, t, p2, tiles2 + E + 1, wsum64, sh);
   }
   return off;
 }
@@ -118,7 +183,7 @@ __global__ void __launch_bounds__(1024)
 scan_kernel(int32_t* __restrict__ hist, int nb, int E, int64_t S, int64_t cap,
             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
             int32_t* __restrict__ dropped, int32_t* __restrict__ tiles1,
-            int bm1, int32_t* __restrict__ tiles2, int bm2) {
+            int bm1, int32_t* __restrict__ tiles2, int bm2, XcdPlan p1, XcdPlan p2) {
   __shared__ int wsum[16];
   const int e = threadIdx.x;
   int32_t run = 0;
@@ -139,7 +204,7 @@ scan_kernel(int32_t* __restrict__ hist, int nb, int E, int64_t S, int64_t cap,
     }
   }
   expert_prefixes(e, E, run, S, cap, counts, offsets, dropped, tiles1, bm1,
-                  tiles2, bm2, wsum);
+                  tiles2, bm2, p1, p2, wsum);
 }
 
 __global__ void __launch_bounds__(256)
@@ -227,17 +292,21 @@ scatter_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
 __global__ void __launch_bounds__(1024)
 tile_prefix_kernel(const int32_t* __restrict__ offsets, int E,
                    int32_t* __restrict__ tiles1, int bm1,
-                   int32_t* __restrict__ tiles2, int bm2) {
+                   int32_t* __restrict__ tiles2, int bm2, XcdPlan p1, XcdPlan p2) {
   __shared__ int wsum[16];
+  __shared__ long long wsum64[16];
+  __shared__ int sh[kXcds];
   const int e = threadIdx.x;
   const int32_t n = e < E ? offsets[e + 1] - offsets[e] : 0;
   int t;
   const int o1 = block_exclusive_scan(e < E ? (n + bm1 - 1) / bm1 : 0, wsum, &t);
   if (e < E) tiles1[e] = o1;
   if (e == 0) tiles1[E] = t;
+  if (p1.nt > 0) xcd_bounds(E, n, bm1, o1, t, p1, tiles1 + E + 1, wsum64, sh);
   const int o2 = block_exclusive_scan(e < E ? (n + bm2 - 1) / bm2 : 0, wsum, &t);
   if (e < E) tiles2[e] = o2;
   if (e == 0) tiles2[E] = t;
+  if (p2.nt > 0) xcd_bounds(E, n, bm2, o2, t, p2, tiles2 + E + 1, wsum64, sh);
 }
 
 // All of the dispatch in one block when the slots fit one chunk (decode-
@@ -248,7 +317,7 @@ dispatch_small_kernel(const int32_t* __restrict__ ids, const float* __restrict__
                       int64_t S, int k, int E, int64_t cap, int nbits,
                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                       int32_t* __restrict__ dropped, int32_t* __restrict__ tiles1,
-                      int bm1, int32_t* __restrict__ tiles2, int bm2,
+                      int bm1, int32_t* __restrict__ tiles2, int bm2, XcdPlan p1, XcdPlan p2,
                       int32_t* __restrict__ sorted_token, float* __restrict__ sorted_w,
                       int32_t* __restrict__ slot_row, int32_t* __restrict__ err) {
   __shared__ int wsum[16];
@@ -270,7 +339,7 @@ dispatch_small_kernel(const int32_t* __restrict__ ids, const float* __restrict__
   __syncthreads();
   const int32_t cnt = tid < E ? h[tid] : 0;
   const int off = expert_prefixes(tid, E, cnt, S, cap, counts, offsets, dropped,
-                                  tiles1, bm1, tiles2, bm2, wsum);
+                                  tiles1, bm1, tiles2, bm2, p1, p2, wsum);
   if (tid < E) offs[tid] = off;
   __syncthreads();
   // ranks: slots in flat order; inside a wave, lanes with the same expert
@@ -354,15 +423,16 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
   if (D.slots <= kDispatchChunk) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, ids, w,
                        D.slots, D.k, D.E, D.cap, nbits, counts, offsets, dropped,
-                       tiles1, routed_bm(D), tiles2, routed_bm(D), sorted_token, sorted_w,
-                       slot_row, err);
+                       tiles1, routed_bm(D), tiles2, routed_bm(D), xcd_plan(D, false),
+                       xcd_plan(D, true), sorted_token, sorted_w, slot_row, err);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(count_kernel, dim3(nblocks), dim3(256), hsz, s, ids,
                      D.slots, D.E, hist, err);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, hist,
                      nblocks, D.E, D.slots, D.cap, counts, offsets, dropped,
-                     tiles1, routed_bm(D), tiles2, routed_bm(D));
+                     tiles1, routed_bm(D), tiles2, routed_bm(D), xcd_plan(D, false),
+                     xcd_plan(D, true));
   hipLaunchKernelGGL(scatter_kernel, dim3(nblocks), dim3(256), 6 * hsz, s, ids,
                      w, D.slots, D.k, D.E, D.cap, nbits, hist, offsets,
                      sorted_token, sorted_w, slot_row);
@@ -372,7 +442,8 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
 hipError_t launch_tile_prefix(const Dims& D, const int32_t* offsets,
                               int32_t* tiles1, int32_t* tiles2, hipStream_t s) {
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, D.E,
-                     tiles1, routed_bm(D), tiles2, routed_bm(D));
+                     tiles1, routed_bm(D), tiles2, routed_bm(D), xcd_plan(D, false),
+                     xcd_plan(D, true));
   return hipGetLastError();
 }
 

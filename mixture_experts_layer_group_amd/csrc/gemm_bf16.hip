@@ -214,19 +214,69 @@ __device__ __forceinline__ uint4 dequant8(uint32_t w, float sc, float bi, uint32
 // round-robin over XCDs) gets a contiguous range of tiles, in expert-major
 // order: per expert, groups of kNG N-tiles; inside a group the expert's
 // M-tiles run fastest, so the workgroups that run together on one XCD share
-// each weight tile and the expert's activation rows.
+// each weight tile and the expert's activation rows.  For ragged groups the
+// ranges are cut at equal estimated cost (XcdPlan; the dispatch wrote the
+// boundaries after the M-tile prefix), for one group at equal count.
 struct TileSched {
   int e, row0, cnt, mt, nt, split;
 };
 
-__device__ __forceinline__ bool schedule_tile(const GemmArgs& g, int bm, TileSched& t) {
+// One tile of the last quarters of the XCD ranges, claimed by thread 0 of a
+// workgroup of XCD x: from the front of x's own quarter (own), else from
+// the back of another XCD's (see XcdPlan); -1 when none is left.  Relaxed
+// device-scope atomics: the counters only hand out distinct tiles.  A
+// counter is read before it is incremented, so workgroups that come late
+// do not queue increments on counters that are spent.
+__device__ int claim_tile(const int32_t* xb, unsigned long long* claims, int x, bool own) {
+  for (int j = own ? 0 : 1; j < (own ? 1 : kXcds); ++j) {
+    const int y = (x + j) & (kXcds - 1);
+    const int hi = xb[y + 1];
+    const int q = (hi - xb[y]) >> 2;
+    if (q <= 0) continue;
+    unsigned long long* c = claims + kClaimStride / 2 * y;
+    const unsigned long long now = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (static_cast<int>(now & 0xffffffffull) + static_cast<int>(now >> 32) >= q) continue;
+    const unsigned long long old = __hip_atomic_fetch_add(
+        c, own ? 1ull : 1ull << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int front = static_cast<int>(old & 0xffffffffull);
+    const int back = static_cast<int>(old >> 32);
+    if (front + back < q) return own ? hi - q + front : hi - 1 - back;
+  }
+  return -1;
+}
+
+__device__ __forceinline__ bool schedule_tile(const GemmArgs& g, int bm, TileSched& t,
+                                              int* lds_word) {
   const int total_mt = g.tiles ? g.tiles[g.E] : (g.single_rows + bm - 1) / bm;
   const int real = total_mt * g.NT;
-  const int share = (real * g.ksplit + 7) >> 3;
   const int bid = blockIdx.x;
   const int local = bid >> 3;
-  if (local >= share) return false;
-  int L = (bid & 7) * share + local;
+  int L;
+  if (g.tiles) {
+    // the XCD's range of equal estimated cost, written after the prefix; its
+    // last quarter is claimed at run time (shared with the other XCDs)
+    const int32_t* xb = g.tiles + g.E + 1;
+    const int start = xb[bid & 7];
+    const int size = xb[(bid & 7) + 1] - start;
+    if (local < size - (size >> 2)) {
+      L = start + local;
+    } else {
+      // the quarter's own claims, then at most kStealers claims elsewhere
+      if (local >= size + kStealers) return false;
+      if (threadIdx.x == 0)
+        *lds_word = claim_tile(xb, reinterpret_cast<unsigned long long*>(
+                                       const_cast<int32_t*>(g.tiles) + tile_claims_at(g.E)),
+                               bid & 7, local < size);
+      __syncthreads();
+      L = *lds_word;
+      __syncthreads();  // the word is LDS that the tile's loads reuse
+      if (L < 0) return false;
+    }
+  } else {
+    const int share = (real * g.ksplit + 7) >> 3;
+    if (local >= share) return false;
+    L = (bid & 7) * share + local;
+  }
   if (L >= real * g.ksplit) return false;
   t.split = L / real;  // K split (slowest, so each split's tiles keep their order)
   L -= t.split * real;
@@ -295,7 +345,7 @@ grouped_gemm_kernel(GemmArgs g) {
 
   // ---------------- tile scheduling
   TileSched ts;
-  if (!schedule_tile(g, TC::BM, ts)) return;
+  if (!schedule_tile(g, TC::BM, ts, reinterpret_cast<int*>(smem))) return;
   const int e = ts.e, row0 = ts.row0, cnt = ts.cnt, mt = ts.mt, nt = ts.nt, split = ts.split;
   const int m0 = mt * TC::BM;  // first row of this tile inside the group
 
@@ -831,14 +881,21 @@ hipError_t launch_bm(int mode, bool gather, bool u4, const GemmArgs& g, dim3 gri
   return hipGetLastError();
 }
 
+// Workgroups of a routed (ragged) launch: rows_upper, an upper bound on the
+// kept rows, fills rows_upper / bm M tiles plus at most one partial tile per
+// expert; rounded to whole XCD rounds.  The XCD ranges written by the
+// dispatch hold at most an eighth of these each.
+int64_t routed_grid(int64_t rows_upper, int bm, int E, int NT, int ksplit) {
+  const int64_t n = (rows_upper / bm + E) * NT * ksplit;
+  return (n + kXcds - 1) / kXcds * kXcds;
+}
+
 // rows_upper: an upper bound on the group's rows (single group) or on the
-// kept rows (grouped); the grid covers its M tiles plus one partial tile per
-// expert, rounded to whole XCD rounds
+// kept rows (grouped)
 hipError_t launch_one(int mode, bool gather, const GemmArgs& g, int64_t rows_upper, int bm,
                       hipStream_t s, bool u4 = false) {
-  const int64_t mt_upper = g.tiles ? rows_upper / bm + g.E : (rows_upper + bm - 1) / bm;
-  int64_t n = mt_upper * g.NT * g.ksplit;
-  n = (n + 7) / 8 * 8;
+  int64_t n = g.tiles ? routed_grid(rows_upper, bm, g.E, g.NT, g.ksplit)
+                      : ((rows_upper + bm - 1) / bm * g.NT * g.ksplit + 7) / 8 * 8;
   if (n <= 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>(n));
   if (bm == 128) return launch_bm<128>(mode, gather, u4, g, grid, s);
@@ -852,6 +909,35 @@ int routed_bm(const Dims& D) {
   if (!D.u4) return 256;
   const int64_t nmax = std::min<int64_t>(D.slots, D.cap * D.E);
   return nmax >= 64 * static_cast<int64_t>(D.E) ? 256 : 128;
+}
+
+// Tile costs for the XCD ranges, in units of one 32-row block's share of a
+// K step, from per-workgroup timestamps of the Mixtral- and Qwen-shaped
+// layers: a gate/up K step costs about 12-19 units plus one per 32-row block
+// (Mixtral-shaped 1.03 us with one block, 1.45 us with eight), a down K step
+// about 5-11 plus one per block; set-up, first loads and epilogue add a few
+// microseconds per tile.  The spread between workloads (and between XCDs)
+// is what the run-time claims of the ranges' last quarters even out.
+constexpr int kStepCostUp = 13, kTileCostUp = 100;
+constexpr int kStepCostDown = 7, kTileCostDown = 60;
+
+XcdPlan xcd_plan(const Dims& D, bool down) {
+  XcdPlan p;
+  if (!D.bf16 || (D.u4 && !u4_tiled(D))) return p;  // no routed tiled GEMM
+  const int64_t nmax = std::min<int64_t>(D.slots, D.cap * D.E);
+  if (down) {
+    p.nt = ntiles(kDown, D.d);
+    p.ksplit = down_splits(D);
+    p.kt = static_cast<int>(D.F / BK / p.ksplit);
+    p.c = p.kt * kStepCostDown + kTileCostDown;
+  } else {
+    p.nt = ntiles(D.swiglu ? kSwiGLU : kReLU, D.F);
+    p.kt = static_cast<int>(D.d / BK);
+    p.c = p.kt * kStepCostUp + kTileCostUp;
+  }
+  p.cap = static_cast<int>(routed_grid(nmax, routed_bm(D), static_cast<int>(D.E), p.nt,
+                                       p.ksplit) / kXcds);
+  return p;
 }
 
 int down_splits(const Dims& D) {

@@ -152,8 +152,8 @@ WsLayout layout_of(const Dims& D) {
   L.logits = take(static_cast<size_t>(rp.S) * T * E * 4);
   L.probpart = take(static_cast<size_t>(L.route_blocks) * E * 4);
   L.hist = take(static_cast<size_t>(L.dispatch_blocks) * E * 4);
-  L.tiles1 = take((E + 1) * 4);
-  L.tiles2 = take((E + 1) * 4);
+  L.tiles1 = take(tile_plan_entries(E) * 4);
+  L.tiles2 = take(tile_plan_entries(E) * 4);
   L.topk_ids = take(S * 4);
   L.topk_w = take(S * 4);
   L.counts = take(E * 4);

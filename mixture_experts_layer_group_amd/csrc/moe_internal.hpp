@@ -149,6 +149,46 @@ constexpr int kSelectWaves = 4;       // tokens in flight per select block
 // The dispatch scan writes the per-expert M-tile prefix for this size.
 int routed_bm(const Dims& D);
 
+// How the routed grouped GEMM's tiles are shared out over the chip's 8 XCDs
+// (hardware dispatch sends workgroup i to XCD i mod 8).  Each XCD takes a
+// contiguous range of the tile list (so tiles sharing weights and rows meet
+// in its L2), the ranges cut at equal estimated cost rather than equal
+// count: a tile of b 32-row blocks costs kt*b + c (kt K steps; c the part of
+// a K step that does not shrink with the rows, times kt, plus the tile's
+// set-up and epilogue, in the same units), so XCDs given many short tiles
+// (skewed routing, ragged tails) take more of them.  No range holds more
+// than `cap` tiles, the workgroups one XCD receives.  The dispatch (or the
+// tile-prefix kernel) writes the kXcds + 1 boundaries after the E + 1
+// M-tile prefixes; nt == 0: no routed tiled GEMM runs.  The first three
+// quarters of a range go to the XCD's workgroups by their order; the last
+// quarter is claimed at run time through one 64-bit counter per XCD (low
+// half: the XCD's own claims from the front, high half: other XCDs' claims
+// from the back, the claim valid while the two sum to less than the
+// quarter), so XCDs that finish early take over tiles of slower ones.  The
+// producer of the boundaries zeroes the counters.
+constexpr int kXcds = 8;
+struct XcdPlan {
+  int nt = 0;      // N tiles
+  int ksplit = 1;  // K splits (the tile list repeats once per split)
+  int kt = 0;      // K steps per tile
+  int c = 0;       // cost of a tile beyond kt per 32-row block
+  int cap = 0;     // workgroups per XCD in the launch
+};
+XcdPlan xcd_plan(const Dims& D, bool down);
+// Workgroups per XCD that may take tiles of other XCDs' last quarters (the
+// grid's other surplus workgroups exit without touching memory).
+constexpr int kStealers = 64;
+// A tile-prefix buffer (int32 entries, 128-byte aligned): E + 1 prefixes,
+// kXcds + 1 boundaries, then kXcds 64-bit claim counters, one per 128-byte
+// line (kClaimStride entries apart).
+constexpr int kClaimStride = 32;
+__host__ __device__ inline int64_t tile_claims_at(int64_t E) {
+  return (E + 1 + kXcds + 1 + kClaimStride - 1) / kClaimStride * kClaimStride;
+}
+__host__ __device__ inline int64_t tile_plan_entries(int64_t E) {
+  return tile_claims_at(E) + kClaimStride * kXcds;
+}
+
 // K splits of the grouped down projection (1 or 2).  Too few output tiles
 // for the chip leave its last round of workgroups mostly idle; splitting
 // the reduction in two halves the tile length and doubles the tile count.
