@@ -77,62 +77,109 @@ __device__ __forceinline__ V block_exclusive_scan(V v, V* wsum, V* total) {
   return base + x - v;
 }
 
-// The XCD ranges of one routed GEMM (XcdPlan): thread e holds expert e's
-// kept rows `kp`, its first M tile `mt_off` and the M-tile total.  An
-// expert's N-tile columns are contiguous in the tile list (each holds the
-// expert's M tiles) and cost the same, w per column, so the tile where the
-// running cost reaches x/8 of the total is found by the thread of the expert
-// it falls in, rounded to the nearest column.  Thread 0 then clamps each
-// boundary so that no range exceeds cap tiles and the later XCDs can still
-// hold the rest, and writes the kXcds + 1 boundaries (the last one is the
-// tile count); threads 0-7 zero the claim counters.
-__device__ void xcd_bounds(int E, int32_t kp, int bm, int mt_off, int mt_total,
-                           const XcdPlan& p, int32_t* __restrict__ bounds,
-                           long long* wsum64, int* sh) {
-  // the run-time claim counters of the ranges' last quarters start at zero
-  if (threadIdx.x < kXcds)
-    *reinterpret_cast<unsigned long long*>(bounds - (E + 1) + tile_claims_at(E) +
-                                           kClaimStride * threadIdx.x) = 0;
-  const int mte = threadIdx.x < E ? (kp + bm - 1) / bm : 0;
-  long long w = 0;
-  if (mte > 0) {
-    const int last = kp - (mte - 1) * bm;
-    const long long blocks = static_cast<long long>(mte - 1) * (bm / 32) + (last + 31) / 32;
-    w = p.kt * blocks + static_cast<long long>(p.c) * mte;
+// The XCD ranges of the two routed GEMMs (XcdPlan; nt == 0 or tiles null:
+// none), by the whole block (thread e holds expert e's kept rows kp and
+// first M tile mt_off; E <= 1024).  An expert's N-tile columns are
+// contiguous in the tile list (each holds its M tiles) and cost the same,
+// w = kt x (its 32-row blocks) + c x (its M tiles), so in units of one
+// column of every expert the list's cost is the prefix of w: expert e spans
+// [pre[e], pre[e + 1]) (both read from LDS, so the spans tile the line
+// exactly), its columns w / nt each.  The thread of the expert where the
+// running cost reaches x/8 of the total (over the K splits) writes that
+// boundary, rounded to the nearest column.  fp32 costs are plenty for
+// balancing; a boundary no thread writes stays at -1, which the clamps
+// lift.  Threads 0 and 64 then clamp each GEMM's boundaries so that no
+// range exceeds cap tiles and the later XCDs can still hold the rest, and
+// write the kXcds + 1 of them (the last is the tile count); threads 0-7 zero
+// the claim counters.
+struct XcdScratch {
+  float wsum[2][16];
+  float pre[2][1025];
+  int sh[2][kXcds];
+};
+
+__device__ __forceinline__ float gemm_cost(int kp, int mte, const XcdPlan& p) {
+  return mte > 0 ? static_cast<float>(p.kt) * static_cast<float>((kp + 31) >> 5) +
+                       static_cast<float>(p.c) * static_cast<float>(mte)
+                 : 0.f;
+}
+
+__device__ void xcd_bounds(int E, int32_t kp, int mte, int mt_off, int mt_total,
+                           const XcdPlan& p1, int32_t* __restrict__ tiles1,
+                           const XcdPlan& p2, int32_t* __restrict__ tiles2, XcdScratch& x_) {
+  const int e = threadIdx.x, lane = e & (kWave - 1), wv = e / kWave, nw = blockDim.x / kWave;
+  const bool on1 = tiles1 != nullptr && p1.nt > 0, on2 = tiles2 != nullptr && p2.nt > 0;
+  if (e < kXcds) {
+    if (on1)
+      *reinterpret_cast<unsigned long long*>(tiles1 + tile_claims_at(E) + kClaimStride * e) = 0;
+    if (on2)
+      *reinterpret_cast<unsigned long long*>(tiles2 + tile_claims_at(E) + kClaimStride * e) = 0;
+    x_.sh[0][e] = -1;
+    x_.sh[1][e] = -1;
   }
-  long long wt;
-  const long long P = block_exclusive_scan<long long>(w, wsum64, &wt);
-  const long long split_cost = wt * p.nt;
-  const long long total = split_cost * p.ksplit;
-  const long long split_tiles = static_cast<long long>(mt_total) * p.nt;
-  const long long all_tiles = split_tiles * p.ksplit;
-  if (w > 0) {
-    const long long lo = P * p.nt, hi = (P + w) * p.nt;
-    for (int x = 1; x < kXcds; ++x) {
-      const long long target = total * x / kXcds;
-      const long long sp = target / split_cost;
-      const long long r = target - sp * split_cost;
-      if (r >= lo && r < hi) {
-        const long long col = (r - lo + w / 2) / w;
-        sh[x] = static_cast<int>(sp * split_tiles + static_cast<long long>(mt_off) * p.nt +
-                                 col * mte);
+  const float w[2] = {on1 ? gemm_cost(kp, mte, p1) : 0.f, on2 ? gemm_cost(kp, mte, p2) : 0.f};
+  // exclusive prefix of both costs over the block (one pass, two barriers)
+  float inc[2] = {w[0], w[1]};
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const float y = __shfl_up(inc[g], o, kWave);
+      if (lane >= o) inc[g] += y;
+    }
+  }
+  if (lane == kWave - 1) {
+    x_.wsum[0][wv] = inc[0];
+    x_.wsum[1][wv] = inc[1];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    float base = 0.f;
+    for (int v = 0; v < wv; ++v) base += x_.wsum[g][v];
+    const float P = base + inc[g] - w[g];
+    if (e < E) x_.pre[g][e] = P;
+    if (e == E - 1) x_.pre[g][E] = P + w[g];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const XcdPlan& p = g == 0 ? p1 : p2;
+    const float total = x_.pre[g][E];
+    if (w[g] > 0.f && total > 0.f) {
+      const float lo = x_.pre[g][e], hi = x_.pre[g][e + 1];
+      for (int x = 1; x < kXcds; ++x) {
+        float r = total * static_cast<float>(p.ksplit * x) * (1.f / kXcds);
+        int sp = 0;
+        while (sp + 1 < p.ksplit && r >= total) {
+          r -= total;
+          ++sp;
+        }
+        if (r >= lo && r < hi) {
+          int col = static_cast<int>((r - lo) * static_cast<float>(p.nt) / w[g] + 0.5f);
+          col = col < 0 ? 0 : (col > p.nt ? p.nt : col);
+          x_.sh[g][x] = sp * mt_total * p.nt + mt_off * p.nt + col * mte;
+        }
       }
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    long long prev = 0;
+  const int g = e == 0 ? 0 : (e == kWave && nw > 1 ? 1 : -1);
+  if (g >= 0 && (g == 0 ? on1 : on2)) {
+    const XcdPlan& p = g == 0 ? p1 : p2;
+    int32_t* bounds = (g == 0 ? tiles1 : tiles2) + E + 1;
+    const int all_tiles = mt_total * p.nt * p.ksplit;
+    int prev = 0;
     bounds[0] = 0;
     for (int x = 1; x < kXcds; ++x) {
-      long long v = total > 0 ? sh[x] : 0;
-      const long long lo = max(prev, all_tiles - static_cast<long long>(kXcds - x) * p.cap);
+      int v = x_.sh[g][x];
+      const int lo = max(prev, all_tiles - (kXcds - x) * p.cap);
       v = min(max(v, lo), prev + p.cap);
-      bounds[x] = static_cast<int32_t>(v);
+      bounds[x] = v;
       prev = v;
     }
-    bounds[kXcds] = static_cast<int32_t>(all_tiles);
+    bounds[kXcds] = all_tiles;
   }
-  __syncthreads();
 }
 
 // Kept count, per-expert capacity and M-tile counts of one expert, written
@@ -142,12 +189,10 @@ __device__ __forceinline__ int expert_prefixes(int e, int E, int32_t cnt, int64_
                                                 int64_t cap, int32_t* __restrict__ counts,
                                                 int32_t* __restrict__ offsets,
                                                 int32_t* __restrict__ dropped,
-                                                int32_t* __restrict__ tiles1, int bm1,
-                                                int32_t* __restrict__ tiles2, int bm2,
+                                                int32_t* __restrict__ tiles1,
+                                                int32_t* __restrict__ tiles2, int bm,
                                                 const XcdPlan& p1, const XcdPlan& p2,
                                                 int* wsum) {
-  __shared__ long long wsum64[16];
-  __shared__ int sh[kXcds];
   const bool on = e < E;
   const int32_t kp = on ? (static_cast<int64_t>(cnt) < cap ? cnt : static_cast<int32_t>(cap)) : 0;
   int tot;
@@ -160,19 +205,20 @@ __device__ __forceinline__ int expert_prefixes(int e, int E, int32_t cnt, int64_
     offsets[E] = tot;
     dropped[0] = static_cast<int32_t>(S - tot);
   }
-  if (tiles1) {
+  if (tiles1 || tiles2) {
+    // both GEMMs use bm-row tiles: one M-tile prefix serves both
     int t;
-    const int o1 = block_exclusive_scan(on ? (kp + bm1 - 1) / bm1 : 0, wsum, &t);
-    if (on) tiles1[e] = o1;
-    if (threadIdx.x == 0) tiles1[E] = t;
-    if (p1.nt > 0) xcd_bounds(E, kp, bm1, o1, t, p1, tiles1 + E + 1, wsum64, sh);
-  }
-  if (tiles2) {
-    int t;
-    const int o2 = block_exclusive_scan(on ? (kp + bm2 - 1) / bm2 : 0, wsum, &t);
-    if (on) tiles2[e] = o2;
-    if (threadIdx.x == 0) tiles2[E] = t;
-    if (p2.nt > 0) xcd_bounds(E, kp, bm2, o2, t, p2, tiles2 + E + 1, wsum64, sh);
+    const int mte = on ? (kp + bm - 1) / bm : 0;
+    const int o = block_exclusive_scan(mte, wsum, &t);
+    if (on && tiles1) tiles1[e] = o;
+    if (on && tiles2) tiles2[e] = o;
+    if (threadIdx.x == 0) {
+      if (tiles1) tiles1[E] = t;
+      if (tiles2) tiles2[E] = t;
+    }
+    __shared__ XcdScratch xs;
+    if ((tiles1 && p1.nt > 0) || (tiles2 && p2.nt > 0))
+      xcd_bounds(E, kp, mte, o, t, p1, tiles1, p2, tiles2, xs);
   }
   return off;
 }
@@ -183,7 +229,7 @@ __global__ void __launch_bounds__(1024)
 scan_kernel(int32_t* __restrict__ hist, int nb, int E, int64_t S, int64_t cap,
             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
             int32_t* __restrict__ dropped, int32_t* __restrict__ tiles1,
-            int bm1, int32_t* __restrict__ tiles2, int bm2, XcdPlan p1, XcdPlan p2) {
+            int32_t* __restrict__ tiles2, int bm, XcdPlan p1, XcdPlan p2) {
   __shared__ int wsum[16];
   const int e = threadIdx.x;
   int32_t run = 0;
@@ -203,8 +249,8 @@ scan_kernel(int32_t* __restrict__ hist, int nb, int E, int64_t S, int64_t cap,
       }
     }
   }
-  expert_prefixes(e, E, run, S, cap, counts, offsets, dropped, tiles1, bm1,
-                  tiles2, bm2, p1, p2, wsum);
+  expert_prefixes(e, E, run, S, cap, counts, offsets, dropped, tiles1, tiles2, bm, p1,
+                  p2, wsum);
 }
 
 __global__ void __launch_bounds__(256)
@@ -290,23 +336,24 @@ scatter_kernel(const int32_t* __restrict__ ids, const float* __restrict__ w,
 }
 
 __global__ void __launch_bounds__(1024)
-tile_prefix_kernel(const int32_t* __restrict__ offsets, int E,
-                   int32_t* __restrict__ tiles1, int bm1,
-                   int32_t* __restrict__ tiles2, int bm2, XcdPlan p1, XcdPlan p2) {
+tile_prefix_kernel(const int32_t* __restrict__ offsets, int E, int32_t* __restrict__ tiles1,
+                   int32_t* __restrict__ tiles2, int bm, XcdPlan p1, XcdPlan p2) {
   __shared__ int wsum[16];
-  __shared__ long long wsum64[16];
-  __shared__ int sh[kXcds];
+  __shared__ XcdScratch xs;
   const int e = threadIdx.x;
   const int32_t n = e < E ? offsets[e + 1] - offsets[e] : 0;
+  const int mte = (n + bm - 1) / bm;
   int t;
-  const int o1 = block_exclusive_scan(e < E ? (n + bm1 - 1) / bm1 : 0, wsum, &t);
-  if (e < E) tiles1[e] = o1;
-  if (e == 0) tiles1[E] = t;
-  if (p1.nt > 0) xcd_bounds(E, n, bm1, o1, t, p1, tiles1 + E + 1, wsum64, sh);
-  const int o2 = block_exclusive_scan(e < E ? (n + bm2 - 1) / bm2 : 0, wsum, &t);
-  if (e < E) tiles2[e] = o2;
-  if (e == 0) tiles2[E] = t;
-  if (p2.nt > 0) xcd_bounds(E, n, bm2, o2, t, p2, tiles2 + E + 1, wsum64, sh);
+  const int o = block_exclusive_scan(mte, wsum, &t);
+  if (e < E) {
+    tiles1[e] = o;
+    tiles2[e] = o;
+  }
+  if (e == 0) {
+    tiles1[E] = t;
+    tiles2[E] = t;
+  }
+  if (p1.nt > 0 || p2.nt > 0) xcd_bounds(E, n, mte, o, t, p1, tiles1, p2, tiles2, xs);
 }
 
 // All of the dispatch in one block when the slots fit one chunk (decode-
@@ -317,7 +364,7 @@ dispatch_small_kernel(const int32_t* __restrict__ ids, const float* __restrict__
                       int64_t S, int k, int E, int64_t cap, int nbits,
                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                       int32_t* __restrict__ dropped, int32_t* __restrict__ tiles1,
-                      int bm1, int32_t* __restrict__ tiles2, int bm2, XcdPlan p1, XcdPlan p2,
+                      int32_t* __restrict__ tiles2, int bm, XcdPlan p1, XcdPlan p2,
                       int32_t* __restrict__ sorted_token, float* __restrict__ sorted_w,
                       int32_t* __restrict__ slot_row, int32_t* __restrict__ err) {
   __shared__ int wsum[16];
@@ -339,7 +386,7 @@ dispatch_small_kernel(const int32_t* __restrict__ ids, const float* __restrict__
   __syncthreads();
   const int32_t cnt = tid < E ? h[tid] : 0;
   const int off = expert_prefixes(tid, E, cnt, S, cap, counts, offsets, dropped,
-                                  tiles1, bm1, tiles2, bm2, p1, p2, wsum);
+                                  tiles1, tiles2, bm, p1, p2, wsum);
   if (tid < E) offs[tid] = off;
   __syncthreads();
   // ranks: slots in flat order; inside a wave, lanes with the same expert
@@ -423,7 +470,7 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
   if (D.slots <= kDispatchChunk) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, ids, w,
                        D.slots, D.k, D.E, D.cap, nbits, counts, offsets, dropped,
-                       tiles1, routed_bm(D), tiles2, routed_bm(D), xcd_plan(D, false),
+                       tiles1, tiles2, routed_bm(D), xcd_plan(D, false),
                        xcd_plan(D, true), sorted_token, sorted_w, slot_row, err);
     return hipGetLastError();
   }
@@ -431,7 +478,7 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
                      D.slots, D.E, hist, err);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, hist,
                      nblocks, D.E, D.slots, D.cap, counts, offsets, dropped,
-                     tiles1, routed_bm(D), tiles2, routed_bm(D), xcd_plan(D, false),
+                     tiles1, tiles2, routed_bm(D), xcd_plan(D, false),
                      xcd_plan(D, true));
   hipLaunchKernelGGL(scatter_kernel, dim3(nblocks), dim3(256), 6 * hsz, s, ids,
                      w, D.slots, D.k, D.E, D.cap, nbits, hist, offsets,
@@ -442,7 +489,7 @@ hipError_t launch_dispatch(const Dims& D, const int32_t* ids, const float* w,
 hipError_t launch_tile_prefix(const Dims& D, const int32_t* offsets,
                               int32_t* tiles1, int32_t* tiles2, hipStream_t s) {
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, D.E,
-                     tiles1, routed_bm(D), tiles2, routed_bm(D), xcd_plan(D, false),
+                     tiles1, tiles2, routed_bm(D), xcd_plan(D, false),
                      xcd_plan(D, true));
   return hipGetLastError();
 }

@@ -166,7 +166,7 @@ int routed_bm(const Dims& D);
 // from the back, the claim valid while the two sum to less than the
 // quarter), so XCDs that finish early take over tiles of slower ones.  The
 // producer of the boundaries zeroes the counters.
-constexpr int kXcds = 8;
+constexpr int kXcds = 8;  // (dispatch.hip divides by it with a shift)
 struct XcdPlan {
   int nt = 0;      // N tiles
   int ksplit = 1;  // K splits (the tile list repeats once per split)
