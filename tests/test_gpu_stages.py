@@ -295,6 +295,48 @@ def test_routing_weights_applied_in_the_ffn(name):
     gu.full_check(cfg, inp, r2)
 
 
+def test_grouped_ffn_skewed_loads_clamped_xcd_ranges():
+    """One expert takes 2041 of 2048 rows (8 M tiles per N column), seven
+    take one row each (one-row tiles).  The grouped GEMMs' XCD ranges, cut at
+    equal estimated cost, would give the XCDs holding the one-row tiles more
+    tiles than the 16 workgroups each XCD receives (120 gate/up tiles on a
+    grid of 128): the boundaries are clamped, the down product's list is
+    doubled by its K split, and the last quarters are claimed at run time.
+    Every token of the stage API's output must still meet the oracle's bar,
+    and every dispatched row must come back."""
+    import mixture_experts_layer_group_amd as moe
+    cfg = C("skew-one-expert", 144, T=2048, d=512, E=8, top_k=1, F=1024)
+    T, k, E, d = cfg.T, cfg.top_k, cfg.E, cfg.d
+    gu.log(f"[skewed loads] T={T} d={d} E={E} F={cfg.F}: 2041 rows on expert 0")
+    inp = gu.make_inputs(cfg)
+    spec = moe.spec_from_config(cfg)
+    dev = "cuda"
+    ws = moe.workspace(spec, T)
+    ids = torch.zeros((T, k), dtype=torch.int32, device=dev)
+    ids[T - 7:, 0] = torch.arange(1, 8, dtype=torch.int32, device=dev)
+    g = torch.Generator(device="cpu").manual_seed(144)
+    tw = (0.5 + torch.rand((T, k), generator=g)).to(dev)
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    st = torch.empty(T * k, dtype=torch.int32, device=dev)
+    sw = torch.empty(T * k, dtype=torch.float32, device=dev)
+    sr = torch.empty((T, k), dtype=torch.int32, device=dev)
+    dropped = torch.empty(1, dtype=torch.int32, device=dev)
+    moe.moe_dispatch(spec, T, ids, tw, counts, offsets, st, sw, sr, dropped, None, None, ws)
+    y = torch.full((T * k, d), float("nan"), dtype=torch.float32, device=dev)
+    moe.moe_grouped_ffn(spec, T, offsets, st, inp["x"], inp, y, None, ws)
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    moe.moe_combine(spec, T, y, sr, tw, None, out)
+    torch.cuda.synchronize()
+    assert counts.cpu().tolist() == [T - 7] + [1] * 7
+    assert bool(torch.isfinite(y).all())  # every row written (no tile skipped)
+    ids_h = ids.cpu().numpy()
+    disp = gu.check_dispatch(cfg, ids_h, {"counts_pre": counts, "offsets": offsets,
+                                          "dropped": dropped, "sorted_token": st,
+                                          "slot_row": sr})
+    gu.check_output(cfg, inp, {"out": out}, ids_h, tw.cpu().numpy().astype(np.float64), disp)
+
+
 def test_determinism_bitwise():
     cfg = MEDIUM["swiglu-bf16-zipf-capacity"]
     inp = gu.make_inputs(cfg)
