@@ -346,8 +346,16 @@ grouped_gemm_kernel(GemmArgs g) {
   // ---------------- tile scheduling
   TileSched ts;
   if (!schedule_tile(g, TC::BM, ts, reinterpret_cast<int*>(smem))) return;
-  const int e = ts.e, row0 = ts.row0, cnt = ts.cnt, mt = ts.mt, nt = ts.nt, split = ts.split;
-  const int m0 = mt * TC::BM;  // first row of this tile inside the group
+  const int e = ts.e, row0 = ts.row0, mt = ts.mt, nt = ts.nt, split = ts.split;
+  // The group's rows spread evenly over its M tiles, in 32-row blocks (the
+  // tile count stays ceil(rows / BM)): tiles that share a weight column then
+  // step through K at the same pace and meet in the L2, where a full tile
+  // beside a nearly empty one ran ahead of it and the weights were fetched
+  // twice.  cnt is this tile's end inside the group.
+  const int mte = (ts.cnt + TC::BM - 1) / TC::BM;
+  const int tr = mte > 0 ? min(TC::BM, ((ts.cnt + mte - 1) / mte + 31) / 32 * 32) : TC::BM;
+  const int m0 = mt * tr;  // first row of this tile inside the group
+  const int cnt = min(ts.cnt, m0 + tr);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
