@@ -16,6 +16,10 @@ pytestmark = pytest.mark.gpu
 C = synth.LayerConfig
 CASES = [synth.CONFIGS[5],
          C("graph-bf16-capacity", 150, T=300, d=256, E=8, top_k=2, F=384, capacity_factor=1.25),
+         # enough tiles (256 gate/up, 128 split down units) that the last
+         # quarter of every XCD range is claimed at run time: each replay
+         # must find the claim counters zeroed by the dispatch it replays
+         C("graph-bf16-claims", 152, T=4096, d=512, E=8, top_k=2, F=1024),
          C("graph-sigmoid-shared", 151, T=130, d=256, E=16, top_k=4, F=128,
            router=synth.SIGMOID_GROUP, routed_scaling=2.5, n_group=4, topk_group=2,
            shared_experts=1, shared_F=128, router_dtype=synth.BF16, bias_range=0.05)]
