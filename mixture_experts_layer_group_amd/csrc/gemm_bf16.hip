@@ -755,68 +755,132 @@ grouped_gemm_kernel(GemmArgs g) {
   // lane holds, for block (nb, mb) and item v: output column
   //   colbase(nb) + 8*(v/4) + 4*(lane/32) + v%4, row arow_l[mb].
   bool sat = false;
+  // fp16 outputs go through LDS, free once every wave has left the K loop:
+  // each wave puts its 4-column pieces there, then the workgroup copies
+  // whole rows out in 16-byte pieces, eight to a 128-byte line.  Stored
+  // directly, the MFMA layout puts 16 bytes into each of 32 rows per store
+  // instruction.  fp32 rows (the stage API's) keep the direct stores.
+  constexpr int kCols = MODE == kSwiGLU ? BN / 2 : BN;  // output columns of a tile
+  constexpr int kStRow = kCols * 2 + 16;                 // staged row, padded
+  constexpr bool kStageFits =
+      TC::BM * kStRow <= TC::NSA * TC::kTileBytesA + TC::NSW * TC::kWBytes;
+  if (kStageFits && (MODE != kDown || g.y16) && g.ldo % 8 == 0 && g.N % 8 == 0) {
+    __syncthreads();  // the K loop's last LDS reads are done in every wave
 #pragma unroll
-  for (int mb = 0; mb < TC::MB; ++mb) {
-    const int m = m0 + arow_l[mb];
-    if (m >= cnt) continue;
-    const int64_t orow_off = static_cast<int64_t>(row0 + m) * g.ldo;
-    uint16_t* orow = static_cast<uint16_t*>(g.out) + orow_off;
-    float* orow_f = (split ? g.part : static_cast<float*>(g.out)) + orow_off;
-    // the routing weight of the row, when the caller asks for weighted rows
-    // (each K split is scaled; the splits add up to the scaled row)
-    const float rsc = MODE == kDown && g.row_scale != nullptr ? g.row_scale[row0 + m] : 1.f;
-    if (MODE == kSwiGLU) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = nt * (BN / 2) + wn * 32 + 8 * q + 4 * fh;
-        if (col >= g.N) continue;
-        float h[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          h[v] = silu(acc[0][mb][4 * q + v]) * acc[1][mb][4 * q + v];
-        uint2 pk;
-        pk.x = pack_h2(h[0], h[1], sat);
-        pk.y = pack_h2(h[2], h[3], sat);
-        *reinterpret_cast<uint2*>(orow + col) = pk;
-      }
-    } else {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
+    for (int mb = 0; mb < TC::MB; ++mb) {
+      const int r = arow_l[mb];
+      if (m0 + r >= cnt) continue;
+      uint8_t* srow = smem + r * kStRow;
+      const float rsc =
+          MODE == kDown && g.row_scale != nullptr ? g.row_scale[row0 + m0 + r] : 1.f;
+      if (MODE == kSwiGLU) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = nt * BN + wn * 64 + nb * 32 + 8 * q + 4 * fh;
-          if (col >= g.N) continue;
-          if (MODE == kDown) {
-            float4 o = make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
-                                   acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
-            if (g.row_scale != nullptr) {
-              o.x *= rsc;
-              o.y *= rsc;
-              o.z *= rsc;
-              o.w *= rsc;
-            }
-            if (g.y16) {  // fp16 rows inside the layer (saturating, reported)
-              uint16_t* orow_h =
-                  reinterpret_cast<uint16_t*>(split ? static_cast<void*>(g.part) : g.out) +
-                  orow_off;
-              uint2 pk;
-              pk.x = pack_h2(o.x, o.y, sat);
-              pk.y = pack_h2(o.z, o.w, sat);
-              *reinterpret_cast<uint2*>(orow_h + col) = pk;
-            } else {
-              *reinterpret_cast<float4*>(orow_f + col) = o;
-            }
-          } else {
+          float h[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            h[v] = silu(acc[0][mb][4 * q + v]) * acc[1][mb][4 * q + v];
+          uint2 pk;
+          pk.x = pack_h2(h[0], h[1], sat);
+          pk.y = pack_h2(h[2], h[3], sat);
+          *reinterpret_cast<uint2*>(srow + 2 * (wn * 32 + 8 * q + 4 * fh)) = pk;
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
             float h[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const float z = acc[nb][mb][4 * q + v];
-              h[v] = z > 0.f ? z : 0.f;
+              h[v] = MODE == kDown ? (g.row_scale != nullptr ? z * rsc : z) : (z > 0.f ? z : 0.f);
             }
             uint2 pk;
             pk.x = pack_h2(h[0], h[1], sat);
             pk.y = pack_h2(h[2], h[3], sat);
-            *reinterpret_cast<uint2*>(orow + col) = pk;
+            *reinterpret_cast<uint2*>(srow + 2 * (wn * 64 + nb * 32 + 8 * q + 4 * fh)) = pk;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int rows = min(TC::BM, cnt - m0);
+    const int col0 = MODE == kSwiGLU ? nt * (BN / 2) : nt * BN;
+    const int ncol = min(kCols, g.N - col0);
+    constexpr int kPieces = kCols / 8;  // 16-byte pieces of a staged row
+    uint16_t* obase = static_cast<uint16_t*>(
+        MODE == kDown && split ? static_cast<void*>(g.part) : g.out);
+    for (int i = tid; i < rows * kPieces; i += kThreads) {
+      const int r = i / kPieces, c = (i - r * kPieces) * 8;
+      if (c >= ncol) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(smem + r * kStRow + 2 * c);
+      *reinterpret_cast<uint4*>(obase + static_cast<int64_t>(row0 + m0 + r) * g.ldo + col0 + c) = v;
+    }
+  } else {
+  #pragma unroll
+    for (int mb = 0; mb < TC::MB; ++mb) {
+      const int m = m0 + arow_l[mb];
+      if (m >= cnt) continue;
+      const int64_t orow_off = static_cast<int64_t>(row0 + m) * g.ldo;
+      uint16_t* orow = static_cast<uint16_t*>(g.out) + orow_off;
+      float* orow_f = (split ? g.part : static_cast<float*>(g.out)) + orow_off;
+      // the routing weight of the row, when the caller asks for weighted rows
+      // (each K split is scaled; the splits add up to the scaled row)
+      const float rsc = MODE == kDown && g.row_scale != nullptr ? g.row_scale[row0 + m] : 1.f;
+      if (MODE == kSwiGLU) {
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nt * (BN / 2) + wn * 32 + 8 * q + 4 * fh;
+          if (col >= g.N) continue;
+          float h[4];
+  #pragma unroll
+          for (int v = 0; v < 4; ++v)
+            h[v] = silu(acc[0][mb][4 * q + v]) * acc[1][mb][4 * q + v];
+          uint2 pk;
+          pk.x = pack_h2(h[0], h[1], sat);
+          pk.y = pack_h2(h[2], h[3], sat);
+          *reinterpret_cast<uint2*>(orow + col) = pk;
+        }
+      } else {
+  #pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+  #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = nt * BN + wn * 64 + nb * 32 + 8 * q + 4 * fh;
+            if (col >= g.N) continue;
+            if (MODE == kDown) {
+              float4 o = make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1],
+                                     acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
+              if (g.row_scale != nullptr) {
+                o.x *= rsc;
+                o.y *= rsc;
+                o.z *= rsc;
+                o.w *= rsc;
+              }
+              if (g.y16) {  // fp16 rows inside the layer (saturating, reported)
+                uint16_t* orow_h =
+                    reinterpret_cast<uint16_t*>(split ? static_cast<void*>(g.part) : g.out) +
+                    orow_off;
+                uint2 pk;
+                pk.x = pack_h2(o.x, o.y, sat);
+                pk.y = pack_h2(o.z, o.w, sat);
+                *reinterpret_cast<uint2*>(orow_h + col) = pk;
+              } else {
+                *reinterpret_cast<float4*>(orow_f + col) = o;
+              }
+            } else {
+              float h[4];
+  #pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const float z = acc[nb][mb][4 * q + v];
+                h[v] = z > 0.f ? z : 0.f;
+              }
+              uint2 pk;
+              pk.x = pack_h2(h[0], h[1], sat);
+              pk.y = pack_h2(h[2], h[3], sat);
+              *reinterpret_cast<uint2*>(orow + col) = pk;
+            }
           }
         }
       }
