@@ -128,14 +128,24 @@ __device__ __forceinline__ int swz(int r, int c) {
   return r * kRowBytes + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
 }
 
+// The largest e < E with p[e] <= v, for a non-decreasing p with p[0] <= v,
+// searched by the whole wave: each round the lanes read 64 evenly spaced
+// entries of the remaining range at once and a ballot keeps the stretch after
+// the last one not above v (one round up to 64 experts, two up to 4096),
+// where a binary search made one dependent load per halving.
 __device__ __forceinline__ int largest_le(const int32_t* __restrict__ p, int E,
                                           int32_t v) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p[mid] <= v) lo = mid; else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  int base = 0, span = E;
+  while (span > 1) {
+    const int step = (span + 63) >> 6;
+    const int i = lane * step;
+    const bool le = i < span && p[base + i] <= v;
+    const int last = 63 - __builtin_clzll(__ballot(le));  // lane 0 always holds
+    base += last * step;
+    span = min(step, span - last * step);
   }
-  return lo;
+  return base;
 }
 
 // silu with the hardware reciprocal (about 1 ulp of fp32) instead of an
