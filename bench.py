@@ -710,13 +710,13 @@ def summarize_traffic(args) -> int:
         f.write(f"# HBM traffic of the {what} per layer call, {cfg.name}\n\n")
         f.write("Commands (repository root, one MI355X; the probe runs a 1 GiB elementwise "
                 "negation for calibration, then three layer calls):\n\n```\n")
-        f.write("cd /tmp && export TMPDIR=/tmp\n")
+        f.write("export REPO=$PWD OUT=/tmp/moe_profiles TMPDIR=/tmp && mkdir -p $OUT && cd /tmp\n")
         for c, dd in (("FETCH_SIZE", "pmc_fetch"), ("WRITE_SIZE", "pmc_write")):
             f.write(f"timeout -s KILL 120 rocprofv3 --kernel-include-regex '{regex}' "
-                    f"--pmc {c} --output-format csv -d $REPO/gpurun_out/{dd} "
+                    f"--pmc {c} --output-format csv -d $OUT/{dd} "
                     f"-o p -- python3 $REPO/bench.py --config {cfg.cfg_id} --traffic-probe\n")
         f.write(f"python3 $REPO/bench.py --config {cfg.cfg_id} --summarize-traffic "
-                f"$REPO/gpurun_out/pmc_fetch $REPO/gpurun_out/pmc_write"
+                f"$OUT/pmc_fetch $OUT/pmc_write"
                 f"{' --side' if args.side else ''}\n```\n\n")
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             r = res[c]
@@ -777,11 +777,12 @@ def summarize_stats(args) -> int:
     c = cfg.cfg_id
     out = [f"# Kernel time of {STATS_WORKLOADS.get(c, cfg.name)}", "",
            "Commands (repository root, one MI355X):", "", "```",
-           f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format "
-           f"csv -d $REPO/gpurun_out/prof_c{c} -o bench -- python3 $REPO/bench.py --config {c} "
-           f"--steps 20 --warmup 2 --no-cpu-baseline > $REPO/gpurun_out/prof_c{c}.log",
-           f"python3 $REPO/bench.py --config {c} --summarize-stats $REPO/gpurun_out/prof_c{c} "
-           f"$REPO/gpurun_out/prof_c{c}.log",
+           f"export REPO=$PWD OUT=/tmp/moe_profiles TMPDIR=/tmp && mkdir -p $OUT && cd /tmp",
+           f"rocprofv3 --kernel-trace --stats --output-format "
+           f"csv -d $OUT/prof_c{c} -o bench -- python3 $REPO/bench.py --config {c} "
+           f"--steps 20 --warmup 2 --no-cpu-baseline > $OUT/prof_c{c}.log",
+           f"python3 $REPO/bench.py --config {c} --summarize-stats $OUT/prof_c{c} "
+           f"$OUT/prof_c{c}.log",
            "```", "",
            "| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |",
            "|---|---|---|---|---|---|"]
@@ -842,13 +843,14 @@ def summarize_mfma(args) -> int:
     with open(path, "w") as f:
         f.write(f"# Matrix-core counters of the bf16 expert GEMMs, {cfg.name}\n\n")
         f.write("Commands (repository root, one MI355X; three layer calls after a calibration "
-                "copy):\n\n```\ncd /tmp && export TMPDIR=/tmp\n")
+                "copy):\n\n```\nexport REPO=$PWD OUT=/tmp/moe_profiles TMPDIR=/tmp && "
+                "mkdir -p $OUT && cd /tmp\n")
         f.write(f"timeout -s KILL 120 rocprofv3 --kernel-trace --kernel-include-regex "
                 f"'neg_kernel|grouped_gemm' --pmc {MFMA_COUNTERS} --output-format csv "
-                f"-d $REPO/gpurun_out/pmc_mfma -o p -- python3 $REPO/bench.py --config "
+                f"-d $OUT/pmc_mfma -o p -- python3 $REPO/bench.py --config "
                 f"{cfg.cfg_id} --traffic-probe\n")
         f.write(f"python3 $REPO/bench.py --config {cfg.cfg_id} --summarize-mfma "
-                "$REPO/gpurun_out/pmc_mfma\n```\n\n")
+                "$OUT/pmc_mfma\n```\n\n")
         f.write("MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
                 "MFMA FLOPs = 512 x SQ_INSTS_VALU_MFMA_MOPS_*; the clock is GRBM_GUI_ACTIVE "
                 "summed over the 8 XCDs, / 8, over the dispatch's duration (under counter "
